@@ -1,0 +1,64 @@
+"""The CPU oracle against its pins, and the pins against planted mistakes."""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+from oracle import oracle as O
+from tests import oracle_pins as P
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    return O.default()
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(oracle, pin):
+    pin(oracle)
+
+
+# Each mutant is a plausible slip in the oracle's C source; at least one pin must catch it.
+MUTANTS = [
+    ("q4k nibble halves swapped", "int q = (r < 32) ? (byte & 15) : (byte >> 4);",
+     "int q = (r < 32) ? (byte >> 4) : (byte & 15);"),
+    ("q4k scale high bits from wrong byte", "*sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);",
+     "*sc = (s[j + 4] & 15) | ((s[j] >> 6) << 4);"),
+    ("q4k min low bits from scale nibble", "*m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);",
+     "*m = (s[j + 4] & 15) | ((s[j] >> 6) << 4);"),
+    ("dropped min term", "w[e] = d * sc * q - dmin * m;", "w[e] = d * sc * q;"),
+    ("min term sign", "w[e] = d * sc * q - dmin * m;", "w[e] = d * sc * q + dmin * m;"),
+    ("q5k wrong high bit", "q += ((qh[e % 32] >> g) & 1) << 4;", "q += ((qh[e % 32] >> (g ^ 1)) & 1) << 4;"),
+    ("q6k offset", "w[e] = d * scales[e / 16] * (q - 32);", "w[e] = d * scales[e / 16] * (q - 31);"),
+    ("q6k scale granularity", "w[e] = d * scales[e / 16] * (q - 32);", "w[e] = d * scales[e / 32] * (q - 32);"),
+    ("q6k high bit shift", "int hi = (qh[32 * h + i] >> (2 * r)) & 3;", "int hi = (qh[32 * h + i] >> r) & 3;"),
+    ("q6k low-byte index", "int lbyte = ql[64 * h + 32 * (r & 1) + i];", "int lbyte = ql[64 * h + 32 * (r >> 1) + i];"),
+    ("fp16 subnormal exponent", "v = ldexp((double)man, -24);", "v = ldexp((double)man, -25);"),
+    ("fp16 normal bias", "v = ldexp((double)(man | 0x400), exp - 25);", "v = ldexp((double)(man | 0x400), exp - 24);"),
+    ("bf16 shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("x row ignored", "const double *xb = xd + b * cols + s * 256;", "const double *xb = xd + s * 256;"),
+    ("abs dropped", "magp[b] += fabs(p);", "magp[b] += p;"),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, orig, mut):
+    src = open(O._SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor not found: {orig}"
+    d = tempfile.mkdtemp(prefix="kqo_mut_")
+    try:
+        path = os.path.join(d, "mut.c")
+        open(path, "w").write(src.replace(orig, mut))
+        so = os.path.join(d, "libmut.so")
+        O.compile_c(path, so)
+        bad = O.Oracle(so)
+        caught = []
+        for pin in P.ALL_PINS:
+            try:
+                pin(bad)
+            except (AssertionError, ValueError) as e:
+                caught.append(f"{pin.__name__}: {e}")
+        assert caught, f"no pin caught mutant '{name}'"
+    finally:
+        shutil.rmtree(d, ignore_errors=True)

@@ -1,0 +1,44 @@
+"""The seeded input generators: determinism, value ranges and workload sizes."""
+import numpy as np
+import torch
+
+from oracle import oracle as O
+from quant_weight_streaming_amd import synth
+
+
+def test_deterministic():
+    a = synth.gen_weights("q4k", 64, 1024, 5)
+    b = synth.gen_weights("q4k", 64, 1024, 5)
+    c = synth.gen_weights("q4k", 64, 1024, 6)
+    assert torch.equal(a, b) and not torch.equal(a, c)
+    assert torch.equal(synth.gen_x(2, 512, 1), synth.gen_x(2, 512, 1))
+
+
+def test_sweep_bytes_match_workload():
+    # 52 x (QKV 4608x5120 + O 5120x4096 + gate_up 62464x5120 Q4_K + down 5120x31232 Q6_K) + head 131072x5120 Q6_K
+    assert synth.sweep_bytes("q4k") == 18_029_690_880
+    assert synth.sweep_bytes("q5k") == 20_108_492_800
+    assert len(synth.sweep()) == 209
+
+
+def test_value_ranges():
+    w = synth.gen_weights("q4k", 128, 2048, 1).numpy().reshape(-1, 144)
+    d = w[:, 0:2].copy().view(np.float16).astype(np.float64)
+    assert np.all(d >= 0) and 0.005 < d.mean() < 0.011          # |N(0,1)| * 1e-2 has mean 0.00798
+    W = O.dequant("q6k", 64, 2048, synth.gen_weights("q6k", 64, 2048, 2).numpy())
+    assert np.isfinite(W).all()
+    sc = synth.gen_weights("q6k", 64, 2048, 2).numpy().reshape(-1, 210)[:, 192:208].view(np.int8)
+    assert sc.min() == -64 and sc.max() == 63
+
+
+def test_merge_fraction():
+    w = synth.gen_weights("q4k", 512, 1024, 3, merge_frac=0.25).numpy().reshape(-1, 144)
+    W = O.dequant("q4k", 512, 1024, synth.gen_weights("q4k", 512, 1024, 3, merge_frac=0.25).numpy())
+    # recover (sc, m) of each sub-block through the oracle by comparing pairs of rows is awkward; use
+    # the scale bytes directly: a selected super-block has sc[2k+1]==sc[2k] and m[2k+1]==m[2k] for all k.
+    s = w[:, 4:16].astype(np.int32)
+    sc = np.concatenate([s[:, 0:4] & 63, (s[:, 8:12] & 15) | ((s[:, 0:4] >> 6) << 4)], 1)
+    m = np.concatenate([s[:, 4:8] & 63, (s[:, 8:12] >> 4) | ((s[:, 4:8] >> 6) << 4)], 1)
+    merged = np.all((sc[:, 0::2] == sc[:, 1::2]) & (m[:, 0::2] == m[:, 1::2]), axis=1)
+    assert 0.2 < merged.mean() < 0.3
+    assert np.isfinite(W).all()
