@@ -1,0 +1,151 @@
+/*
+ * kq.h -- C ABI of the K-quant decode GEMV library for AMD MI355X (gfx950).
+ *
+ * The operation is the decode-step matrix-vector product over GGUF K-quant
+ * weights,
+ *
+ *     y[b, r] = sum_k dequant(W)[r, k] * x[b, k]        for b < batch <= 8,
+ *
+ * where every generated token streams the whole quantised decoder through it
+ * once.  Sources for what is computed:
+ *   - Q4_K / Q5_K / Q6_K super-blocks executed natively on the GPU, with a
+ *     backend-specific repack: daily.dev summary of the ExecuTorch announcement,
+ *     Q&A "How does ExecuTorch export Muse Glimmer GGUF checkpoints for CUDA and
+ *     Apple Silicon?".
+ *   - decode priced as weight bytes streamed per token: "Muse-Glimmer-30B (text
+ *     decoder) - Apple Core AI", decode table and the paragraph after it.
+ *   - batch 1 per exported method: "Muse Glimmer 30B - ExecuTorch PTE" card,
+ *     section "Runtime limitations"; batch 1 through 8: SGLang Day-0 post,
+ *     paragraph on the seven-platform sweep.
+ *   - projections that read the same hidden state folded into one product:
+ *     Core AI card, section "The architecture, and what the port had to do
+ *     about it" (qkvg_proj, 4 GEMMs -> 1).
+ *
+ * Dequantisation (one rounding to fp32 of an exact value):
+ *   Q4_K, Q5_K: w = d * sc_g * q - dmin * m_g    (sub-blocks g of 32 weights)
+ *   Q6_K      : w = d * sc_g * (q - 32)          (sub-blocks g of 16 weights)
+ *
+ * Conventions for every entry point:
+ *   - Pointers named w, gguf, out, x, y are DEVICE pointers owned by the caller;
+ *     array-of-pointer and array-of-size arguments of kq_gemv_multi are HOST
+ *     arrays read during the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously; the call returns once it is enqueued.
+ *   - Arguments are validated on the host first; on any error the call returns
+ *     a non-zero KQ_ERR_* code and enqueues nothing.  A failed launch returns
+ *     KQ_ERR_HIP.  No C++ exception crosses the boundary.
+ *   - `cols` (K) must be a positive multiple of 256; `rows` (M) >= 1.
+ *   - GEMV calls on one device share a library-owned scratch area (partial sums
+ *     of K-split row tiles); calls that overlap in time on one device (different
+ *     streams without ordering) race on it.  kq_init allocates it; otherwise the
+ *     first GEMV call on a device does (so that first call must not be made
+ *     inside a stream capture).
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KQ_ABI_VERSION 1
+
+/* weight formats */
+#define KQ_Q4_K 1
+#define KQ_Q5_K 2
+#define KQ_Q6_K 3
+
+/* activation formats: fp32, or bf16 (bit patterns, 2 bytes per element) */
+#define KQ_X_F32 0
+#define KQ_X_BF16 1
+
+#define KQ_MAX_BATCH 8
+#define KQ_MAX_PROJ 8
+
+/* status codes */
+#define KQ_OK 0
+#define KQ_ERR_NULL 1   /* a required pointer is NULL */
+#define KQ_ERR_SHAPE 2  /* rows < 1, cols not a positive multiple of 256, ldx < cols, ldy < rows, ... */
+#define KQ_ERR_ALIGN 3  /* w / x not 16-byte aligned, y not 4-byte aligned, or row stride of x not 16 B */
+#define KQ_ERR_BATCH 4  /* batch outside 1..KQ_MAX_BATCH, or n outside 1..KQ_MAX_PROJ */
+#define KQ_ERR_TYPE 5   /* unknown weight or activation format */
+#define KQ_ERR_HIP 6    /* a HIP runtime call or kernel launch failed */
+#define KQ_ERR_NOMEM 7  /* scratch allocation failed */
+#define KQ_ERR_RANGE 8  /* problem too large for 32-bit tile indexing */
+
+/* Version of this ABI (KQ_ABI_VERSION). */
+int kq_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kq_status_str(int status);
+
+/*
+ * Allocate this library's per-device scratch on `device` (the HIP ordinal).
+ * Optional: GEMV calls allocate it on first use.  Returns KQ_OK if present.
+ */
+int kq_init(int device);
+
+/*
+ * Size in bytes of the repacked form of a rows x cols matrix of `type`, or 0 if
+ * the arguments are invalid.  Host-only; makes no HIP call.
+ *
+ * Layout (all offsets in bytes): rows are grouped in tiles of 64 (the last tile
+ * zero-padded).  Tile t, super-block column c starts at ((t * cols/256) + c) *
+ * 64 * S, S = 144 / 176 / 210.  Inside it, 16-byte chunk k of the super-block
+ * of row 64*t + r is at k*1024 + 16*r, so one 64-lane wavefront reads each
+ * chunk as one contiguous 1 KiB; Q6_K's fp16 d of row r follows all chunks at
+ * 13*1024 + 2*r.  The chunk contents re-order each super-block's bits (scale
+ * and min bytes beside their quants) without changing the byte count.
+ */
+size_t kq_repacked_bytes(int type, int64_t rows, int64_t cols);
+
+/*
+ * Repack GGUF super-blocks into the layout above.
+ *   gguf : device, rows * cols/256 super-blocks in GGUF row-major order
+ *          (144 / 176 / 210 bytes each); any alignment.
+ *   out  : device, kq_repacked_bytes(type, rows, cols) bytes, 16-byte aligned.
+ * One-time, off the per-token path (the "repacked ... kernels" of the daily.dev
+ * summary's GGUF Q&A).
+ */
+int kq_repack(int type, int64_t rows, int64_t cols, const void *gguf, void *out, void *stream);
+
+/*
+ * y[b*ldy + r] = sum_k dequant(W)[r, k] * x[b*ldx + k], r < rows, b < batch.
+ *   w    : repacked Q4_K (resp. Q5_K, Q6_K) weights from kq_repack with the same
+ *          rows and cols (not checked: it would need a device read).
+ *   x    : fp32 or bf16 activations, batch rows of stride ldx elements; 16-byte
+ *          aligned and ldx * element size a multiple of 16.
+ *   y    : fp32 output, batch rows of stride ldy >= rows; 4-byte aligned.
+ * Deterministic: the same inputs give bitwise the same y on every run.
+ */
+int kq_gemv_q4k(const void *w, int64_t rows, int64_t cols, const void *x, int xtype, int64_t ldx, int batch,
+                float *y, int64_t ldy, void *stream);
+int kq_gemv_q5k(const void *w, int64_t rows, int64_t cols, const void *x, int xtype, int64_t ldx, int batch,
+                float *y, int64_t ldy, void *stream);
+int kq_gemv_q6k(const void *w, int64_t rows, int64_t cols, const void *x, int xtype, int64_t ldx, int batch,
+                float *y, int64_t ldy, void *stream);
+
+/*
+ * n projections of one type that read the same x (QKV, gate+up), in ONE launch:
+ * y[i][b*ldy[i] + r] = sum_k dequant(W_i)[r, k] * x[b*ldx + k], r < rows[i].
+ *   w, rows, y, ldy : host arrays of n entries (device pointers in w and y).
+ * Same per-matrix rules as kq_gemv_q4k.  1 <= n <= KQ_MAX_PROJ.
+ */
+int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
+                  int64_t ldx, int batch, float *const *y, const int64_t *ldy, void *stream);
+
+/*
+ * out[r*ldo + k] = dequant(W)[r, k] as fp32 (the single correctly rounded value
+ * of the exact dequantised weight), from the repacked layout.  ldo >= cols,
+ * out 4-byte aligned.  Used to check the repack and unpack bit-exactly.
+ */
+int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

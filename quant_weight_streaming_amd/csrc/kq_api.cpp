@@ -1,0 +1,235 @@
+// C ABI of the K-quant GEMV library: argument validation, launch geometry and
+// the per-device scratch area.  Every step of the computation runs in the HIP
+// kernels of kq_gemv.hip / kq_repack.hip.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "../../include/kq.h"
+#include "kq_internal.h"
+
+namespace kq {
+
+int64_t sb_bytes(int type) {
+  switch (type) {
+    case KQ_Q4_K: return 144;
+    case KQ_Q5_K: return 176;
+    case KQ_Q6_K: return 210;
+    default: return 0;
+  }
+}
+
+static int sub_blocks(int type) { return type == KQ_Q6_K ? 16 : 8; }
+
+// Scratch for K-split row tiles: two partial-sum slots and one arrival counter
+// per wavefront.  The counters are zero between calls (the last arrival of a
+// tile resets its counter), so they are cleared once, at allocation.
+constexpr int kMaxWaves = 8192;
+constexpr size_t kPartialBytes = (size_t)kMaxWaves * 2 * KQ_MAX_BATCH * 64 * sizeof(float);
+constexpr size_t kCounterBytes = (size_t)kMaxWaves * sizeof(uint32_t);
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  bool ready = false;
+  int cus = 0;
+  float* partial = nullptr;
+  uint32_t* counters = nullptr;
+};
+
+static std::mutex g_mu;
+static DeviceState g_dev[kMaxDevices];
+
+static int device_state(int dev, DeviceState** out) {
+  if (dev < 0 || dev >= kMaxDevices) return KQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& s = g_dev[dev];
+  if (!s.ready) {
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return KQ_ERR_HIP;
+    if (hipSetDevice(dev) != hipSuccess) return KQ_ERR_HIP;
+    int rc = KQ_OK;
+    void* p = nullptr;
+    void* c = nullptr;
+    if (hipDeviceGetAttribute(&s.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) rc = KQ_ERR_HIP;
+    if (rc == KQ_OK && hipMalloc(&p, kPartialBytes) != hipSuccess) rc = KQ_ERR_NOMEM;
+    if (rc == KQ_OK && hipMalloc(&c, kCounterBytes) != hipSuccess) rc = KQ_ERR_NOMEM;
+    if (rc == KQ_OK && hipMemset(c, 0, kCounterBytes) != hipSuccess) rc = KQ_ERR_HIP;
+    if (rc == KQ_OK && hipDeviceSynchronize() != hipSuccess) rc = KQ_ERR_HIP;
+    if (rc != KQ_OK) {
+      if (p) (void)hipFree(p);
+      if (c) (void)hipFree(c);
+      (void)hipSetDevice(prev);
+      return rc;
+    }
+    s.partial = static_cast<float*>(p);
+    s.counters = static_cast<uint32_t*>(c);
+    s.ready = true;
+    (void)hipSetDevice(prev);
+  }
+  *out = &s;
+  return KQ_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int waves_per_cu() {
+  static int v = [] {
+    const char* e = getenv("KQ_WAVES_PER_CU");
+    int x = e ? atoi(e) : 0;
+    return (x >= 1 && x <= 32) ? x : 8;
+  }();
+  return v;
+}
+
+static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream) {
+  if (type != KQ_Q4_K && type != KQ_Q5_K && type != KQ_Q6_K) return KQ_ERR_TYPE;
+  if (xtype != KQ_X_F32 && xtype != KQ_X_BF16) return KQ_ERR_TYPE;
+  if (batch < 1 || batch > KQ_MAX_BATCH || n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
+  if (!w || !rows || !y || !ldy || !x) return KQ_ERR_NULL;
+  for (int i = 0; i < n; ++i)
+    if (!w[i] || !y[i]) return KQ_ERR_NULL;
+  if (cols <= 0 || cols % 256 != 0 || ldx < cols) return KQ_ERR_SHAPE;
+  for (int i = 0; i < n; ++i)
+    if (rows[i] < 1 || ldy[i] < rows[i]) return KQ_ERR_SHAPE;
+  const int64_t esize = xtype == KQ_X_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * esize) % 16 != 0) return KQ_ERR_ALIGN;
+  for (int i = 0; i < n; ++i)
+    if (!aligned(w[i], 16) || !aligned(y[i], 4)) return KQ_ERR_ALIGN;
+
+  const int64_t n_cols = cols / 256;
+  GemvArgs a{};
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    if (rows[i] > (int64_t)INT32_MAX - 64) return KQ_ERR_RANGE;
+    a.w[i] = static_cast<const uint8_t*>(w[i]);
+    a.y[i] = y[i];
+    a.ldy[i] = ldy[i];
+    a.rows[i] = (int32_t)rows[i];
+    a.tile_begin[i] = (int32_t)tiles;
+    tiles += (rows[i] + 63) / 64;
+    if (tiles > INT32_MAX) return KQ_ERR_RANGE;
+  }
+  for (int i = n; i <= KQ_MAX_PROJ; ++i) a.tile_begin[i] = (int32_t)tiles;
+  const int64_t n_units = tiles * n_cols;
+  if (n_units + 2 * n_cols + 4 * (int64_t)kMaxWaves >= INT32_MAX) return KQ_ERR_RANGE;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  DeviceState* st = nullptr;
+  int rc = device_state(dev, &st);
+  if (rc != KQ_OK) return rc;
+
+  // Launch geometry: an even run of units per wavefront, about waves_per_cu()
+  // wavefronts per CU; the activation sums of the columns one wavefront touches
+  // must fit 16 KiB of LDS per wavefront.
+  const int64_t target = (int64_t)st->cus * waves_per_cu();
+  int64_t upw = (n_units + target - 1) / target;
+  if (upw < 1) upw = 1;
+  const int64_t per_col = (int64_t)sub_blocks(type) * batch;   // LDS floats per column
+  const int64_t cap = 4096 / per_col;                            // columns that fit 16 KiB
+  if (n_cols > cap && upw > cap) upw = cap;
+  int64_t n_waves = (n_units + upw - 1) / upw;
+  if (n_waves > kMaxWaves) {
+    upw = (n_units + kMaxWaves - 1) / kMaxWaves;
+    if (n_cols > cap && upw > cap) return KQ_ERR_RANGE;
+    n_waves = (n_units + upw - 1) / upw;
+  }
+  const int64_t tcols = n_cols < upw ? n_cols : upw;
+  a.nproj = n;
+  a.n_cols = (int32_t)n_cols;
+  a.x = x;
+  a.ldx = ldx;
+  a.n_units = (int32_t)n_units;
+  a.upw = (int32_t)upw;
+  a.n_waves = (int32_t)n_waves;
+  a.tsb = (int32_t)(tcols * sub_blocks(type));
+  a.partial = st->partial;
+  a.counters = st->counters;
+  const size_t lds = (size_t)4 * a.tsb * batch * sizeof(float);
+  int64_t grid = (n_waves + 3) / 4;
+  grid = (grid + 7) / 8 * 8;  // whole XCD rounds for the block remap
+  if (launch_gemv(type, xtype, batch, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+extern "C" {
+
+int kq_abi_version(void) { return KQ_ABI_VERSION; }
+
+const char* kq_status_str(int status) {
+  switch (status) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_NULL: return "null pointer argument";
+    case KQ_ERR_SHAPE: return "invalid shape or stride";
+    case KQ_ERR_ALIGN: return "misaligned pointer or stride";
+    case KQ_ERR_BATCH: return "batch or projection count out of range";
+    case KQ_ERR_TYPE: return "unknown weight or activation format";
+    case KQ_ERR_HIP: return "HIP runtime error";
+    case KQ_ERR_NOMEM: return "device allocation failed";
+    case KQ_ERR_RANGE: return "problem too large";
+    default: return "unknown status";
+  }
+}
+
+int kq_init(int device) {
+  DeviceState* st = nullptr;
+  return device_state(device, &st);
+}
+
+size_t kq_repacked_bytes(int type, int64_t rows, int64_t cols) {
+  const int64_t sbb = sb_bytes(type);
+  if (!sbb || rows < 1 || cols <= 0 || cols % 256 != 0) return 0;
+  const int64_t tiles = (rows + 63) / 64;
+  return (size_t)(tiles * (cols / 256) * 64 * sbb);
+}
+
+int kq_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, void* stream) {
+  if (!sb_bytes(type)) return KQ_ERR_TYPE;
+  if (!gguf || !out) return KQ_ERR_NULL;
+  if (rows < 1 || cols <= 0 || cols % 256 != 0) return KQ_ERR_SHAPE;
+  if (!aligned(out, 16) || !aligned(gguf, type == KQ_Q6_K ? 2 : 4)) return KQ_ERR_ALIGN;
+  if (rows > (int64_t)INT32_MAX - 64 || cols / 256 > INT32_MAX) return KQ_ERR_RANGE;
+  if (launch_repack(type, rows, cols, gguf, out, static_cast<hipStream_t>(stream)) != hipSuccess) return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+int kq_gemv_q4k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
+                float* y, int64_t ldy, void* stream) {
+  return gemv_impl(KQ_Q4_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, stream);
+}
+
+int kq_gemv_q5k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
+                float* y, int64_t ldy, void* stream) {
+  return gemv_impl(KQ_Q5_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, stream);
+}
+
+int kq_gemv_q6k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
+                float* y, int64_t ldy, void* stream) {
+  return gemv_impl(KQ_Q6_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, stream);
+}
+
+int kq_gemv_multi(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x, int xtype,
+                  int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream) {
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream);
+}
+
+int kq_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo, void* stream) {
+  if (!sb_bytes(type)) return KQ_ERR_TYPE;
+  if (!w || !out) return KQ_ERR_NULL;
+  if (rows < 1 || cols <= 0 || cols % 256 != 0 || ldo < cols) return KQ_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(out, 4)) return KQ_ERR_ALIGN;
+  if (rows > (int64_t)INT32_MAX - 64 || cols / 256 > INT32_MAX) return KQ_ERR_RANGE;
+  if (launch_dequant(type, w, rows, cols, out, ldo, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Host/device interface between the C-ABI layer (kq_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kq.h"
+
+namespace kq {
+
+// Kernel arguments of one GEMV launch (one or several projections sharing x).
+struct GemvArgs {
+  const uint8_t* w[KQ_MAX_PROJ];       // repacked weights of each projection
+  float* y[KQ_MAX_PROJ];               // outputs
+  int64_t ldy[KQ_MAX_PROJ];            // output row strides (elements)
+  int32_t rows[KQ_MAX_PROJ];           // rows of each projection
+  int32_t tile_begin[KQ_MAX_PROJ + 1]; // first global tile of each projection (prefix sums)
+  int32_t nproj;
+  int32_t n_cols;                      // super-block columns = cols / 256
+  const void* x;                       // activations (fp32 or bf16)
+  int64_t ldx;                         // activation row stride (elements)
+  int32_t n_units;                     // total tiles * n_cols
+  int32_t upw;                         // units per wavefront
+  int32_t n_waves;                     // wavefronts with work
+  int32_t tsb;                         // LDS floats per wavefront / batch: min(n_cols, upw) * sub-blocks per column
+  float* partial;                      // scratch: [n_waves][2][KQ_MAX_BATCH][64] partial sums
+  uint32_t* counters;                  // scratch: [n_waves] arrival counters, zero between calls
+};
+
+hipError_t launch_gemv(int type, int xtype, int batch, const GemvArgs& a, int grid, size_t lds, hipStream_t s);
+hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s);
+hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo,
+                          hipStream_t s);
+
+int64_t sb_bytes(int type);
+
+}  // namespace kq

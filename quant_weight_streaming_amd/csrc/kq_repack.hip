@@ -1,0 +1,245 @@
+// One-time repack of GGUF K-quant super-blocks into the wavefront-coalesced
+// tile layout (kq_common.h), and the fp32 dequantisation of that layout.
+//
+// GGUF super-block element order (public GGUF K-quant layout):
+//   Q4_K/Q5_K: element 64c + i (i < 32) is the low nibble of qs[32c + i],
+//              element 64c + 32 + i its high nibble; the Q5_K fifth bit of
+//              element 32g + i is bit g of qh[i].
+//   Q6_K: element 128h + 32r + i keeps its low nibble in ql[64h + 32(r&1) + i]
+//         (low half for r < 2) and its top two bits in bits 2r..2r+1 of
+//         qh[32h + i]; scales[e/16] is its int8 sub-block scale.
+#include "kq_common.h"
+#include "kq_internal.h"
+
+namespace kq {
+
+// byte i of a super-block held as 32-bit words
+template <int N> __device__ __forceinline__ uint32_t byte_at(const uint32_t (&W)[N], int i) {
+  return (W[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+}
+
+template <int QT> struct Repack;
+
+template <> struct Repack<KQ_Q4_K> {
+  static constexpr int kWords = 36;
+  // nibble of element e (0..255) from qs bytes starting at byte offset QS
+  template <int N> static __device__ __forceinline__ uint32_t nib(const uint32_t (&W)[N], int qs_off, int e) {
+    const int c = e / 64, r = e % 64;
+    const uint32_t b = byte_at(W, qs_off + 32 * c + (r % 32));
+    return (r < 32) ? (b & 15u) : (b >> 4);
+  }
+  template <int N> static __device__ __forceinline__ void quant_chunks(const uint32_t (&W)[N], int qs_off, u32x4* ch) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint32_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o |= nib(W, qs_off, 32 * g + 8 * j + 2 * p) << (4 * p);
+          o |= nib(W, qs_off, 32 * g + 8 * j + 2 * p + 1) << (16 + 4 * p);
+        }
+        v[j] = o;
+      }
+      ch[1 + g] = u32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  static __device__ __forceinline__ void run(const uint8_t* sb, u32x4* ch, uint16_t& d6) {
+    uint32_t W[kWords];
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(sb);
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) W[i] = p[i];
+    ch[0] = u32x4{W[0], W[1], W[2], W[3]};
+    quant_chunks(W, 16, ch);
+    d6 = 0;
+  }
+};
+
+template <> struct Repack<KQ_Q5_K> {
+  static constexpr int kWords = 44;
+  static __device__ __forceinline__ void run(const uint8_t* sb, u32x4* ch, uint16_t& d6) {
+    uint32_t W[kWords];
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(sb);
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) W[i] = p[i];
+    ch[0] = u32x4{W[0], W[1], W[2], W[3]};
+    Repack<KQ_Q4_K>::quant_chunks(W, 48, ch);
+    uint32_t H[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int pi = 0; pi < 16; ++pi) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int e = 32 * g + 2 * pi + s;          // = 32g + 8j + 2p + s with pi = 4j + p
+          const uint32_t bit = (byte_at(W, 16 + e % 32) >> g) & 1u;
+          o |= bit << (pi + 16 * s);
+        }
+      }
+      H[g] = o;
+    }
+    ch[9] = u32x4{H[0], H[1], H[2], H[3]};
+    ch[10] = u32x4{H[4], H[5], H[6], H[7]};
+    d6 = 0;
+  }
+};
+
+template <> struct Repack<KQ_Q6_K> {
+  static constexpr int kHalves = 105;
+  template <int N> static __device__ __forceinline__ uint32_t b16(const uint16_t (&U)[N], int i) {
+    return (U[i >> 1] >> (8 * (i & 1))) & 0xFFu;
+  }
+  template <int N> static __device__ __forceinline__ uint32_t lo(const uint16_t (&U)[N], int e) {
+    const int h = e / 128, r = (e % 128) / 32, i = e % 32;
+    const uint32_t b = b16(U, 64 * h + 32 * (r & 1) + i);
+    return (r < 2) ? (b & 15u) : (b >> 4);
+  }
+  template <int N> static __device__ __forceinline__ uint32_t hi(const uint16_t (&U)[N], int e) {
+    const int h = e / 128, r = (e % 128) / 32, i = e % 32;
+    return (b16(U, 128 + 32 * h + i) >> (2 * r)) & 3u;
+  }
+  static __device__ __forceinline__ void run(const uint8_t* sb, u32x4* ch, uint16_t& d6) {
+    uint16_t U[kHalves];
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(sb);
+#pragma unroll
+    for (int i = 0; i < kHalves; ++i) U[i] = p[i];
+    uint32_t L[16][2], H[16];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      uint32_t h = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int e = 16 * g + 8 * j + 2 * pp + s;
+            o |= lo(U, e) << (4 * pp + 16 * s);
+            h |= hi(U, e) << (2 * (4 * j + pp) + 16 * s);
+          }
+        }
+        L[g][j] = o;
+      }
+      H[g] = h;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ch[k] = u32x4{L[2 * k][0], L[2 * k][1], L[2 * k + 1][0], L[2 * k + 1][1]};
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ch[8 + k] = u32x4{H[4 * k], H[4 * k + 1], H[4 * k + 2], H[4 * k + 3]};
+    uint32_t S[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) S[k] = (uint32_t)U[96 + 2 * k] | ((uint32_t)U[97 + 2 * k] << 16);
+    ch[12] = u32x4{S[0], S[1], S[2], S[3]};
+    d6 = U[104];
+  }
+};
+
+template <int QT>
+__global__ void __launch_bounds__(256) repack_kernel(const uint8_t* __restrict__ gguf, uint8_t* __restrict__ out,
+                                                     int64_t rows, int n_cols, int64_t total) {
+  using F = Fmt<QT>;
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(gid & 63);
+    const int64_t unit = gid >> 6;               // tile * n_cols + column
+    const int64_t t = unit / n_cols;
+    const int c = (int)(unit - t * n_cols);
+    const int64_t row = t * kTileRows + lane;
+    u32x4 ch[F::kChunks];
+    uint16_t d6 = 0;
+    if (row < rows) {
+      Repack<QT>::run(gguf + (row * n_cols + c) * F::kSbBytes, ch, d6);
+    } else {
+#pragma unroll
+      for (int k = 0; k < F::kChunks; ++k) ch[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+    uint8_t* tb = out + unit * tile_bytes<QT>();
+#pragma unroll
+    for (int k = 0; k < F::kChunks; ++k)
+      *reinterpret_cast<u32x4*>(tb + k * kChunkStride + lane * kChunk) = ch[k];
+    if constexpr (QT == KQ_Q6_K) reinterpret_cast<uint16_t*>(tb + 13 * kChunkStride)[lane] = d6;
+  }
+}
+
+// out[row*ldo + 256c + e] = fp32 dequantised weight, from the repacked layout,
+// through the same unpacking the GEMV uses.
+template <int QT>
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
+                                                      int64_t rows, int n_cols, int64_t total, int64_t ldo) {
+  using F = Fmt<QT>;
+  const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(gid & 63);
+    const int64_t unit = gid >> 6;
+    const int64_t t = unit / n_cols;
+    const int c = (int)(unit - t * n_cols);
+    const int64_t row = t * kTileRows + lane;
+    const uint8_t* tb = w + unit * tile_bytes<QT>();
+    u32x4 ch[F::kChunks];
+#pragma unroll
+    for (int k = 0; k < F::kChunks; ++k)
+      ch[k] = *reinterpret_cast<const u32x4*>(tb + k * kChunkStride + lane * kChunk);
+    uint32_t d6 = 0;
+    if constexpr (QT == KQ_Q6_K) d6 = reinterpret_cast<const uint16_t*>(tb + 13 * kChunkStride)[lane];
+    float a[F::kSubBlocks], cm[F::kSubBlocks];
+    sb_coeffs<QT>(ch, d6, 1.0f, a, cm);
+    if (row >= rows) continue;
+    float* o = out + row * ldo + (int64_t)c * 256;
+#pragma unroll
+    for (int g = 0; g < F::kSubBlocks; ++g) {
+      uint32_t pr[F::kPairs];
+      unpack_pairs<QT>(ch, g, M, K, pr);
+#pragma unroll
+      for (int i = 0; i < F::kPairs; ++i) {
+        const int e = g * F::kSubW + 2 * i;
+        if constexpr (QT == KQ_Q6_K) {
+          o[e] = a[g] * (bf16_lo(pr[i]) - 160.0f);
+          o[e + 1] = a[g] * (bf16_hi(pr[i]) - 160.0f);
+        } else {
+          o[e] = __builtin_fmaf(a[g], bf16_lo(pr[i]) - 128.0f, -cm[g]);
+          o[e + 1] = __builtin_fmaf(a[g], bf16_hi(pr[i]) - 128.0f, -cm[g]);
+        }
+      }
+    }
+  }
+}
+
+static int grid_for(int64_t total) {
+  int64_t g = (total + 255) / 256;
+  return (int)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s) {
+  const int n_cols = (int)(cols / 256);
+  const int64_t n_tiles = (rows + kTileRows - 1) / kTileRows;
+  const int64_t total = n_tiles * n_cols * kTileRows;
+  const uint8_t* in = static_cast<const uint8_t*>(gguf);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  switch (type) {
+    case KQ_Q4_K: hipLaunchKernelGGL(repack_kernel<KQ_Q4_K>, dim3(grid_for(total)), dim3(256), 0, s, in, o, rows, n_cols, total); break;
+    case KQ_Q5_K: hipLaunchKernelGGL(repack_kernel<KQ_Q5_K>, dim3(grid_for(total)), dim3(256), 0, s, in, o, rows, n_cols, total); break;
+    case KQ_Q6_K: hipLaunchKernelGGL(repack_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, o, rows, n_cols, total); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo, hipStream_t s) {
+  const int n_cols = (int)(cols / 256);
+  const int64_t n_tiles = (rows + kTileRows - 1) / kTileRows;
+  const int64_t total = n_tiles * n_cols * kTileRows;
+  const uint8_t* in = static_cast<const uint8_t*>(w);
+  switch (type) {
+    case KQ_Q4_K: hipLaunchKernelGGL(dequant_kernel<KQ_Q4_K>, dim3(grid_for(total)), dim3(256), 0, s, in, out, rows, n_cols, total, ldo); break;
+    case KQ_Q5_K: hipLaunchKernelGGL(dequant_kernel<KQ_Q5_K>, dim3(grid_for(total)), dim3(256), 0, s, in, out, rows, n_cols, total, ldo); break;
+    case KQ_Q6_K: hipLaunchKernelGGL(dequant_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, out, rows, n_cols, total, ldo); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kq

@@ -1,0 +1,169 @@
+"""Thin Python binding of libkq.so (the C ABI in include/kq.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if libkq.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkq.so")
+
+KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 1, 2, 3
+KQ_X_F32, KQ_X_BF16 = 0, 1
+KQ_MAX_BATCH, KQ_MAX_PROJ = 8, 8
+TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
+SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
+STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
+          5: "KQ_ERR_TYPE", 6: "KQ_ERR_HIP", 7: "KQ_ERR_NOMEM", 8: "KQ_ERR_RANGE"}
+EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant")
+
+
+class KQError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({lib().kq_status_str(code).decode()})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkq.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run quant_weight_streaming_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.kq_abi_version.restype = ci
+        L.kq_status_str.argtypes = [ci]
+        L.kq_status_str.restype = ctypes.c_char_p
+        L.kq_init.argtypes = [ci]
+        L.kq_init.restype = ci
+        L.kq_repacked_bytes.argtypes = [ci, i64, i64]
+        L.kq_repacked_bytes.restype = ctypes.c_size_t
+        L.kq_repack.argtypes = [ci, i64, i64, vp, vp, vp]
+        L.kq_repack.restype = ci
+        for n in ("kq_gemv_q4k", "kq_gemv_q5k", "kq_gemv_q6k"):
+            f = getattr(L, n)
+            f.argtypes = [vp, i64, i64, vp, ci, i64, ci, vp, i64, vp]
+            f.restype = ci
+        L.kq_gemv_multi.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
+                                    ctypes.POINTER(vp), ctypes.POINTER(i64), vp]
+        L.kq_gemv_multi.restype = ci
+        L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
+        L.kq_dequant.restype = ci
+        _lib = L
+    return _lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise KQError(fn, rc)
+
+
+def _xtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return KQ_X_BF16
+    if x.dtype == torch.float32:
+        return KQ_X_F32
+    raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+
+
+def _type(qtype) -> int:
+    return TYPE_ID[qtype] if isinstance(qtype, str) else int(qtype)
+
+
+# ---------------------------------------------------------------- C-ABI mirrors
+
+def kq_abi_version() -> int:
+    return lib().kq_abi_version()
+
+
+def kq_init(device: int = 0) -> None:
+    _check("kq_init", lib().kq_init(device))
+
+
+def kq_repacked_bytes(qtype, rows: int, cols: int) -> int:
+    return int(lib().kq_repacked_bytes(_type(qtype), rows, cols))
+
+
+def kq_repack(qtype, rows: int, cols: int, gguf: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _check("kq_repack", lib().kq_repack(_type(qtype), rows, cols, gguf.data_ptr(), out.data_ptr(), _stream(stream)))
+
+
+def _gemv(fn: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    if x.dim() != 2 or y.dim() != 2:
+        raise ValueError("x is [batch, ldx], y is [batch, ldy]")
+    f = getattr(lib(), fn)
+    _check(fn, f(w.data_ptr(), rows, cols, x.data_ptr(), _xtype(x), x.stride(0), x.shape[0], y.data_ptr(),
+                 y.stride(0), _stream(stream)))
+
+
+def kq_gemv_q4k(w, rows, cols, x, y, stream=None):
+    _gemv("kq_gemv_q4k", w, rows, cols, x, y, stream)
+
+
+def kq_gemv_q5k(w, rows, cols, x, y, stream=None):
+    _gemv("kq_gemv_q5k", w, rows, cols, x, y, stream)
+
+
+def kq_gemv_q6k(w, rows, cols, x, y, stream=None):
+    _gemv("kq_gemv_q6k", w, rows, cols, x, y, stream)
+
+
+def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) -> None:
+    n = len(ws)
+    if len(rows) != n or len(ys) != n:
+        raise ValueError("ws, rows and ys must have the same length")
+    W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in ws])
+    R = (ctypes.c_int64 * n)(*rows)
+    Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
+    _check("kq_gemv_multi", lib().kq_gemv_multi(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
+                                                x.shape[0], Y, LD, _stream(stream)))
+
+
+def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:
+    _check("kq_dequant", lib().kq_dequant(_type(qtype), w.data_ptr(), rows, cols, out.data_ptr(), out.stride(0),
+                                          _stream(stream)))
+
+
+# ---------------------------------------------------------------- conveniences
+
+GEMV = {"q4k": kq_gemv_q4k, "q5k": kq_gemv_q5k, "q6k": kq_gemv_q6k}
+
+
+def repack(qtype: str, gguf: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+    """GGUF bytes on the device -> new repacked uint8 tensor."""
+    out = torch.empty(kq_repacked_bytes(qtype, rows, cols), dtype=torch.uint8, device=gguf.device)
+    kq_repack(qtype, rows, cols, gguf, out, stream)
+    return out
+
+
+def gemv(qtype: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: torch.Tensor = None,
+         stream=None) -> torch.Tensor:
+    if y is None:
+        y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=x.device)
+    GEMV[qtype](w, rows, cols, x, y, stream)
+    return y
+
+
+def dequant(qtype: str, w: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+    out = torch.empty((rows, cols), dtype=torch.float32, device=w.device)
+    kq_dequant(qtype, w, rows, cols, out, stream)
+    return out

@@ -1,0 +1,84 @@
+"""The C-ABI library: it loads, exports every symbol include/kq.h declares, and
+rejects invalid arguments on the host (no device work, so this runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quant_weight_streaming_amd import kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "kq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_matches_binding():
+    assert declared_symbols() == sorted(kq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = kq.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_version_and_sizes():
+    assert kq.kq_abi_version() == 1
+    assert kq.kq_repacked_bytes("q4k", 256, 1024) == 256 * 4 * 144
+    assert kq.kq_repacked_bytes("q5k", 1, 256) == 64 * 176          # one zero-padded tile
+    assert kq.kq_repacked_bytes("q6k", 65, 512) == 2 * 2 * 64 * 210
+    assert kq.kq_repacked_bytes("q4k", 64, 300) == 0                 # cols not a multiple of 256
+    assert kq.kq_repacked_bytes(9, 64, 256) == 0
+    assert kq.kq_repacked_bytes("q4k", 0, 256) == 0
+
+
+A16 = 0x10000  # a fake, 16-byte aligned "device" address: validation fails before any use
+
+
+@pytest.mark.parametrize("args,code", [
+    # (w, rows, cols, x, xtype, ldx, batch, y, ldy)
+    ((None, 64, 256, A16, 1, 256, 1, A16, 64), 1),
+    ((A16, 64, 256, None, 1, 256, 1, A16, 64), 1),
+    ((A16, 64, 256, A16, 1, 256, 1, None, 64), 1),
+    ((A16, 64, 300, A16, 1, 300, 1, A16, 64), 2),       # cols % 256
+    ((A16, 0, 256, A16, 1, 256, 1, A16, 64), 2),        # rows < 1
+    ((A16, 64, 256, A16, 1, 128, 1, A16, 64), 2),       # ldx < cols
+    ((A16, 64, 256, A16, 1, 256, 1, A16, 32), 2),       # ldy < rows
+    ((A16 + 4, 64, 256, A16, 1, 256, 1, A16, 64), 3),   # w misaligned
+    ((A16, 64, 256, A16 + 2, 1, 256, 1, A16, 64), 3),   # x misaligned
+    ((A16, 64, 256, A16, 1, 260, 1, A16, 64), 3),       # bf16 row stride not 16 B
+    ((A16, 64, 256, A16, 1, 256, 0, A16, 64), 4),       # batch 0
+    ((A16, 64, 256, A16, 1, 256, 9, A16, 64), 4),       # batch 9
+    ((A16, 64, 256, A16, 7, 256, 1, A16, 64), 5),       # xtype
+])
+def test_gemv_rejects(args, code):
+    for fn in ("kq_gemv_q4k", "kq_gemv_q5k", "kq_gemv_q6k"):
+        assert getattr(kq.lib(), fn)(*args, None) == code
+
+
+def test_multi_and_others_reject():
+    L = kq.lib()
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    W = (vp * 2)(A16, A16)
+    R = (i64 * 2)(64, 64)
+    Y = (vp * 2)(A16, A16)
+    LD = (i64 * 2)(64, 64)
+    assert L.kq_gemv_multi(9, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None) == 5
+    assert L.kq_gemv_multi(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None) == 4
+    assert L.kq_gemv_multi(1, 9, W, R, 256, A16, 1, 256, 1, Y, LD, None) == 4
+    Yb = (vp * 2)(A16, None)
+    assert L.kq_gemv_multi(1, 2, W, R, 256, A16, 1, 256, 1, Yb, LD, None) == 1
+    Rb = (i64 * 2)(64, 0)
+    assert L.kq_gemv_multi(1, 2, W, Rb, 256, A16, 1, 256, 1, Y, LD, None) == 2
+    assert L.kq_repack(1, 64, 256, None, A16, None) == 1
+    assert L.kq_repack(1, 64, 300, A16, A16, None) == 2
+    assert L.kq_repack(1, 64, 256, A16 + 2, A16, None) == 3       # Q4_K input needs 4-byte alignment
+    assert L.kq_repack(4, 64, 256, A16, A16, None) == 5
+    assert L.kq_dequant(1, A16, 64, 256, A16, 100, None) == 2     # ldo < cols
+    assert L.kq_dequant(3, A16 + 8, 64, 256, A16, 256, None) == 3
+    assert kq.lib().kq_status_str(3) == b"misaligned pointer or stride"

@@ -1,0 +1,197 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Dequantised weights must match bit-exactly; every output must satisfy
+|y_gpu - y_oracle| <= 1e-4 * sum_k |w_k x_k| (so an output whose terms are all
+zero must be exactly zero).  Small cases compare every output; the full-size
+workloads (one launch each, as the benchmark issues them) compare sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quant_weight_streaming_amd import kq, synth
+from tests.gpu_cases import check_dequant, check_y, oracle_rows, sample_rows, say, x_host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+DEV = "cuda:0"
+
+
+def run_case(qtype, rows, cols, batch, xdtype, seed, merge=0.0, check_w=True):
+    say(f"case {qtype} rows={rows} cols={cols} B={batch} x={xdtype} seed={seed}")
+    g = synth.gen_weights(qtype, rows, cols, synth.seed_of("w", seed), merge_frac=merge)
+    x = synth.gen_x(batch, cols, synth.seed_of("x", seed), xdtype)
+    gd = g.to(DEV)
+    w = kq.repack(qtype, gd, rows, cols)
+    y = kq.gemv(qtype, w, rows, cols, x.to(DEV))
+    torch.cuda.synchronize()
+    yo, ao = O.gemv(qtype, rows, cols, g.numpy(), x_host(x))
+    worst = check_y(y.cpu().numpy(), yo, ao, f"{qtype} {rows}x{cols} B={batch} {xdtype}")
+    if check_w:
+        check_dequant(qtype, w, rows, cols, g.numpy(), np.arange(rows), f"{qtype} {rows}x{cols}")
+    return worst
+
+
+def test_config0_exact():
+    """Q4_K 256 x 1024, batch 1, fp32 x ~ N(0,1), seed 0."""
+    run_case("q4k", 256, 1024, 1, "f32", 0)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8])
+def test_small_ragged(qtype, xdtype, batch):
+    # 4 row tiles (the last one 17 rows), 5 super-block columns
+    run_case(qtype, 3 * 64 + 17, 5 * 256, batch, xdtype, 100 + batch, check_w=(batch == 1))
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_units_span_tiles(qtype, batch):
+    # 301 tiles x 20 columns: each wavefront takes a run of units that starts and ends inside tiles
+    run_case(qtype, 300 * 64 + 37, 20 * 256, batch, "bf16", 200 + batch, check_w=False)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q6k"])
+def test_long_rows_split_many_ways(qtype):
+    # 5 tiles x 122 columns (the down projection's K): one unit per wavefront, 122 partials per tile
+    run_case(qtype, 300, 31232, 2, "bf16", 300)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+def test_single_row_single_column(qtype):
+    run_case(qtype, 1, 256, 3, "bf16", 400)
+    run_case(qtype, 1, 256, 1, "f32", 401)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+def test_multi_projection(qtype, xdtype):
+    parts = [100, 64, 37]
+    cols, batch = 1024, 3
+    say(f"case multi {qtype} parts={parts} x={xdtype}")
+    gs = [synth.gen_weights(qtype, r, cols, synth.seed_of("multi", qtype, i)) for i, r in enumerate(parts)]
+    x = synth.gen_x(batch, cols, 7, xdtype)
+    ws = [kq.repack(qtype, g.to(DEV), r, cols) for g, r in zip(gs, parts)]
+    # outputs with padded strides to check ldy handling
+    ys = [torch.full((batch, r + 5), float("nan"), device=DEV) for r in parts]
+    kq.kq_gemv_multi(qtype, ws, parts, cols, x.to(DEV), ys)
+    torch.cuda.synchronize()
+    for g, r, y in zip(gs, parts, ys):
+        yo, ao = O.gemv(qtype, r, cols, g.numpy(), x_host(x))
+        check_y(y[:, :r].cpu().numpy(), yo, ao, f"multi {qtype} part {r}")
+        assert torch.isnan(y[:, r:]).all(), "wrote outside [0, rows)"
+
+
+def _fields(qtype, n, rng):
+    d = torch.as_tensor(rng.integers(0x1000, 0x2C00, n))
+    if qtype == "q6k":
+        return dict(d=d, sc=torch.as_tensor(rng.integers(-64, 64, (n, 16))), q=torch.as_tensor(rng.integers(0, 64, (n, 256))))
+    qmax = 16 if qtype == "q4k" else 32
+    return dict(d=d, dmin=torch.as_tensor(rng.integers(0x1000, 0x2C00, n)), sc=torch.as_tensor(rng.integers(0, 64, (n, 8))),
+                m=torch.as_tensor(rng.integers(0, 64, (n, 8))), q=torch.as_tensor(rng.integers(0, qmax, (n, 256))))
+
+
+def _pack(qtype, f):
+    if qtype == "q6k":
+        return synth.pack_q6k(f["d"], f["sc"], f["q"])
+    p = synth.pack_q4k if qtype == "q4k" else synth.pack_q5k
+    return p(f["d"], f["dmin"], f["sc"], f["m"], f["q"])
+
+
+def _run_fields(qtype, f, rows, cols, x, where):
+    g = _pack(qtype, f).reshape(rows, -1)
+    w = kq.repack(qtype, g.to(DEV), rows, cols)
+    y = kq.gemv(qtype, w, rows, cols, x.to(DEV))
+    torch.cuda.synchronize()
+    yo, ao = O.gemv(qtype, rows, cols, g.numpy(), x_host(x))
+    check_y(y.cpu().numpy(), yo, ao, where)
+    check_dequant(qtype, w, rows, cols, g.numpy(), np.arange(rows), where)
+    return y.cpu().numpy(), yo, ao
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+def test_zero_rows_are_exactly_zero(qtype, xdtype):
+    """Rows whose weights are all zero give exactly 0: zero super-blocks (d = dmin = 0),
+    zero quants with zero mins (Q4_K/Q5_K), all quants 32 (Q6_K)."""
+    rows, cols = 130, 768
+    say(f"case zero rows {qtype} {xdtype}")
+    rng = np.random.default_rng(1)
+    f = _fields(qtype, rows * 3, rng)
+    sb = lambda r: slice(3 * r, 3 * r + 3)
+    zero_rows = [0, 5, 64, 129]
+    f["d"][sb(0)] = 0
+    if qtype != "q6k":
+        f["dmin"][sb(0)] = 0
+        f["q"][sb(5)] = 0; f["m"][sb(5)] = 0
+        f["q"][sb(64)] = 0; f["m"][sb(64)] = 0
+        f["d"][sb(129)] = 0; f["m"][sb(129)] = 0
+    else:
+        f["q"][sb(5)] = 32
+        f["q"][sb(64)] = 32
+        f["sc"][sb(129)] = 0
+    x = synth.gen_x(2, cols, 3, xdtype)
+    y, yo, ao = _run_fields(qtype, f, rows, cols, x, f"zero rows {qtype} {xdtype}")
+    for r in zero_rows:
+        assert np.all(ao[:, r] == 0) and np.all(y[:, r] == 0), f"row {r} not exactly zero"
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+def test_subnormal_and_extreme_scales(qtype):
+    rows, cols = 70, 512
+    say(f"case subnormal/extreme {qtype}")
+    rng = np.random.default_rng(2)
+    f = _fields(qtype, rows * 2, rng)
+    f["d"][:40] = torch.as_tensor(rng.integers(1, 0x400, 40))          # fp16 subnormal d
+    f["d"][40:50] = 0x7BFF                                             # 65504
+    if qtype != "q6k":
+        f["dmin"][20:60] = torch.as_tensor(rng.integers(1, 0x400, 40))
+        f["dmin"][60:70] = 0x7BFF
+    x = synth.gen_x(1, cols, 4, "bf16")
+    _run_fields(qtype, f, rows, cols, x, f"subnormal {qtype}")
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+def test_one_hot_picks_columns_exactly(qtype, xdtype):
+    """x = e_k gives y = W[:, k] bit-exactly: each weight is rounded once, like the dequantised value."""
+    rows, cols = 200, 1024
+    say(f"case one-hot {qtype} {xdtype}")
+    g = synth.gen_weights(qtype, rows, cols, 9)
+    ks = [0, 31, 32, 255, 256, 700, 1023, 513]
+    x = torch.zeros(len(ks), cols, dtype=torch.float32)
+    for b, k in enumerate(ks):
+        x[b, k] = 1.0
+    x = x.to(torch.bfloat16) if xdtype == "bf16" else x
+    w = kq.repack(qtype, g.to(DEV), rows, cols)
+    y = kq.gemv(qtype, w, rows, cols, x.to(DEV)).cpu().numpy()
+    W = O.dequant_f32(qtype, rows, cols, g.numpy())
+    for b, k in enumerate(ks):
+        assert np.array_equal(y[b], W[:, k]), f"column {k}"
+
+
+def test_zero_x_and_determinism():
+    rows, cols = 500, 2048
+    say("case zero-x / determinism")
+    g = synth.gen_weights("q6k", rows, cols, 10).to(DEV)
+    w = kq.repack("q6k", g, rows, cols)
+    y0 = kq.gemv("q6k", w, rows, cols, torch.zeros(4, cols, dtype=torch.bfloat16, device=DEV))
+    assert torch.all(y0 == 0)
+    x = synth.gen_x(8, cols, 11).to(DEV)
+    y1 = kq.gemv("q6k", w, rows, cols, x)
+    y2 = kq.gemv("q6k", w, rows, cols, x)
+    assert torch.equal(y1, y2)
+
+
+def test_strided_x():
+    rows, cols, batch = 128, 1024, 3
+    say("case strided x")
+    g = synth.gen_weights("q4k", rows, cols, 12)
+    xfull = synth.gen_x(batch, cols + 64, 13)
+    x = xfull[:, :cols]                       # row stride cols + 64 (128 B multiple)
+    w = kq.repack("q4k", g.to(DEV), rows, cols)
+    y = kq.gemv("q4k", w, rows, cols, xfull.to(DEV)[:, :cols])
+    yo, ao = O.gemv("q4k", rows, cols, g.numpy(), x_host(x))
+    check_y(y.cpu().numpy(), yo, ao, "strided x")
