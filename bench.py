@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Decode-step K-quant GEMV weight-streaming benchmark on one MI355X.
+
+One step = one decode-equivalent token: the 209 GEMVs of a synthetic 52-layer
+28B-class decoder, back to back on one stream:
+  52 x { QKV Q4_K 4608x5120 (one launch over q/k/v), O Q4_K 5120x4096,
+         gate+up Q4_K 62464x5120 (one launch over gate/up), down Q6_K 5120x31232 }
+  + head Q6_K 131072x5120  =  18,029,690,880 weight bytes.
+Weights are resident in HBM (repacked once, untimed); every GEMV has its own
+seeded bf16 activations.  The headline value is weight GB/s of the
+hipGraph-replayed sweep at batch 1; batch 8, plain stream launches, the
+Q5_K gate+up variant with merged sub-blocks (batch 2/4/8), per-kernel times,
+the roofline of the dominant kernel and the CPU oracle baseline are reported in
+the same JSON line.  Decode priced as weight bytes per token follows the Core AI
+card's decode table ("23.7 x 17.9 GB is 424 GB/s of traffic").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-c4]
+       python bench.py --profile-kernel N     # only the dominant kernel, N launches (for rocprofv3)
+       python bench.py --copy-calibration N   # N plain device copies of 1 GiB (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import dataclasses
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "K-quant GEMV weight GB/s (% of HBM peak) + decode-equiv tok/s, batch 1 and 8"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "quant_weight_streaming_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "quant_weight_streaming_amd", "build.py")]:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Sweep:
+    """Device-resident weights, activations and outputs of one sweep, with the launch list."""
+
+    def __init__(self, cfg: int, gate_up_type: str, batches, merge: float, sample_frac: float):
+        import torch
+        from quant_weight_streaming_amd import kq, synth
+        self.torch, self.kq, self.synth = torch, kq, synth
+        self.cfg, self.batches = cfg, list(batches)
+        self.entries = []          # (layer, spec, [repacked part tensors], parts)
+        self.samples = []          # (qtype, rows_sampled, cols, host gguf bytes, layer, spec name)
+        self.weight_bytes = 0
+        dev = "cuda:0"
+        t0 = time.time()
+        for layer, spec in synth.sweep(gate_up_type):
+            g = synth.gen_weights(spec.qtype, spec.rows, spec.cols, synth.seed_of(cfg, layer, spec.name),
+                                  device=dev, merge_frac=merge if spec.qtype == "q4k" else 0.0)
+            parts = list(spec.parts) or [spec.rows]
+            starts = [0]
+            for r in parts:
+                starts.append(starts[-1] + r)
+            reps = [kq.repack(spec.qtype, g[starts[i]:starts[i + 1]].contiguous(), r, spec.cols)
+                    for i, r in enumerate(parts)]
+            if sample_frac > 0:
+                rs = min(spec.rows, max(1, int(math.ceil(sample_frac * spec.rows))))
+                self.samples.append((spec.qtype, rs, spec.cols, g[:rs].cpu().numpy(), layer, spec.name))
+            self.weight_bytes += spec.rows * spec.cols // 256 * synth.SB_BYTES[spec.qtype]
+            self.entries.append((layer, spec, reps, parts))
+            del g
+        torch.cuda.synchronize()
+        log(f"[bench] cfg{cfg} sweep: {len(self.entries)} GEMVs, {self.weight_bytes} weight bytes, "
+            f"generated+repacked in {time.time() - t0:.1f} s")
+        self.x, self.y = {}, {}
+        for B in self.batches:
+            self.x[B] = [synth.gen_x(B, spec.cols, synth.seed_of(cfg, layer, spec.name, "x", B), "bf16", device=dev)
+                         for layer, spec, _, _ in self.entries]
+            self.y[B] = [[torch.empty((B, r), dtype=torch.float32, device=dev) for r in parts]
+                         for _, _, _, parts in self.entries]
+        self._keep = []
+
+    def calls(self, B: int, stream: int):
+        """Pre-marshalled C-ABI calls of one step (minimal Python work per launch)."""
+        L = self.kq.lib()
+        out = []
+        for i, (layer, spec, reps, parts) in enumerate(self.entries):
+            x, ys = self.x[B][i], self.y[B][i]
+            t = self.kq.TYPE_ID[spec.qtype]
+            if len(parts) > 1:
+                n = len(parts)
+                W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in reps])
+                R = (ctypes.c_int64 * n)(*parts)
+                Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+                LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
+                self._keep += [W, R, Y, LD]
+                out.append((L.kq_gemv_multi, (t, n, W, R, spec.cols, x.data_ptr(), 1, x.stride(0), B, Y, LD, stream),
+                            spec.name))
+            else:
+                fn = getattr(L, {"q4k": "kq_gemv_q4k", "q5k": "kq_gemv_q5k", "q6k": "kq_gemv_q6k"}[spec.qtype])
+                out.append((fn, (reps[0].data_ptr(), spec.rows, spec.cols, x.data_ptr(), 1, x.stride(0), B,
+                                 ys[0].data_ptr(), ys[0].stride(0), stream), spec.name))
+        return out
+
+
+def run_calls(calls):
+    for fn, args, name in calls:
+        rc = fn(*args)
+        if rc:
+            raise RuntimeError(f"{name}: GEMV launch failed with status {rc}")
+
+
+def time_sweep(sw: Sweep, B: int, steps: int, warmup: int):
+    """Plain stream launches and hipGraph replay of the whole sweep; returns ms per step for both."""
+    torch = sw.torch
+    stream = torch.cuda.current_stream()
+    calls = sw.calls(B, stream.cuda_stream)
+    for _ in range(warmup):
+        run_calls(calls)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run_calls(calls)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plain_ms = e0.elapsed_time(e1) / steps
+    ref = [[y.clone() for y in ys] for ys in sw.y[B]]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_calls(sw.calls(B, torch.cuda.current_stream().cuda_stream))
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    # every replay must reproduce the eager outputs bitwise (deterministic kernels)
+    for i in (0, 1, 2, 3, len(ref) - 1):
+        for y, r in zip(sw.y[B][i], ref[i]):
+            if not torch.equal(y, r):
+                raise RuntimeError(f"graph replay differs from eager launch (GEMV {i}, B={B})")
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    del g
+    return plain_ms, graph_ms
+
+
+def kernel_times(sw: Sweep, B: int, reps: int = 2):
+    """Average duration per GEMV class from per-launch HIP events on the launch stream."""
+    torch = sw.torch
+    stream = torch.cuda.current_stream()
+    calls = sw.calls(B, stream.cuda_stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    acc = {}
+    for _ in range(reps):
+        for (fn, args, name), (a, b) in zip(calls, ev):
+            a.record(stream)
+            rc = fn(*args)
+            if rc:
+                raise RuntimeError(f"{name}: status {rc}")
+            b.record(stream)
+        torch.cuda.synchronize()
+        for (fn, args, name), (a, b) in zip(calls, ev):
+            acc.setdefault(name, []).append(a.elapsed_time(b))
+    out = {}
+    for layer, spec, _, _ in sw.entries:
+        if spec.name in out:
+            continue
+        wb = spec.rows * spec.cols // 256 * sw.synth.SB_BYTES[spec.qtype]
+        ms = sum(acc[spec.name]) / len(acc[spec.name])
+        out[spec.name] = dict(qtype=spec.qtype, rows=spec.rows, cols=spec.cols, launches=len(acc[spec.name]),
+                              avg_us=round(ms * 1e3, 2), weight_gbs=round(wb / ms / 1e6, 1),
+                              weight_bytes=wb, x_bytes=B * spec.cols * 2, y_bytes=B * spec.rows * 4)
+    return out
+
+
+def cpu_baseline(sw: Sweep, frac: float):
+    """The CPU oracle on the sampled rows of every sweep tensor, batch 1 (compute time only)."""
+    from oracle import oracle as O
+    import numpy as np
+    torch = sw.torch
+    Or = O.default()
+    total_s, total_bytes = 0.0, 0
+    for (qtype, rs, cols, g, layer, name), xs in zip(sw.samples, sw.x[1]):
+        x = xs.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        t = time.perf_counter()
+        Or.gemv(qtype, rs, cols, g, x)
+        total_s += time.perf_counter() - t
+        total_bytes += g.nbytes
+    try:
+        threads = int(Or.L.omp_get_max_threads())
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    gbs = total_bytes / total_s / 1e9
+    return dict(value=round(gbs, 3), unit="GB/s", cores=threads, kind="oracle",
+                sample=(f"first {frac:.3f} of the rows of each of the 209 sweep tensors at batch 1 "
+                        f"({total_bytes} of {sw.weight_bytes} weight bytes), fp64 C oracle, {total_s:.1f} s"),
+                seconds=round(total_s, 2), decode_equiv_tok_s=round(gbs * 1e9 / sw.weight_bytes, 3))
+
+
+def oracle_rate_probe() -> float:
+    """Weight GB/s of the CPU oracle on a small Q4_K + Q6_K probe (sizes the baseline sample)."""
+    from oracle import oracle as O
+    from quant_weight_streaming_amd import synth
+    import numpy as np
+    import torch
+    t, nb = 0.0, 0
+    for qt, rows, cols in (("q4k", 1024, 5120), ("q6k", 128, 31232)):
+        g = synth.gen_weights(qt, rows, cols, 5).numpy()
+        x = synth.gen_x(1, cols, 6).view(torch.int16).numpy().view(np.uint16)
+        s = time.perf_counter()
+        O.gemv(qt, rows, cols, g, x)
+        t += time.perf_counter() - s
+        nb += g.nbytes
+    return nb / t / 1e9
+
+
+def load_traffic(name: str):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter summary, if it matches these kernels."""
+    p = os.path.join(ROOT, "profiles", f"{name}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def profile_kernel(n: int):
+    """Only the dominant kernel (gate+up Q4_K, batch 1): n launches over 8 distinct weight copies."""
+    import torch
+    from quant_weight_streaming_amd import kq, synth
+    spec = synth.GATE_UP
+    kq.kq_init(0)
+    copies = []
+    for i in range(8):
+        g = synth.gen_weights("q4k", spec.rows, spec.cols, synth.seed_of("prof", i), device="cuda:0")
+        copies.append([kq.repack("q4k", g[:spec.parts[0]].contiguous(), spec.parts[0], spec.cols),
+                       kq.repack("q4k", g[spec.parts[0]:].contiguous(), spec.parts[1], spec.cols)])
+        del g
+    x = synth.gen_x(1, spec.cols, 1, device="cuda:0")
+    ys = [torch.empty((1, r), device="cuda:0") for r in spec.parts]
+    for i in range(n):
+        kq.kq_gemv_multi("q4k", copies[i % 8], list(spec.parts), spec.cols, x, ys)
+    torch.cuda.synchronize()
+    log(f"[bench] profile-kernel: {n} launches done")
+
+
+def copy_calibration(n: int):
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(n):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy-calibration: {n} copies of {1 << 30} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-c4", action="store_true", help="skip the Q5_K / merged-sub-block sweep")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--profile-kernel", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}): the K-quant GEMV path "
+              f"is built and timed on a single MI355X; multi-GPU sharding is a design note, not a run.",
+              file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    if args.profile_kernel:
+        return profile_kernel(args.profile_kernel)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
+
+    import torch
+    from quant_weight_streaming_amd import kq, synth
+    kq.lib()                       # fails loudly if the HIP library is not built
+    kq.kq_init(0)
+
+    frac = 0.0
+    if not args.no_cpu:
+        rate = oracle_rate_probe()
+        frac = min(1.0, args.cpu_seconds * rate * 1e9 / synth.sweep_bytes("q4k"))
+        log(f"[bench] oracle probe {rate:.3f} GB/s -> sample fraction {frac:.3f}")
+
+    sw = Sweep(3, "q4k", (1, 8), 0.0, frac)
+    res = {}
+    for B in (1, 8):
+        plain, graph = time_sweep(sw, B, args.steps, args.warmup)
+        res[B] = dict(plain_ms=plain, graph_ms=graph)
+        log(f"[bench] cfg3 B={B}: plain {plain:.3f} ms ({sw.weight_bytes / plain / 1e6:.0f} GB/s), "
+            f"graph {graph:.3f} ms ({sw.weight_bytes / graph / 1e6:.0f} GB/s)")
+    kt1 = kernel_times(sw, 1)
+    kt8 = kernel_times(sw, 8)
+    cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
+    if cpu:
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads over {cpu['seconds']} s")
+
+    # roofline of the dominant kernel (gate+up, batch 1): algorithmic bytes per launch / mean launch time
+    gu = kt1["gate_up"]
+    alg = gu["weight_bytes"] + gu["x_bytes"] + gu["y_bytes"]
+    achieved = alg / (gu["avg_us"] * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=load_traffic("gate_up_q4k_b1_traffic"),
+                    kernel="gemv_kernel<Q4_K, B=1, bf16> (gate+up 62464x5120, one launch over both halves)",
+                    algorithmic_bytes_per_launch=alg, avg_launch_us=gu["avg_us"])
+
+    c4 = None
+    if not args.no_c4:
+        bytes3 = sw.weight_bytes
+        del sw
+        torch.cuda.empty_cache()
+        sw4 = Sweep(4, "q5k", (2, 4, 8), 0.25, 0.0)
+        c4 = {}
+        for B in (2, 4, 8):
+            plain, graph = time_sweep(sw4, B, max(3, args.steps // 2), args.warmup)
+            c4[f"b{B}"] = dict(graph_ms=round(graph, 4), plain_ms=round(plain, 4),
+                               weight_gbs=round(sw4.weight_bytes / graph / 1e6, 1),
+                               pct_of_hbm_peak=round(100 * sw4.weight_bytes / graph / 1e6 / HBM_PEAK_GBS, 2),
+                               tok_s=round(B / graph * 1e3, 1))
+            log(f"[bench] cfg4 B={B}: graph {graph:.3f} ms ({sw4.weight_bytes / graph / 1e6:.0f} GB/s)")
+        c4["weight_bytes"] = sw4.weight_bytes
+        c4["kernels_b8"] = kernel_times(sw4, 8)
+        sw = None
+    else:
+        bytes3 = sw.weight_bytes
+
+    g1 = res[1]["graph_ms"]
+    gbs1 = bytes3 / g1 / 1e6
+    line = {
+        "metric": METRIC,
+        "value": round(gbs1, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g1, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sweep52_q4k_q6k: 52 x {QKV Q4_K 4608x5120, O Q4_K 5120x4096, gate+up Q4_K "
+                               "62464x5120, down Q6_K 5120x31232} + head Q6_K 131072x5120",
+                   "weight_bytes": bytes3, "batch": 1, "launch": "hipGraph replay of 209 GEMV launches",
+                   "x": "bf16 N(0,1), own seed per GEMV", "y": "fp32"},
+        "pct_of_hbm_peak": round(100 * gbs1 / HBM_PEAK_GBS, 2),
+        "decode_equiv_tok_s": round(1e3 / g1, 1),
+        "batch8": {"graph_ms": round(res[8]["graph_ms"], 4), "plain_ms": round(res[8]["plain_ms"], 4),
+                   "weight_gbs": round(bytes3 / res[8]["graph_ms"] / 1e6, 1),
+                   "pct_of_hbm_peak": round(100 * bytes3 / res[8]["graph_ms"] / 1e6 / HBM_PEAK_GBS, 2),
+                   "tok_s": round(8e3 / res[8]["graph_ms"], 1)},
+        "batch1_plain_launch": {"ms": round(res[1]["plain_ms"], 4),
+                                "weight_gbs": round(bytes3 / res[1]["plain_ms"] / 1e6, 1)},
+        "kernels_b1": kt1,
+        "kernels_b8": kt8,
+        "c4_q5k_merged": c4,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -74,13 +74,11 @@ static int device_state(int dev, DeviceState** out) {
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Target resident wavefronts per CU (tuning knob; KQ_WAVES_PER_CU overrides the default).
 static int waves_per_cu() {
-  static int v = [] {
-    const char* e = getenv("KQ_WAVES_PER_CU");
-    int x = e ? atoi(e) : 0;
-    return (x >= 1 && x <= 32) ? x : 8;
-  }();
-  return v;
+  const char* e = getenv("KQ_WAVES_PER_CU");
+  const int x = e ? atoi(e) : 0;
+  return (x >= 1 && x <= 32) ? x : 8;
 }
 
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,

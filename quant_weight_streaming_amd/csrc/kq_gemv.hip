@@ -153,32 +153,39 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, int t, bool full,
     }
     return;
   }
+  // Hand-off without an L2 writeback: the partials are written with agent-scope
+  // atomic stores (write-through to the device coherence point), the wavefront
+  // waits until they are acknowledged, and only then bumps the tile's counter.
+  // The last arrival reads the partials with agent-scope atomic loads, which
+  // bypass the (per-XCD) caches.
   const int n_cols = a.n_cols, upw = a.upw;
   const int slot = (t == u0 / n_cols) ? 0 : 1;
   float* mine = a.partial + (int64_t)(w * 2 + slot) * kPartialStride;
 #pragma unroll
-  for (int b = 0; b < B; ++b) mine[b * kTileRows + lane] = acc[b];
-  __threadfence();
+  for (int b = 0; b < B; ++b)
+    __hip_atomic_store(mine + b * kTileRows + lane, acc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const int wa = (t * n_cols) / upw, wb = ((t + 1) * n_cols - 1) / upw;
   uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(&a.counters[wa], 1u);
+  if (lane == 0) old = __hip_atomic_fetch_add(&a.counters[wa], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   if (old != (uint32_t)(wb - wa)) return;
-  __threadfence();
+  asm volatile("" ::: "memory");
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
   for (int wc = wa; wc <= wb; ++wc) {
     const int sl = (t == (wc * upw) / n_cols) ? 0 : 1;
-    const float* pp = a.partial + (int64_t)(wc * 2 + sl) * kPartialStride;
+    float* pp = a.partial + (int64_t)(wc * 2 + sl) * kPartialStride;
 #pragma unroll
-    for (int b = 0; b < B; ++b) s[b] += pp[b * kTileRows + lane];
+    for (int b = 0; b < B; ++b)
+      s[b] += __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (live) {
 #pragma unroll
     for (int b = 0; b < B; ++b) y[b * ldy + row] = s[b];
   }
-  if (lane == 0) atomicExch(&a.counters[wa], 0u);
+  if (lane == 0) __hip_atomic_store(&a.counters[wa], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int QT, int B, bool XF32>
@@ -186,7 +193,9 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   using F = Fmt<QT>;
   constexpr int NCH = F::kChunks;
   extern __shared__ float lds_t[];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // readfirstlane: the wavefront index is uniform across the wavefront; saying so
+  // keeps all unit/column bookkeeping and the activation addresses in SGPRs.
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Blocks are dispatched round-robin over the 8 XCDs; give consecutive logical
   // blocks (which share split tiles) to one XCD so partial sums stay in its L2.
   const int nb8 = gridDim.x >> 3;
