@@ -23,12 +23,13 @@ int64_t sb_bytes(int type) {
 
 static int sub_blocks(int type) { return type == KQ_Q6_K ? 16 : 8; }
 
-// Scratch for K-split row tiles: two partial-sum slots and one arrival counter
-// per wavefront.  The counters are zero between calls (the last arrival of a
-// tile resets its counter), so they are cleared once, at allocation.
-constexpr int kMaxWaves = 8192;
-constexpr size_t kPartialBytes = (size_t)kMaxWaves * 2 * KQ_MAX_BATCH * 64 * sizeof(float);
-constexpr size_t kCounterBytes = (size_t)kMaxWaves * sizeof(uint32_t);
+// Scratch for row tiles whose columns span several workgroups: two partial-sum
+// slots and one arrival counter per workgroup.  The counters are zero between
+// calls (the last arrival of a tile resets its counter), so they are cleared
+// once, at allocation.
+constexpr int kMaxGroups = 8192;
+constexpr size_t kPartialBytes = (size_t)kMaxGroups * 2 * KQ_MAX_BATCH * 64 * sizeof(float);
+constexpr size_t kCounterBytes = (size_t)kMaxGroups * sizeof(uint32_t);
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
@@ -112,7 +113,7 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   }
   for (int i = n; i <= KQ_MAX_PROJ; ++i) a.tile_begin[i] = (int32_t)tiles;
   const int64_t n_units = tiles * n_cols;
-  if (n_units + 2 * n_cols + 4 * (int64_t)kMaxWaves >= INT32_MAX) return KQ_ERR_RANGE;
+  if (n_units + 2 * n_cols + 8 * (int64_t)kMaxGroups >= INT32_MAX) return KQ_ERR_RANGE;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
@@ -120,35 +121,36 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   int rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
 
-  // Launch geometry: an even run of units per wavefront, about waves_per_cu()
-  // wavefronts per CU; the activation sums of the columns one wavefront touches
-  // must fit 16 KiB of LDS per wavefront.
+  // Launch geometry: an even run of `upw` units per wavefront, about
+  // waves_per_cu() wavefronts per CU, four wavefronts per workgroup.  A
+  // workgroup stages the activations and sub-block sums of the columns its
+  // 4*upw units touch in LDS (at most 64 KiB), plus its wavefronts' partial sums.
   const int64_t target = (int64_t)st->cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
-  const int64_t per_col = (int64_t)sub_blocks(type) * batch;   // LDS floats per column
-  const int64_t cap = 4096 / per_col;                            // columns that fit 16 KiB
-  if (n_cols > cap && upw > cap) upw = cap;
-  int64_t n_waves = (n_units + upw - 1) / upw;
-  if (n_waves > kMaxWaves) {
-    upw = (n_units + kMaxWaves - 1) / kMaxWaves;
-    if (n_cols > cap && upw > cap) return KQ_ERR_RANGE;
-    n_waves = (n_units + upw - 1) / upw;
+  const int64_t xwords = xtype == KQ_X_F32 ? 256 : 128;                   // x words per column and row
+  const int64_t per_col = (int64_t)batch * 4 * (xwords + sub_blocks(type));  // LDS bytes per staged column
+  const int64_t max_cols = 65536 / per_col;
+  if (n_cols > max_cols && 4 * upw > max_cols) upw = max_cols / 4 > 0 ? max_cols / 4 : 1;
+  if (upw > n_cols + 1) upw = n_cols + 1;   // a wavefront's run then touches at most two tiles
+  int64_t n_groups = (n_units + 4 * upw - 1) / (4 * upw);
+  if (n_groups > kMaxGroups) {
+    upw = (n_units + 4 * (int64_t)kMaxGroups - 1) / (4 * (int64_t)kMaxGroups);
+    if ((n_cols > max_cols && 4 * upw > max_cols) || upw > n_cols + 1) return KQ_ERR_RANGE;
+    n_groups = (n_units + 4 * upw - 1) / (4 * upw);
   }
-  const int64_t tcols = n_cols < upw ? n_cols : upw;
+  const int64_t tcols = n_cols < 4 * upw ? n_cols : 4 * upw;
   a.nproj = n;
   a.n_cols = (int32_t)n_cols;
   a.x = x;
   a.ldx = ldx;
   a.n_units = (int32_t)n_units;
   a.upw = (int32_t)upw;
-  a.n_waves = (int32_t)n_waves;
-  a.tsb = (int32_t)(tcols * sub_blocks(type));
+  a.tsb = (int32_t)tcols;
   a.partial = st->partial;
   a.counters = st->counters;
-  const size_t lds = (size_t)4 * a.tsb * batch * sizeof(float);
-  int64_t grid = (n_waves + 3) / 4;
-  grid = (grid + 7) / 8 * 8;  // whole XCD rounds for the block remap
+  const size_t lds = (size_t)tcols * per_col + (size_t)8 * batch * 64 * sizeof(float);
+  const int64_t grid = (n_groups + 7) / 8 * 8;  // whole XCD rounds for the block remap
   if (launch_gemv(type, xtype, batch, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;

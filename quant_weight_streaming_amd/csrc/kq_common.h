@@ -62,6 +62,14 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   return v;
 }
 
+// (a & m) | b in one v_and_or_b32 (the compiler otherwise splits the Q6_K
+// three-way merge into and/and/or3).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
 }
@@ -99,8 +107,8 @@ __device__ __forceinline__ void unpack_pairs(const u32x4* c, int G, uint32_t M, 
     }
     if constexpr (QT == KQ_Q5_K) {
       const uint32_t H = word(c[9 + G / 4], G % 4);
-      const uint32_t M5 = 0x00100010u;
-#define KQ_Q5_HB(PI) pr[PI] |= shift_signed<(PI) - 4>(H) & M5;
+      const uint32_t M5 = in_vgpr(0x00100010u);
+#define KQ_Q5_HB(PI) pr[PI] = and_or(shift_signed<(PI) - 4>(H), M5, pr[PI]);
       KQ_Q5_HB(0) KQ_Q5_HB(1) KQ_Q5_HB(2) KQ_Q5_HB(3) KQ_Q5_HB(4) KQ_Q5_HB(5) KQ_Q5_HB(6) KQ_Q5_HB(7)
       KQ_Q5_HB(8) KQ_Q5_HB(9) KQ_Q5_HB(10) KQ_Q5_HB(11) KQ_Q5_HB(12) KQ_Q5_HB(13) KQ_Q5_HB(14) KQ_Q5_HB(15)
 #undef KQ_Q5_HB
@@ -109,18 +117,12 @@ __device__ __forceinline__ void unpack_pairs(const u32x4* c, int G, uint32_t M, 
     const u32x4 lq = c[G / 2];
     const uint32_t L0 = word(lq, (G % 2) * 2), L1 = word(lq, (G % 2) * 2 + 1);
     const uint32_t H = word(c[8 + G / 4], G % 4);
-    const uint32_t M6 = 0x00300030u;
-    pr[0] = (L0 & M) | K;
-    pr[1] = ((L0 >> 4) & M) | K;
-    pr[2] = ((L0 >> 8) & M) | K;
-    pr[3] = ((L0 >> 12) & M) | K;
-    pr[4] = (L1 & M) | K;
-    pr[5] = ((L1 >> 4) & M) | K;
-    pr[6] = ((L1 >> 8) & M) | K;
-    pr[7] = ((L1 >> 12) & M) | K;
-#define KQ_Q6_HB(PI) pr[PI] |= shift_signed<2 * (PI) - 4>(H) & M6;
-    KQ_Q6_HB(0) KQ_Q6_HB(1) KQ_Q6_HB(2) KQ_Q6_HB(3) KQ_Q6_HB(4) KQ_Q6_HB(5) KQ_Q6_HB(6) KQ_Q6_HB(7)
-#undef KQ_Q6_HB
+    const uint32_t M6 = in_vgpr(0x00300030u);
+    // pair pi: nibbles of L_{pi/4} >> 4(pi%4), two high bits of H >> (2pi - 4)
+#define KQ_Q6_PAIR(PI, L, P) pr[PI] = and_or(shift_signed<2 * (PI) - 4>(H), M6, and_or(shift_signed<4 * (P)>(L), M, K));
+    KQ_Q6_PAIR(0, L0, 0) KQ_Q6_PAIR(1, L0, 1) KQ_Q6_PAIR(2, L0, 2) KQ_Q6_PAIR(3, L0, 3)
+    KQ_Q6_PAIR(4, L1, 0) KQ_Q6_PAIR(5, L1, 1) KQ_Q6_PAIR(6, L1, 2) KQ_Q6_PAIR(7, L1, 3)
+#undef KQ_Q6_PAIR
   }
 }
 

@@ -3,29 +3,42 @@
 // Work decomposition.  A "unit" is one tile column: 64 rows (lane == row) x one
 // 256-weight super-block column, 9 / 11 / 13 KiB of weights read as coalesced
 // 1 KiB wavefront loads.  Units are ordered tile-major (all columns of tile 0,
-// then tile 1, ...) and each wavefront takes a contiguous run of `upw` of them,
-// so the chip is filled with an even share per wavefront whatever the matrix
-// shape.  A tile whose columns span several wavefronts is finished by the last
-// of them to arrive: each writes its partial row sums to scratch, bumps a
-// counter, and the last one adds the partials in wavefront order (fixed order,
-// so the result is deterministic) and resets the counter for the next call.
+// then tile 1, ...); each wavefront takes a contiguous run of `upw` units and a
+// workgroup the runs of its 4 wavefronts, so the chip gets an even share per
+// wavefront whatever the matrix shape.  Per-tile sums go to LDS; after the
+// main loop the workgroup adds its wavefronts' pieces of each tile in
+// wavefront order, writes y for tiles it covered completely, and hands the
+// rest to the other workgroups sharing the tile (the last to arrive adds all
+// pieces in workgroup order).  Fixed summation orders make y deterministic.
 //
 // Per super-block and lane the 4/5/6-bit quants become bf16 pairs (128 + q)
-// with shift/and-or only, and v_dot2_f32_bf16 takes the activation pair
-// straight from scalar registers: all 64 lanes of a wavefront share the column
-// and so the same activations, which arrive with scalar loads.  Per sub-block
-// the sum S of (128 + q) * x is corrected with T, the same chain of dot2 over
-// (128, 128) (Q6_K: (160, 160) = 128 + 32), computed once per wavefront into
-// LDS; when every q is zero (Q6_K: 32) S and T are bitwise equal and the
-// sub-block contributes exactly zero.  Then
+// with shift/and-or only, and v_dot2_f32_bf16 dots them with the activation
+// pair of the same position.  All 64 lanes (rows) of a wavefront share the
+// column, so the activations are wavefront-uniform; the workgroup stages the
+// activations of its columns in LDS once and every wavefront reads them with
+// broadcast LDS loads.  Per sub-block the sum S of (128 + q) * x is corrected
+// with T, the same chain of dot2 over (128, 128) (Q6_K: (160, 160) = 128 + 32),
+// staged alongside; when every q is zero (Q6_K: 32) S and T are bitwise equal
+// and the sub-block contributes exactly zero.  Then
 //   Q4_K/Q5_K: acc += (d*sc) * (S - T) - (dmin*m/128) * T
 //   Q6_K     : acc += (d*sc) * (S - T).
 // With fp32 activations the weights are converted to exact fp32 q and used
 // with v_fma (S = sum q*x, T = sum x).
+//
+// The weight stream is buffered in registers: while one unit is computed the
+// next DEPTH-1 are in flight.  The main loop issues its refills
+// unconditionally and keeps global stores out of the loop, so the compiler can
+// wait for exactly the unit it consumes instead of for every load in flight.
 #include "kq_common.h"
 #include "kq_internal.h"
 
+#ifndef KQ_DEPTH
+#define KQ_DEPTH 2
+#endif
+
 namespace kq {
+
+constexpr int kTilesPerWave = 2;   // a wavefront's run of units touches at most this many tiles
 
 template <int QT>
 __device__ __forceinline__ const uint8_t* unit_base(const GemvArgs& a, int t, int c) {
@@ -47,216 +60,282 @@ __device__ __forceinline__ void load_unit(const uint8_t* base, int lane, u32x4* 
   }
 }
 
-typedef const __attribute__((address_space(4))) uint32_t* sword_ptr;
-typedef const __attribute__((address_space(4))) float* sfloat_ptr;
-
-// T[i*B + b] for the ncols_t columns c0, c0+1, ... (mod n_cols) that this wavefront touches.
+// Stage the activations of the workgroup's columns c0, c0+1, ... (mod n_cols)
+// in LDS, and T, the per-sub-block activation sums in the dot product's own
+// order (bf16: the same dot2 chain over (128,128), Q6_K (160,160); fp32: sum x).
+// X layout: [ic][b][256 elements]; T layout: [ic * sub-blocks + g][b].
 template <int QT, int B, bool XF32>
-__device__ __forceinline__ void compute_T(const GemvArgs& a, float* T, int c0, int ncols_t, int lane) {
+__device__ __forceinline__ void stage_x_T(const GemvArgs& a, uint32_t* X, float* T, int c0, int len) {
   using F = Fmt<QT>;
-  if constexpr (!(XF32 && QT == KQ_Q6_K)) {
-    const int n = ncols_t * F::kSubBlocks;
-    for (int i = lane; i < n; i += 64) {
-      const int ic = i / F::kSubBlocks, g = i - ic * F::kSubBlocks;
-      int c = c0 + ic;
-      if (c >= a.n_cols) c -= a.n_cols;
-      const int64_t k0 = (int64_t)c * 256 + g * F::kSubW;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        float t = 0.0f;
-        if constexpr (!XF32) {
-          const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + b * a.ldx + k0);
-          const uint32_t Kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;  // bf16 (160,160) / (128,128)
-#pragma unroll
-          for (int v = 0; v < F::kPairs / 4; ++v) {
-            const u32x4 xv = xp[v];
-            t = dot2_bf16(Kc, xv.x, t);
-            t = dot2_bf16(Kc, xv.y, t);
-            t = dot2_bf16(Kc, xv.z, t);
-            t = dot2_bf16(Kc, xv.w, t);
-          }
-        } else {
-          const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + b * a.ldx + k0);
-#pragma unroll
-          for (int v = 0; v < F::kSubW / 4; ++v) {
-            const float4 xv = xp[v];
-            t += xv.x;
-            t += xv.y;
-            t += xv.z;
-            t += xv.w;
-          }
-        }
-        T[i * B + b] = t;
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Accumulate one unit (tile column c, T column index ic) into acc[B].
-template <int QT, int B, bool XF32>
-__device__ __forceinline__ void process_unit(const GemvArgs& a, const u32x4* buf, uint32_t d6, int c, int ic,
-                                             const float* T, float* acc, uint32_t M, uint32_t K) {
-  using F = Fmt<QT>;
-  constexpr int SB = F::kSubBlocks, NP = F::kPairs;
-  float ca[SB], cm[SB];
-  sb_coeffs<QT>(buf, d6, XF32 ? 1.0f : 0.0078125f, ca, cm);
-#pragma unroll
-  for (int g = 0; g < SB; ++g) {
-    uint32_t pr[NP];
-    unpack_pairs<QT>(buf, g, M, K, pr);
+  constexpr int XW = XF32 ? 256 : 128;              // 32-bit words of x per column and batch row
+  constexpr int SW = XF32 ? F::kSubW : F::kSubW / 2;  // words per sub-block
+  const int n = len * F::kSubBlocks;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int ic = i / F::kSubBlocks, g = i - ic * F::kSubBlocks;
+    int c = c0 + ic;
+    if (c >= a.n_cols) c -= a.n_cols;
     const int64_t k0 = (int64_t)c * 256 + g * F::kSubW;
-    const float* Tg = T + (ic * SB + g) * B;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      float s = 0.0f;
-      if constexpr (!XF32) {
-        sword_ptr xw = (sword_ptr)(a.x) + ((b * a.ldx + k0) >> 1);
+      const u32x4* xp = XF32 ? reinterpret_cast<const u32x4*>(static_cast<const float*>(a.x) + b * a.ldx + k0)
+                             : reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + b * a.ldx + k0);
+      u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * XW + g * SW);
+      float t = 0.0f;
+      const uint32_t Kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;  // bf16 (160,160) / (128,128)
 #pragma unroll
-        for (int i = 0; i < NP; ++i) s = dot2_bf16(pr[i], xw[i], s);
-        const float t = Tg[b];
-        acc[b] = __builtin_fmaf(ca[g], s - t, acc[b]);
-        if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], t, acc[b]);
-      } else {
-        sfloat_ptr xf = (sfloat_ptr)(a.x) + (b * a.ldx + k0);
-        const float off = (QT == KQ_Q6_K) ? 160.0f : 128.0f;  // (128 + q) - off = q, or q - 32
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          s = __builtin_fmaf(bf16_lo(pr[i]) - off, xf[2 * i], s);
-          s = __builtin_fmaf(bf16_hi(pr[i]) - off, xf[2 * i + 1], s);
+      for (int v = 0; v < SW / 4; ++v) {
+        const u32x4 xv = xp[v];
+        xl[v] = xv;
+        if constexpr (!XF32) {
+          t = dot2_bf16(Kc, xv.x, t);
+          t = dot2_bf16(Kc, xv.y, t);
+          t = dot2_bf16(Kc, xv.z, t);
+          t = dot2_bf16(Kc, xv.w, t);
+        } else {
+          t += __uint_as_float(xv.x);
+          t += __uint_as_float(xv.y);
+          t += __uint_as_float(xv.z);
+          t += __uint_as_float(xv.w);
         }
-        acc[b] = __builtin_fmaf(ca[g], s, acc[b]);
-        if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], Tg[b], acc[b]);
       }
+      T[i * B + b] = t;
     }
   }
 }
 
-// Tile t's run of units ended in this wavefront: write y, or hand over a partial.
+// Accumulate one unit into acc[B].  Xc / Tc: the staged activations and sums of
+// the unit's column.  The (sub-block, batch row) steps are software-pipelined:
+// each step reads the next step's activations from LDS before its own dot
+// products, and a scheduling barrier keeps the compiler from hoisting reads any
+// further (which would cost registers and occupancy).
+template <int QT, int B, bool XF32>
+__device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, const uint32_t* Xc, const float* Tc,
+                                             float* acc, uint32_t M, uint32_t K) {
+  using F = Fmt<QT>;
+  constexpr int SB = F::kSubBlocks, NP = F::kPairs;
+  constexpr int XW = XF32 ? 256 : 128;
+  constexpr int NV = XF32 ? NP / 2 : NP / 4;        // 16-byte LDS reads per sub-block and batch row
+  constexpr int SWD = XF32 ? F::kSubW : F::kSubW / 2;
+  float ca[SB], cm[SB];
+  sb_coeffs<QT>(buf, d6, XF32 ? 1.0f : 0.0078125f, ca, cm);
+  u32x4 xc[NV], xn[NV];
+  float tc, tn = 0.0f;
+  {
+    const u32x4* xl = reinterpret_cast<const u32x4*>(Xc);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) xc[v] = xl[v];
+    tc = Tc[0];
+  }
+  uint32_t pr[NP];
+#pragma unroll
+  for (int g = 0; g < SB; ++g) {
+    unpack_pairs<QT>(buf, g, M, K, pr);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int gn = (b + 1 < B) ? g : g + 1, bn = (b + 1 < B) ? b + 1 : 0;
+      if (gn < SB) {
+        const u32x4* xl = reinterpret_cast<const u32x4*>(Xc + bn * XW + gn * SWD);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) xn[v] = xl[v];
+        tn = Tc[gn * B + bn];
+      }
+      float s = 0.0f;
+      if constexpr (!XF32) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          s = dot2_bf16(pr[4 * v + 0], xc[v].x, s);
+          s = dot2_bf16(pr[4 * v + 1], xc[v].y, s);
+          s = dot2_bf16(pr[4 * v + 2], xc[v].z, s);
+          s = dot2_bf16(pr[4 * v + 3], xc[v].w, s);
+        }
+        acc[b] = __builtin_fmaf(ca[g], s - tc, acc[b]);
+        if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
+      } else {
+        const float off = (QT == KQ_Q6_K) ? 160.0f : 128.0f;  // (128 + q) - off = q, or q - 32
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          s = __builtin_fmaf(bf16_lo(pr[2 * v]) - off, __uint_as_float(xc[v].x), s);
+          s = __builtin_fmaf(bf16_hi(pr[2 * v]) - off, __uint_as_float(xc[v].y), s);
+          s = __builtin_fmaf(bf16_lo(pr[2 * v + 1]) - off, __uint_as_float(xc[v].z), s);
+          s = __builtin_fmaf(bf16_hi(pr[2 * v + 1]) - off, __uint_as_float(xc[v].w), s);
+        }
+        acc[b] = __builtin_fmaf(ca[g], s, acc[b]);
+        if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) xc[v] = xn[v];
+      tc = tn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Write finished row sums of tile t (all of its columns) to y.
 template <int B>
-__device__ __forceinline__ void finish_tile(const GemvArgs& a, int t, bool full, int w, int u0, int lane,
-                                            float* acc) {
+__device__ __forceinline__ void write_tile(const GemvArgs& a, int t, int lane, const float* v) {
   int p = 0;
 #pragma unroll
   for (int i = 1; i < KQ_MAX_PROJ; ++i)
     if (i < a.nproj && t >= a.tile_begin[i]) p = i;
   const int row = (t - a.tile_begin[p]) * kTileRows + lane;
-  float* y = a.y[p];
-  const int64_t ldy = a.ldy[p];
-  const bool live = row < a.rows[p];
-  if (full) {
-    if (live) {
+  if (row < a.rows[p]) {
+    float* y = a.y[p];
+    const int64_t ldy = a.ldy[p];
 #pragma unroll
-      for (int b = 0; b < B; ++b) y[b * ldy + row] = acc[b];
-    }
-    return;
+    for (int b = 0; b < B; ++b) y[b * ldy + row] = v[b];
   }
-  // Hand-off without an L2 writeback: the partials are written with agent-scope
-  // atomic stores (write-through to the device coherence point), the wavefront
-  // waits until they are acknowledged, and only then bumps the tile's counter.
-  // The last arrival reads the partials with agent-scope atomic loads, which
-  // bypass the (per-XCD) caches.
-  const int n_cols = a.n_cols, upw = a.upw;
-  const int slot = (t == u0 / n_cols) ? 0 : 1;
-  float* mine = a.partial + (int64_t)(w * 2 + slot) * kPartialStride;
+}
+
+// Workgroup L holds its sum for tile t, whose columns other workgroups share.
+// Hand it over; the last workgroup to arrive adds all of them in workgroup
+// order and writes y.  No L2 writeback is needed: the partials are written with
+// agent-scope atomic stores (write-through to the device coherence point), the
+// wavefront waits until they are acknowledged before bumping the tile's
+// counter, and the last arrival reads them with agent-scope atomic loads, which
+// bypass the per-XCD caches.  The counter is reset for the next call.
+template <int B>
+__device__ __forceinline__ void hand_off(const GemvArgs& a, int t, int L, int wgu, int lane, const float* v) {
+  const int n_cols = a.n_cols;
+  const int slot = (t == (L * wgu) / n_cols) ? 0 : 1;
+  float* mine = a.partial + (int64_t)(L * 2 + slot) * kPartialStride;
 #pragma unroll
   for (int b = 0; b < B; ++b)
-    __hip_atomic_store(mine + b * kTileRows + lane, acc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + b * kTileRows + lane, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  const int wa = (t * n_cols) / upw, wb = ((t + 1) * n_cols - 1) / upw;
+  const int la = (t * n_cols) / wgu, lb = ((t + 1) * n_cols - 1) / wgu;
   uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(&a.counters[wa], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = __hip_atomic_fetch_add(&a.counters[la], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
-  if (old != (uint32_t)(wb - wa)) return;
+  if (old != (uint32_t)(lb - la)) return;
   asm volatile("" ::: "memory");
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
-  for (int wc = wa; wc <= wb; ++wc) {
-    const int sl = (t == (wc * upw) / n_cols) ? 0 : 1;
-    float* pp = a.partial + (int64_t)(wc * 2 + sl) * kPartialStride;
+  for (int l = la; l <= lb; ++l) {
+    const int sl = (t == (l * wgu) / n_cols) ? 0 : 1;
+    float* pp = a.partial + (int64_t)(l * 2 + sl) * kPartialStride;
 #pragma unroll
     for (int b = 0; b < B; ++b)
       s[b] += __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (live) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) y[b * ldy + row] = s[b];
-  }
-  if (lane == 0) __hip_atomic_store(&a.counters[wa], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  write_tile<B>(a, t, lane, s);
+  if (lane == 0) __hip_atomic_store(&a.counters[la], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT, int B, bool XF32>
+template <int QT, int B, bool XF32, int DEPTH>
 __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   using F = Fmt<QT>;
-  constexpr int NCH = F::kChunks;
-  extern __shared__ float lds_t[];
+  constexpr int NCH = F::kChunks, SB = F::kSubBlocks;
+  constexpr int XW = XF32 ? 256 : 128;
+  extern __shared__ uint32_t lds_words[];
   // readfirstlane: the wavefront index is uniform across the wavefront; saying so
-  // keeps all unit/column bookkeeping and the activation addresses in SGPRs.
+  // keeps all unit/column bookkeeping in SGPRs.
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Blocks are dispatched round-robin over the 8 XCDs; give consecutive logical
-  // blocks (which share split tiles) to one XCD so partial sums stay in its L2.
+  // Blocks are dispatched round-robin over the 8 XCDs; consecutive logical
+  // blocks (which share split tiles) go to one XCD.
   const int nb8 = gridDim.x >> 3;
   const int lblock = (blockIdx.x & 7) * nb8 + (blockIdx.x >> 3);
-  const int w = lblock * 4 + wid;
-  if (w >= a.n_waves) return;
-  const int n_cols = a.n_cols;
-  const int u0 = w * a.upw;
-  const int u1 = min(u0 + a.upw, a.n_units);
-  const int c0 = u0 % n_cols;
-  float* T = lds_t + wid * a.tsb * B;
+  const int n_cols = a.n_cols, upw = a.upw, wgu = 4 * upw;
+  const int U0 = lblock * wgu;                     // the workgroup's run of units [U0, U1)
+  if (U0 >= a.n_units) return;                     // whole workgroup idle
+  const int U1 = min(U0 + wgu, a.n_units);
+  const int c0w = U0 % n_cols;
+  const int len = min(n_cols, U1 - U0);
+  uint32_t* X = lds_words;
+  float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);
+  float* P = T + a.tsb * SB * B;                   // per-wavefront tile sums [4][kTilesPerWave][B][64]
+  const int u0 = U0 + wid * upw;
+  const int u1 = min(u0 + upw, U1);
+  const bool active = u0 < U1;
+  const int t0 = u0 / n_cols;                      // first tile of this wavefront
   const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
 
-  // Weight loads for the first two units go out before the activation sums,
-  // so their latency overlaps.
-  u32x4 bA[NCH], bB[NCH];
-  uint32_t dA = 0, dB = 0;
-  int tl = u0 / n_cols, cl = c0;  // next unit to load
-  load_unit<QT>(unit_base<QT>(a, tl, cl), lane, bA, dA);
-  if (++cl == n_cols) { cl = 0; ++tl; }
-  if (u0 + 1 < u1) load_unit<QT>(unit_base<QT>(a, tl, cl), lane, bB, dB);
-  if (++cl == n_cols) { cl = 0; ++tl; }
-
-  compute_T<QT, B, XF32>(a, T, c0, min(n_cols, u1 - u0), lane);
-
-  float acc[B];
+  // The first DEPTH units' weight loads go out before the activations are
+  // staged, so their latency overlaps the staging.
+  u32x4 buf[DEPTH][NCH];
+  uint32_t d6[DEPTH];
+  int tl = t0, cl = u0 % n_cols;                   // next unit to load
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-  int t = u0 / n_cols, c = c0, ic = 0;
-  int u = u0;
-  auto step = [&](const u32x4* buf, uint32_t d6) {
-    process_unit<QT, B, XF32>(a, buf, d6, c, ic, T, acc, M, K);
-    if (c == n_cols - 1 || u + 1 == u1) {
-      const bool full = (t * n_cols >= u0) && (c == n_cols - 1);
-      finish_tile<B>(a, t, full, w, u0, lane, acc);
+  for (int k = 0; k < DEPTH; ++k) {
+    d6[k] = 0;
+    if (u0 + k < u1) load_unit<QT>(unit_base<QT>(a, tl, cl), lane, buf[k], d6[k]);
+    if (++cl == n_cols) { cl = 0; ++tl; }
+  }
+  stage_x_T<QT, B, XF32>(a, X, T, c0w, len);
+  __syncthreads();
+
+  if (active) {
+    float acc[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-    }
-    ++u;
-    if (++c == n_cols) { c = 0; ++t; }
-    if (++ic == n_cols) ic = 0;
-  };
-  while (true) {
-    step(bA, dA);
-    if (u + 1 < u1) {
-      load_unit<QT>(unit_base<QT>(a, tl, cl), lane, bA, dA);
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    int t = t0, c = u0 % n_cols;
+    int ic = c - c0w;
+    if (ic < 0) ic += n_cols;
+    int u = u0;
+    // consume buf[k] (unit u); at a tile's last unit or the run's end park the sum in LDS
+    auto consume = [&](int k) {
+      process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+      if (c == n_cols - 1 || u + 1 == u1) {
+        float* pw = P + ((wid * kTilesPerWave + (t - t0)) * B) * kTileRows;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          pw[b * kTileRows + lane] = acc[b];
+          acc[b] = 0.0f;
+        }
+      }
+      ++u;
+      if (++c == n_cols) { c = 0; ++t; }
+      if (++ic == n_cols) ic = 0;
+    };
+    auto refill = [&](int k) {
+      load_unit<QT>(unit_base<QT>(a, tl, cl), lane, buf[k], d6[k]);
       if (++cl == n_cols) { cl = 0; ++tl; }
+    };
+    // main loop: every refill is in range, so the loads are unconditional
+    while (u + 2 * DEPTH <= u1) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        consume(k);
+        refill(k);
+      }
     }
-    if (u >= u1) break;
-    step(bB, dB);
-    if (u + 1 < u1) {
-      load_unit<QT>(unit_base<QT>(a, tl, cl), lane, bB, dB);
-      if (++cl == n_cols) { cl = 0; ++tl; }
+    // fewer than 2*DEPTH units left (kept as a loop: unrolling it raises register pressure)
+    while (u < u1) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        if (u < u1) {
+          const bool more = u + DEPTH < u1;
+          consume(k);
+          if (more) refill(k);
+        }
+      }
     }
-    if (u >= u1) break;
+  }
+  __syncthreads();
+
+  // Each tile of the workgroup: add the wavefronts' sums in wavefront order;
+  // write y if the workgroup covered the whole tile, else hand it over.
+  const int tA = U0 / n_cols, tB = (U1 - 1) / n_cols;
+  for (int t = tA + wid; t <= tB; t += 4) {
+    const int ts = t * n_cols, te = ts + n_cols;
+    float s[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) s[b] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
+      if (max(a0, ts) >= min(a1, te)) continue;
+      const float* pw = P + ((i * kTilesPerWave + (t - a0 / n_cols)) * B) * kTileRows;
+#pragma unroll
+      for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
+    }
+    if (ts >= U0 && te <= U1) write_tile<B>(a, t, lane, s);
+    else hand_off<B>(a, t, lblock, wgu, lane, s);
   }
 }
 
 template <int QT, int B, bool XF32>
 static hipError_t launch_one(const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_kernel<QT, B, XF32>), dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, KQ_DEPTH>), dim3(grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

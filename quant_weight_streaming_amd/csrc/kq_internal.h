@@ -21,10 +21,9 @@ struct GemvArgs {
   int64_t ldx;                         // activation row stride (elements)
   int32_t n_units;                     // total tiles * n_cols
   int32_t upw;                         // units per wavefront
-  int32_t n_waves;                     // wavefronts with work
-  int32_t tsb;                         // LDS floats per wavefront / batch: min(n_cols, upw) * sub-blocks per column
-  float* partial;                      // scratch: [n_waves][2][KQ_MAX_BATCH][64] partial sums
-  uint32_t* counters;                  // scratch: [n_waves] arrival counters, zero between calls
+  int32_t tsb;                         // columns staged in LDS per workgroup: min(n_cols, 4 * upw)
+  float* partial;                      // scratch: [workgroups][2][KQ_MAX_BATCH][64] partial sums
+  uint32_t* counters;                  // scratch: [workgroups] arrival counters, zero between calls
 };
 
 hipError_t launch_gemv(int type, int xtype, int batch, const GemvArgs& a, int grid, size_t lds, hipStream_t s);
