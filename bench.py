@@ -156,32 +156,38 @@ def time_sweep(sw: Sweep, B: int, steps: int, warmup: int):
     return plain_ms, graph_ms
 
 
-def kernel_times(sw: Sweep, B: int, reps: int = 2):
-    """Average duration per GEMV class from per-launch HIP events on the launch stream."""
+def kernel_times(sw: Sweep, B: int, reps: int = 3):
+    """Average launch duration per GEMV class, from HIP events on the launch stream around a hipGraph
+    of all of that class's launches in the sweep (52 distinct weight tensors per layer class, so no
+    launch re-reads another's weights from cache), replayed `reps` times: elapsed / launches."""
     torch = sw.torch
     stream = torch.cuda.current_stream()
-    calls = sw.calls(B, stream.cuda_stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-    acc = {}
-    for _ in range(reps):
-        for (fn, args, name), (a, b) in zip(calls, ev):
-            a.record(stream)
-            rc = fn(*args)
-            if rc:
-                raise RuntimeError(f"{name}: status {rc}")
-            b.record(stream)
-        torch.cuda.synchronize()
-        for (fn, args, name), (a, b) in zip(calls, ev):
-            acc.setdefault(name, []).append(a.elapsed_time(b))
+    names = []
+    for _, spec, _, _ in sw.entries:
+        if spec.name not in names:
+            names.append(spec.name)
     out = {}
-    for layer, spec, _, _ in sw.entries:
-        if spec.name in out:
-            continue
+    for name in names:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls = [c for c in sw.calls(B, torch.cuda.current_stream().cuda_stream) if c[2] == name]
+            run_calls(calls)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_rep = max(reps, -(-26 // len(calls)))
+        e0.record(stream)
+        for _ in range(n_rep):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (n_rep * len(calls))
+        del g
+        spec = next(s for _, s, _, _ in sw.entries if s.name == name)
         wb = spec.rows * spec.cols // 256 * sw.synth.SB_BYTES[spec.qtype]
-        ms = sum(acc[spec.name]) / len(acc[spec.name])
-        out[spec.name] = dict(qtype=spec.qtype, rows=spec.rows, cols=spec.cols, launches=len(acc[spec.name]),
-                              avg_us=round(ms * 1e3, 2), weight_gbs=round(wb / ms / 1e6, 1),
-                              weight_bytes=wb, x_bytes=B * spec.cols * 2, y_bytes=B * spec.rows * 4)
+        out[name] = dict(qtype=spec.qtype, rows=spec.rows, cols=spec.cols, launches=n_rep * len(calls),
+                         avg_us=round(ms * 1e3, 2), weight_gbs=round(wb / ms / 1e6, 1),
+                         weight_bytes=wb, x_bytes=B * spec.cols * 2, y_bytes=B * spec.rows * 4)
     return out
 
 
@@ -267,6 +273,62 @@ def copy_calibration(n: int):
     log(f"[bench] copy-calibration: {n} copies of {1 << 30} bytes")
 
 
+def summarize_trace(src: str, cmd: str) -> str:
+    """Text summary of a rocprofv3 --kernel-trace --stats run of this benchmark: the GEMV rows of the
+    stats table, then every GEMV dispatch grouped by (kernel, grid) and named by sweep class (each timed
+    sweep issues the 209 GEMVs in sweep order, so a key's first dispatch falls at its sweep position)."""
+    import csv
+    from quant_weight_streaming_amd import synth
+    stats = [r for r in csv.DictReader(open(glob.glob(os.path.join(src, "*_kernel_stats.csv"))[0]))
+             if "kq::" in r["Name"]]
+    trace = [r for r in csv.DictReader(open(glob.glob(os.path.join(src, "*_kernel_trace.csv"))[0]))
+             if "kq::gemv_kernel" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    order = [spec.name for _, spec in synth.sweep("q4k")]
+    groups, label = {}, {}
+    for i, r in enumerate(trace):
+        key = (r["Kernel_Name"].split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+        if key not in label:
+            label[key] = order[i % len(order)]
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"command: {cmd}", "", "rocprofv3 kernel stats (kq kernels; durations in us):",
+           f"{'kernel':44s} {'calls':>6s} {'avg':>9s} {'min':>9s} {'max':>9s}"]
+    for r in stats:
+        out.append(f"{r['Name'].split('(')[0].replace('void ', ''):44s} {int(r['Calls']):6d} "
+                   f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    out += ["", "GEMV dispatches by kernel and grid (from the kernel trace; durations in us):",
+            f"{'kernel':36s} {'workgroups':>10s} {'class':>8s} {'calls':>6s} {'avg':>9s} {'median':>9s} {'min':>9s} {'max':>9s}"]
+    for key, d in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        d = sorted(d)
+        out.append(f"{key[0]:36s} {key[1]:10d} {label[key]:>8s} {len(d):6d} {sum(d) / len(d):9.2f} "
+                   f"{d[len(d) // 2]:9.2f} {d[0]:9.2f} {d[-1]:9.2f}")
+    return "\n".join(out) + "\n"
+
+
+def summarize_counters(kfetch: str, kwrite: str, cfetch: str, cwrite: str) -> dict:
+    """HBM bytes per launch of the dominant GEMV from FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch),
+    each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    import csv
+
+    def rows(d, pred):
+        f = glob.glob(os.path.join(d, "*_counter_collection.csv"))[0]
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(f)) if pred(r)]
+    gemv = lambda r: "kq::gemv_kernel" in r["Kernel_Name"]
+    copy = lambda r: "copyBuffer" in r["Kernel_Name"]
+    kf, kw = rows(kfetch, gemv), rows(kwrite, gemv)
+    cf, cw = rows(cfetch, copy), rows(cwrite, copy)
+    gib_kib = float(1 << 20)
+    f_fac, w_fac = gib_kib / (sum(cf) / len(cf)), gib_kib / (sum(cw) / len(cw))
+    fetch_b = sum(kf) / len(kf) * 1024 * f_fac
+    write_b = sum(kw) / len(kw) * 1024 * w_fac
+    return dict(kernel_hash=kernel_source_hash(), dispatches=len(kf),
+                fetch_kib_per_dispatch=sum(kf) / len(kf), write_kib_per_dispatch=sum(kw) / len(kw),
+                copy_1gib_fetch_kib=sum(cf) / len(cf), copy_1gib_write_kib=sum(cw) / len(cw),
+                fetch_scale=f_fac, write_scale=w_fac,
+                hbm_fetch_bytes_per_launch=round(fetch_b), hbm_write_bytes_per_launch=round(write_b),
+                hbm_bytes_per_launch=round(fetch_b + write_b))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,8 +338,19 @@ def main():
     ap.add_argument("--no-c4", action="store_true", help="skip the Q5_K / merged-sub-block sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--profile-kernel", type=int, default=0)
-    ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, help="N plain 1 GiB device copies")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "COMMAND"),
+                    help="print a text summary of a rocprofv3 kernel-trace run of this benchmark")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("GEMV_FETCH", "GEMV_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="print the HBM-traffic JSON of the dominant kernel from four rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_trace:
+        sys.path.insert(0, ROOT)
+        sys.stdout.write(summarize_trace(*args.summarize_trace))
+        return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}): the K-quant GEMV path "
