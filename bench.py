@@ -40,6 +40,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def weight_gbs(weight_bytes: float, ms: float) -> float:
+    """Weight bytes streamed per millisecond of device time, in GB/s (decimal)."""
+    return weight_bytes / ms / 1e6
+
+
+def tok_s(ms_per_step: float, batch: int = 1) -> float:
+    """Decode-equivalent tokens per second when one step streams the whole weight set once for `batch` tokens."""
+    return batch * 1e3 / ms_per_step
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "quant_weight_streaming_amd", "csrc", "*"))) + \
@@ -186,7 +196,7 @@ def kernel_times(sw: Sweep, B: int, reps: int = 3):
         spec = next(s for _, s, _, _ in sw.entries if s.name == name)
         wb = spec.rows * spec.cols // 256 * sw.synth.SB_BYTES[spec.qtype]
         out[name] = dict(qtype=spec.qtype, rows=spec.rows, cols=spec.cols, launches=n_rep * len(calls),
-                         avg_us=round(ms * 1e3, 2), weight_gbs=round(wb / ms / 1e6, 1),
+                         avg_us=round(ms * 1e3, 2), weight_gbs=round(weight_gbs(wb, ms), 1),
                          weight_bytes=wb, x_bytes=B * spec.cols * 2, y_bytes=B * spec.rows * 4)
     return out
 
@@ -406,9 +416,9 @@ def main():
         for B in (2, 4, 8):
             plain, graph = time_sweep(sw4, B, max(3, args.steps // 2), args.warmup)
             c4[f"b{B}"] = dict(graph_ms=round(graph, 4), plain_ms=round(plain, 4),
-                               weight_gbs=round(sw4.weight_bytes / graph / 1e6, 1),
-                               pct_of_hbm_peak=round(100 * sw4.weight_bytes / graph / 1e6 / HBM_PEAK_GBS, 2),
-                               tok_s=round(B / graph * 1e3, 1))
+                               weight_gbs=round(weight_gbs(sw4.weight_bytes, graph), 1),
+                               pct_of_hbm_peak=round(100 * weight_gbs(sw4.weight_bytes, graph) / HBM_PEAK_GBS, 2),
+                               tok_s=round(tok_s(graph, B), 1))
             log(f"[bench] cfg4 B={B}: graph {graph:.3f} ms ({sw4.weight_bytes / graph / 1e6:.0f} GB/s)")
         c4["weight_bytes"] = sw4.weight_bytes
         c4["kernels_b8"] = kernel_times(sw4, 8)
@@ -417,7 +427,7 @@ def main():
         bytes3 = sw.weight_bytes
 
     g1 = res[1]["graph_ms"]
-    gbs1 = bytes3 / g1 / 1e6
+    gbs1 = weight_gbs(bytes3, g1)
     line = {
         "metric": METRIC,
         "value": round(gbs1, 1),
@@ -436,13 +446,13 @@ def main():
                    "weight_bytes": bytes3, "batch": 1, "launch": "hipGraph replay of 209 GEMV launches",
                    "x": "bf16 N(0,1), own seed per GEMV", "y": "fp32"},
         "pct_of_hbm_peak": round(100 * gbs1 / HBM_PEAK_GBS, 2),
-        "decode_equiv_tok_s": round(1e3 / g1, 1),
+        "decode_equiv_tok_s": round(tok_s(g1), 1),
         "batch8": {"graph_ms": round(res[8]["graph_ms"], 4), "plain_ms": round(res[8]["plain_ms"], 4),
-                   "weight_gbs": round(bytes3 / res[8]["graph_ms"] / 1e6, 1),
-                   "pct_of_hbm_peak": round(100 * bytes3 / res[8]["graph_ms"] / 1e6 / HBM_PEAK_GBS, 2),
-                   "tok_s": round(8e3 / res[8]["graph_ms"], 1)},
+                   "weight_gbs": round(weight_gbs(bytes3, res[8]["graph_ms"]), 1),
+                   "pct_of_hbm_peak": round(100 * weight_gbs(bytes3, res[8]["graph_ms"]) / HBM_PEAK_GBS, 2),
+                   "tok_s": round(tok_s(res[8]["graph_ms"], 8), 1)},
         "batch1_plain_launch": {"ms": round(res[1]["plain_ms"], 4),
-                                "weight_gbs": round(bytes3 / res[1]["plain_ms"] / 1e6, 1)},
+                                "weight_gbs": round(weight_gbs(bytes3, res[1]["plain_ms"]), 1)},
         "kernels_b1": kt1,
         "kernels_b8": kt8,
         "c4_q5k_merged": c4,
