@@ -41,6 +41,11 @@ constexpr int kTileRows = 64;
 constexpr int kChunk = 16;                      // bytes per lane per chunk
 constexpr int kChunkStride = kTileRows * kChunk;  // 1024 bytes between chunks of one tile
 constexpr int kPartialStride = KQ_MAX_BATCH * kTileRows;  // floats per partial-sum slot
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx950: 32-bit data
+// format, bounds checked against num_records.
+constexpr int kBufferFlags = 0x00020000;
+// Cache-policy operand of buffer loads: nontemporal (the weights are read once).
+constexpr int kCacheNT = 2;
 
 template <int QT> struct Fmt;
 template <> struct Fmt<KQ_Q4_K> {

@@ -26,9 +26,10 @@
 // with v_fma (S = sum q*x, T = sum x).
 //
 // The weight stream is buffered in registers: while one unit is computed the
-// next DEPTH-1 are in flight.  The main loop issues its refills
-// unconditionally and keeps global stores out of the loop, so the compiler can
-// wait for exactly the unit it consumes instead of for every load in flight.
+// next DEPTH-1 are in flight.  The main loop issues each refill before the
+// computation that needs the oldest buffer, unconditionally, and keeps global
+// stores out of the loop, so the compiler waits for exactly the unit it
+// consumes instead of for every load in flight.
 #include "kq_common.h"
 #include "kq_internal.h"
 
@@ -40,24 +41,33 @@ namespace kq {
 
 constexpr int kTilesPerWave = 2;   // a wavefront's run of units touches at most this many tiles
 
+// Buffer resource over unit (t, c): base = its first byte, size = one unit, or
+// size 0 when `live` is false, which turns every load through it into a
+// zero-filled no-op that moves no data (loads past the wavefront's last unit).
 template <int QT>
-__device__ __forceinline__ const uint8_t* unit_base(const GemvArgs& a, int t, int c) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const GemvArgs& a, int t, int c, bool live) {
   int p = 0;
 #pragma unroll
   for (int i = 1; i < KQ_MAX_PROJ; ++i)
     if (i < a.nproj && t >= a.tile_begin[i]) p = i;
-  return a.w[p] + ((int64_t)(t - a.tile_begin[p]) * a.n_cols + c) * tile_bytes<QT>();
+  const uint64_t addr = reinterpret_cast<uint64_t>(a.w[p]) +
+                        ((int64_t)(t - a.tile_begin[p]) * a.n_cols + c) * tile_bytes<QT>();
+  // every operand is wavefront-uniform; say so, so the resource stays in SGPRs
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(live ? (int)tile_bytes<QT>() : 0);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           kBufferFlags);
 }
 
+// One unit's weights: chunk k of this lane's row, nontemporal (read once).
 template <int QT>
-__device__ __forceinline__ void load_unit(const uint8_t* base, int lane, u32x4* buf, uint32_t& d6) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + lane * kChunk);
+__device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, int lane, u32x4* buf, uint32_t& d6) {
 #pragma unroll
-  for (int k = 0; k < Fmt<QT>::kChunks; ++k) buf[k] = __builtin_nontemporal_load(p + k * kTileRows);
-  if constexpr (QT == KQ_Q6_K) {
-    const uint16_t* dp = reinterpret_cast<const uint16_t*>(base + 13 * kChunkStride) + lane;
-    d6 = __builtin_nontemporal_load(dp);
-  }
+  for (int k = 0; k < Fmt<QT>::kChunks; ++k)
+    buf[k] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * kChunk + k * kChunkStride, 0, kCacheNT);
+  if constexpr (QT == KQ_Q6_K)
+    d6 = __builtin_amdgcn_raw_buffer_load_b16(r, 13 * kChunkStride + 2 * lane, 0, kCacheNT);
 }
 
 // Stage the activations of the workgroup's columns c0, c0+1, ... (mod n_cols)
@@ -211,12 +221,25 @@ __device__ __forceinline__ void hand_off(const GemvArgs& a, int t, int L, int wg
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
-  for (int l = la; l <= lb; ++l) {
-    const int sl = (t == (l * wgu) / n_cols) ? 0 : 1;
-    float* pp = a.partial + (int64_t)(l * 2 + sl) * kPartialStride;
+  // read the pieces four workgroups at a time (one round trip per four), then
+  // add them in workgroup order
+  for (int l0 = la; l0 <= lb; l0 += 4) {
+    float v[4][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b)
-      s[b] += __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < 4; ++j) {
+      const int l = l0 + j;
+      const int sl = (t == (l * wgu) / n_cols) ? 0 : 1;
+      const float* pp = a.partial + (int64_t)(l * 2 + sl) * kPartialStride;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        v[j][b] = l <= lb ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (l0 + j <= lb) s[b] += v[j][b];
   }
   write_tile<B>(a, t, lane, s);
   if (lane == 0) __hip_atomic_store(&a.counters[la], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -250,17 +273,25 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   const int t0 = u0 / n_cols;                      // first tile of this wavefront
   const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
 
-  // The first DEPTH units' weight loads go out before the activations are
-  // staged, so their latency overlaps the staging.
+  // The weight stream runs DEPTH-1 units ahead of the unit being computed.
+  // The first DEPTH-1 units' loads go out before the activations are staged,
+  // so their latency overlaps the staging.
   u32x4 buf[DEPTH][NCH];
   uint32_t d6[DEPTH];
-  int tl = t0, cl = u0 % n_cols;                   // next unit to load
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k) {
-    d6[k] = 0;
-    if (u0 + k < u1) load_unit<QT>(unit_base<QT>(a, tl, cl), lane, buf[k], d6[k]);
+  for (int k = 0; k < DEPTH; ++k) d6[k] = 0;       // Q4_K / Q5_K never load it
+  int ul = u0, tl = t0, cl = u0 % n_cols;          // next unit to load
+  auto refill = [&](int k) {
+    load_unit<QT>(unit_rsrc<QT>(a, tl, cl, ul < u1), lane, buf[k], d6[k]);
+    ++ul;
     if (++cl == n_cols) { cl = 0; ++tl; }
-  }
+    // keep the loads ahead of the computation that follows: neither the IR
+    // passes nor the machine scheduler may move work across this point
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
   stage_x_T<QT, B, XF32>(a, X, T, c0w, len);
   __syncthreads();
 
@@ -287,27 +318,15 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
       if (++c == n_cols) { c = 0; ++t; }
       if (++ic == n_cols) ic = 0;
     };
-    auto refill = [&](int k) {
-      load_unit<QT>(unit_base<QT>(a, tl, cl), lane, buf[k], d6[k]);
-      if (++cl == n_cols) { cl = 0; ++tl; }
-    };
-    // main loop: every refill is in range, so the loads are unconditional
-    while (u + 2 * DEPTH <= u1) {
-#pragma unroll
-      for (int k = 0; k < DEPTH; ++k) {
-        consume(k);
-        refill(k);
-      }
-    }
-    // fewer than 2*DEPTH units left (kept as a loop: unrolling it raises register pressure)
+    // Each step issues the load of unit u+DEPTH-1 into the buffer the previous
+    // step freed, then computes unit u.  Loads past the run are issued too,
+    // through a zero-size resource, so every step has the same loads in flight
+    // and the wait before a computation is for its own unit only.
     while (u < u1) {
 #pragma unroll
       for (int k = 0; k < DEPTH; ++k) {
-        if (u < u1) {
-          const bool more = u + DEPTH < u1;
-          consume(k);
-          if (more) refill(k);
-        }
+        refill((k + DEPTH - 1) % DEPTH);
+        if (u < u1) consume(k);
       }
     }
   }
