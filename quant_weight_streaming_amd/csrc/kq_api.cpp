@@ -21,7 +21,6 @@ int64_t sb_bytes(int type) {
   }
 }
 
-static int sub_blocks(int type) { return type == KQ_Q6_K ? 16 : 8; }
 
 // Scratch for row tiles whose columns span several workgroups: two partial-sum
 // slots and one arrival counter per workgroup.  The counters are zero between
@@ -75,11 +74,23 @@ static int device_state(int dev, DeviceState** out) {
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Target resident wavefronts per CU (tuning knob; KQ_WAVES_PER_CU overrides the default).
+// Tuning knobs, read per call: target wavefronts per CU (KQ_WAVES_PER_CU, default
+// 8) and wavefronts per workgroup (KQ_WG_WAVES, 4 or 8; default 8 from batch
+// kWideBatch up, where one workgroup per CU stages the activations of all its
+// columns once and reuses them across its row tiles, else 4).
 static int waves_per_cu() {
   const char* e = getenv("KQ_WAVES_PER_CU");
   const int x = e ? atoi(e) : 0;
   return (x >= 1 && x <= 32) ? x : 8;
+}
+
+constexpr int kWideBatch = 2;
+
+static int wg_waves(int batch) {
+  const char* e = getenv("KQ_WG_WAVES");
+  const int x = e ? atoi(e) : 0;
+  if (x == 4 || x == 8) return x;
+  return batch >= kWideBatch ? 8 : 4;
 }
 
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
@@ -122,24 +133,27 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   if (rc != KQ_OK) return rc;
 
   // Launch geometry: an even run of `upw` units per wavefront, about
-  // waves_per_cu() wavefronts per CU, four wavefronts per workgroup.  A
-  // workgroup stages the activations and sub-block sums of the columns its
-  // 4*upw units touch in LDS (at most 64 KiB), plus its wavefronts' partial sums.
+  // waves_per_cu() wavefronts per CU, nw wavefronts per workgroup.  A
+  // workgroup stages the activations (and sub-block sums) of the columns its
+  // nw*upw units touch in LDS, within `budget` bytes (64 KiB leaves room for two
+  // 4-wavefront workgroups per CU, 112 KiB is for one 8-wavefront workgroup),
+  // plus its wavefronts' partial sums.
+  const int nw = wg_waves(batch);
+  const int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
   const int64_t target = (int64_t)st->cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
-  const int64_t xwords = xtype == KQ_X_F32 ? 256 : 128;                   // x words per column and row
-  const int64_t per_col = (int64_t)batch * 4 * (xwords + sub_blocks(type));  // LDS bytes per staged column
-  const int64_t max_cols = 65536 / per_col;
-  if (n_cols > max_cols && 4 * upw > max_cols) upw = max_cols / 4 > 0 ? max_cols / 4 : 1;
+  const int64_t per_col = (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, 1) - gemv_lds_bytes(type, xtype, batch, nw, 0));
+  const int64_t max_cols = budget / per_col;
+  if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
   if (upw > n_cols + 1) upw = n_cols + 1;   // a wavefront's run then touches at most two tiles
-  int64_t n_groups = (n_units + 4 * upw - 1) / (4 * upw);
+  int64_t n_groups = (n_units + nw * upw - 1) / (nw * upw);
   if (n_groups > kMaxGroups) {
-    upw = (n_units + 4 * (int64_t)kMaxGroups - 1) / (4 * (int64_t)kMaxGroups);
-    if ((n_cols > max_cols && 4 * upw > max_cols) || upw > n_cols + 1) return KQ_ERR_RANGE;
-    n_groups = (n_units + 4 * upw - 1) / (4 * upw);
+    upw = (n_units + nw * (int64_t)kMaxGroups - 1) / (nw * (int64_t)kMaxGroups);
+    if ((n_cols > max_cols && nw * upw > max_cols) || upw > n_cols + 1) return KQ_ERR_RANGE;
+    n_groups = (n_units + nw * upw - 1) / (nw * upw);
   }
-  const int64_t tcols = n_cols < 4 * upw ? n_cols : 4 * upw;
+  const int64_t tcols = n_cols < nw * upw ? n_cols : nw * upw;
   a.nproj = n;
   a.n_cols = (int32_t)n_cols;
   a.x = x;
@@ -149,9 +163,9 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   a.tsb = (int32_t)tcols;
   a.partial = st->partial;
   a.counters = st->counters;
-  const size_t lds = (size_t)tcols * per_col + (size_t)8 * batch * 64 * sizeof(float);
+  const size_t lds = gemv_lds_bytes(type, xtype, batch, nw, (int)tcols);
   const int64_t grid = (n_groups + 7) / 8 * 8;  // whole XCD rounds for the block remap
-  if (launch_gemv(type, xtype, batch, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_gemv(type, xtype, batch, nw, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;
 }

@@ -36,10 +36,14 @@
 #ifndef KQ_DEPTH
 #define KQ_DEPTH 2
 #endif
+#ifndef KQ_MFMA_MIN_BATCH
+#define KQ_MFMA_MIN_BATCH 2
+#endif
 
 namespace kq {
 
 constexpr int kTilesPerWave = 2;   // a wavefront's run of units touches at most this many tiles
+constexpr int kMfmaMinBatch = KQ_MFMA_MIN_BATCH;  // bf16 batches from this size use the matrix cores
 
 // Buffer resource over unit (t, c): base = its first byte, size = one unit, or
 // size 0 when `live` is false, which turns every load through it into a
@@ -74,13 +78,13 @@ __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, int lane, u3
 // in LDS, and T, the per-sub-block activation sums in the dot product's own
 // order (bf16: the same dot2 chain over (128,128), Q6_K (160,160); fp32: sum x).
 // X layout: [ic][b][256 elements]; T layout: [ic * sub-blocks + g][b].
-template <int QT, int B, bool XF32>
+template <int QT, int B, bool XF32, int NT>
 __device__ __forceinline__ void stage_x_T(const GemvArgs& a, uint32_t* X, float* T, int c0, int len) {
   using F = Fmt<QT>;
   constexpr int XW = XF32 ? 256 : 128;              // 32-bit words of x per column and batch row
   constexpr int SW = XF32 ? F::kSubW : F::kSubW / 2;  // words per sub-block
   const int n = len * F::kSubBlocks;
-  for (int i = threadIdx.x; i < n; i += 256) {
+  for (int i = threadIdx.x; i < n; i += NT) {
     const int ic = i / F::kSubBlocks, g = i - ic * F::kSubBlocks;
     int c = c0 + ic;
     if (c >= a.n_cols) c -= a.n_cols;
@@ -180,6 +184,129 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
   }
 }
 
+// ---------------------------------------------------------------- matrix-core path
+//
+// With bf16 activations the products q * x of a unit go through
+// v_mfma_f32_16x16x32_bf16 instead of v_dot2.  The operands are arranged
+// block-diagonally so that the instruction consumes the lane == row layout
+// as it is: for one block of 8 consecutive columns k0..k0+7,
+//   B operand: lane l supplies its own row's 8 weights (128 + q, bf16), which is
+//              B[8j + kk][n] with n = l % 16, j = l / 16;
+//   A operand: A[4j + b][8j + kk] = x[b][k0 + kk] and zero for the other 24 of
+//              the 32 columns of row 4j + b, so lane la holds x[la % 4] when
+//              (la % 16) / 4 == la / 16 and zeros otherwise;
+//   result:    D[4j + b][n] = sum_kk x[b][k0 + kk] * w[16j + n][k0 + kk], held by
+//              lane 16j + n in register b: lane == row again, one register per
+//              batch row (four batch rows per instruction; a second set covers
+//              batch rows 4..7).
+// A sub-block is 4 (Q6_K: 2) such instructions accumulating in place, then
+// scaled on the VALU as in the dot2 path.  The activation sum T is the same
+// sequence of instructions with every weight equal to the offset (128, Q6_K
+// 160); the matrix core evaluates each output position with the same
+// arithmetic, so T is computed once per column and sub-block while staging,
+// and a sub-block whose quants are all zero (Q6_K: 32) gives S == T exactly.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Byte offsets inside the workgroup's LDS for the matrix-core path:
+//   X [ic][b][256] bf16 (B * 512 bytes per column), then T [ic][g][NB][4] floats,
+//   then Z, 512 zero bytes that the inactive operand lanes read.
+template <int QT, int B>
+struct MfmaLds {
+  static constexpr int NB = (B + 3) / 4;                       // operand sets of 4 batch rows
+  static constexpr int kXCol = B * 512;                        // bytes of x per column
+  static constexpr int kTCol = Fmt<QT>::kSubBlocks * NB * 16;  // bytes of T per column
+  static constexpr int kPerCol = kXCol + kTCol;
+};
+
+// A-operand byte offset of this lane for operand set gb at column ic (see above).
+template <int B>
+__device__ __forceinline__ int a_operand_offset(int lane, int gb, int ic, int x_base, int z_base) {
+  const int b = 4 * gb + (lane & 3);
+  const bool active = ((lane & 15) >> 2) == (lane >> 4) && b < B;
+  return active ? x_base + ic * B * 512 + b * 512 : z_base;
+}
+
+template <int QT, int B, int NW>
+__device__ __forceinline__ void stage_x_mfma(const GemvArgs& a, uint8_t* lds, int c0, int len, int wid, int lane) {
+  using F = Fmt<QT>;
+  using L = MfmaLds<QT, B>;
+  constexpr int NB = L::NB, SB = F::kSubBlocks, KB = F::kSubW / 8;
+  const int t_base = len * L::kXCol, z_base = t_base + len * L::kTCol;
+  // x of the workgroup's columns, 16 bytes per thread and step
+  const int nv = len * B * 32;
+  for (int i = threadIdx.x; i < nv; i += 64 * NW) {
+    const int ic = i / (B * 32), r = i - ic * (B * 32), b = r >> 5, v = r & 31;
+    int c = c0 + ic;
+    if (c >= a.n_cols) c -= a.n_cols;
+    const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + b * a.ldx +
+                                                     (int64_t)c * 256) + v;
+    *reinterpret_cast<u32x4*>(lds + (ic * B + b) * 512 + v * 16) = *xp;
+  }
+  if (threadIdx.x < 32) *reinterpret_cast<u32x4*>(lds + z_base + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  // T[ic][g][gb][b'] = the sub-block's products with every weight = the offset
+  const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;
+  const bf16x8 bconst = __builtin_bit_cast(bf16x8, u32x4{kc, kc, kc, kc});
+  for (int i = wid; i < len * SB; i += NW) {
+    const int ic = i / SB, g = i - ic * SB;
+#pragma unroll
+    for (int gb = 0; gb < NB; ++gb) {
+      const uint8_t* ap = lds + a_operand_offset<B>(lane, gb, ic, 0, z_base) + g * F::kSubW * 2;
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(ap + kb * 16), bconst, t,
+                                                    0, 0, 0);
+      if (lane == 0) *reinterpret_cast<f32x4*>(lds + t_base + ((ic * SB + g) * NB + gb) * 16) = t;
+    }
+  }
+}
+
+// One unit on the matrix cores: ap[gb] are this lane's A-operand pointers for
+// the unit's column, Tc the column's T block.
+template <int QT, int B>
+__device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6, const uint8_t* const* ap,
+                                                  const float* Tc, float* acc, uint32_t M, uint32_t K) {
+  using F = Fmt<QT>;
+  constexpr int SB = F::kSubBlocks, NP = F::kPairs, KB = F::kSubW / 8, NB = MfmaLds<QT, B>::NB;
+  float ca[SB], cm[SB];
+  sb_coeffs<QT>(buf, d6, 0.0078125f, ca, cm);
+  uint32_t pr[NP];
+#pragma unroll
+  for (int g = 0; g < SB; ++g) {
+    unpack_pairs<QT>(buf, g, M, K, pr);
+    f32x4 S[NB];
+#pragma unroll
+    for (int gb = 0; gb < NB; ++gb) S[gb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
+#pragma unroll
+      for (int gb = 0; gb < NB; ++gb)
+        S[gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2), bop, S[gb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int gb = 0; gb < NB; ++gb) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * gb + r < B) {
+          float& v = acc[4 * gb + r];
+          v = __builtin_fmaf(ca[g], S[gb][r] - t[r], v);
+          if constexpr (QT != KQ_Q6_K) v = __builtin_fmaf(-cm[g], t[r], v);
+        }
+      }
+      // The instruction writes all four result registers when it completes;
+      // keep all four allocated until here, also when fewer than four batch
+      // rows of this set are read, so that nothing else is placed in them
+      // while the write is still pending.
+      asm volatile("" ::"v"(S[gb]));
+    }
+  }
+}
+
 // Write finished row sums of tile t (all of its columns) to y.
 template <int B>
 __device__ __forceinline__ void write_tile(const GemvArgs& a, int t, int lane, const float* v) {
@@ -245,8 +372,8 @@ __device__ __forceinline__ void hand_off(const GemvArgs& a, int t, int L, int wg
   if (lane == 0) __hip_atomic_store(&a.counters[la], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT, int B, bool XF32, int DEPTH>
-__global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
+template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH>
+__global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   using F = Fmt<QT>;
   constexpr int NCH = F::kChunks, SB = F::kSubBlocks;
   constexpr int XW = XF32 ? 256 : 128;
@@ -258,7 +385,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   // blocks (which share split tiles) go to one XCD.
   const int nb8 = gridDim.x >> 3;
   const int lblock = (blockIdx.x & 7) * nb8 + (blockIdx.x >> 3);
-  const int n_cols = a.n_cols, upw = a.upw, wgu = 4 * upw;
+  const int n_cols = a.n_cols, upw = a.upw, wgu = NW * upw;
   const int U0 = lblock * wgu;                     // the workgroup's run of units [U0, U1)
   if (U0 >= a.n_units) return;                     // whole workgroup idle
   const int U1 = min(U0 + wgu, a.n_units);
@@ -266,7 +393,10 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   const int len = min(n_cols, U1 - U0);
   uint32_t* X = lds_words;
   float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);
-  float* P = T + a.tsb * SB * B;                   // per-wavefront tile sums [4][kTilesPerWave][B][64]
+  // per-wavefront tile sums [NW][kTilesPerWave][B][64] follow the staged columns
+  float* P = MF ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds_words) +
+                                           a.tsb * MfmaLds<QT, B>::kPerCol + 512)
+                : T + a.tsb * SB * B;
   const int u0 = U0 + wid * upw;
   const int u1 = min(u0 + upw, U1);
   const bool active = u0 < U1;
@@ -292,7 +422,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   };
 #pragma unroll
   for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
-  stage_x_T<QT, B, XF32>(a, X, T, c0w, len);
+  if constexpr (MF) stage_x_mfma<QT, B, NW>(a, reinterpret_cast<uint8_t*>(lds_words), c0w, len, wid, lane);
+  else stage_x_T<QT, B, XF32, 64 * NW>(a, X, T, c0w, len);
   __syncthreads();
 
   if (active) {
@@ -305,7 +436,19 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
     int u = u0;
     // consume buf[k] (unit u); at a tile's last unit or the run's end park the sum in LDS
     auto consume = [&](int k) {
-      process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+      if constexpr (MF) {
+        constexpr int NB = MfmaLds<QT, B>::NB;
+        uint8_t* base = reinterpret_cast<uint8_t*>(lds_words);
+        const int t_base = len * MfmaLds<QT, B>::kXCol, z_base = t_base + len * MfmaLds<QT, B>::kTCol;
+        const uint8_t* ap[NB];
+#pragma unroll
+        for (int gb = 0; gb < NB; ++gb) ap[gb] = base + a_operand_offset<B>(lane, gb, ic, 0, z_base);
+        process_unit_mfma<QT, B>(buf[k], d6[k], ap,
+                                 reinterpret_cast<const float*>(base + t_base + ic * MfmaLds<QT, B>::kTCol),
+                                 acc, M, K);
+      } else {
+        process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+      }
       if (c == n_cols - 1 || u + 1 == u1) {
         float* pw = P + ((wid * kTilesPerWave + (t - t0)) * B) * kTileRows;
 #pragma unroll
@@ -335,12 +478,12 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
   // Each tile of the workgroup: add the wavefronts' sums in wavefront order;
   // write y if the workgroup covered the whole tile, else hand it over.
   const int tA = U0 / n_cols, tB = (U1 - 1) / n_cols;
-  for (int t = tA + wid; t <= tB; t += 4) {
+  for (int t = tA + wid; t <= tB; t += NW) {
     const int ts = t * n_cols, te = ts + n_cols;
     float s[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) s[b] = 0.0f;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NW; ++i) {
       const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
       if (max(a0, ts) >= min(a1, te)) continue;
       const float* pw = P + ((i * kTilesPerWave + (t - a0 / n_cols)) * B) * kTileRows;
@@ -353,32 +496,50 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvArgs a) {
 }
 
 template <int QT, int B, bool XF32>
-static hipError_t launch_one(const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, KQ_DEPTH>), dim3(grid), dim3(256), lds, s, a);
+static hipError_t launch_one(const GemvArgs& a, int nw, int grid, size_t lds, hipStream_t s) {
+  constexpr bool kMf = !XF32 && B >= kMfmaMinBatch;
+  if (nw == 8)
+    hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, kMf, 8, KQ_DEPTH>), dim3(grid), dim3(512), lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, kMf, 4, KQ_DEPTH>), dim3(grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
 template <int QT, bool XF32>
-static hipError_t launch_b(const GemvArgs& a, int batch, int grid, size_t lds, hipStream_t s) {
+static hipError_t launch_b(const GemvArgs& a, int batch, int nw, int grid, size_t lds, hipStream_t s) {
   switch (batch) {
-    case 1: return launch_one<QT, 1, XF32>(a, grid, lds, s);
-    case 2: return launch_one<QT, 2, XF32>(a, grid, lds, s);
-    case 3: return launch_one<QT, 3, XF32>(a, grid, lds, s);
-    case 4: return launch_one<QT, 4, XF32>(a, grid, lds, s);
-    case 5: return launch_one<QT, 5, XF32>(a, grid, lds, s);
-    case 6: return launch_one<QT, 6, XF32>(a, grid, lds, s);
-    case 7: return launch_one<QT, 7, XF32>(a, grid, lds, s);
-    case 8: return launch_one<QT, 8, XF32>(a, grid, lds, s);
+    case 1: return launch_one<QT, 1, XF32>(a, nw, grid, lds, s);
+    case 2: return launch_one<QT, 2, XF32>(a, nw, grid, lds, s);
+    case 3: return launch_one<QT, 3, XF32>(a, nw, grid, lds, s);
+    case 4: return launch_one<QT, 4, XF32>(a, nw, grid, lds, s);
+    case 5: return launch_one<QT, 5, XF32>(a, nw, grid, lds, s);
+    case 6: return launch_one<QT, 6, XF32>(a, nw, grid, lds, s);
+    case 7: return launch_one<QT, 7, XF32>(a, nw, grid, lds, s);
+    case 8: return launch_one<QT, 8, XF32>(a, nw, grid, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemv(int type, int xtype, int batch, const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
+bool gemv_uses_mfma(int xtype, int batch) { return xtype == KQ_X_BF16 && batch >= kMfmaMinBatch; }
+
+size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, int staged_cols) {
+  const size_t partials = (size_t)nw * kTilesPerWave * batch * kTileRows * sizeof(float);
+  const int sb = type == KQ_Q6_K ? 16 : 8;
+  if (gemv_uses_mfma(xtype, batch)) {
+    const int nb = (batch + 3) / 4;
+    return (size_t)staged_cols * (batch * 512 + sb * nb * 16) + 512 + partials;
+  }
+  const int xwords = xtype == KQ_X_F32 ? 256 : 128;
+  return (size_t)staged_cols * batch * 4 * (xwords + sb) + partials;
+}
+
+hipError_t launch_gemv(int type, int xtype, int batch, int nw, const GemvArgs& a, int grid, size_t lds,
+                       hipStream_t s) {
   const bool f32 = xtype == KQ_X_F32;
   switch (type) {
-    case KQ_Q4_K: return f32 ? launch_b<KQ_Q4_K, true>(a, batch, grid, lds, s) : launch_b<KQ_Q4_K, false>(a, batch, grid, lds, s);
-    case KQ_Q5_K: return f32 ? launch_b<KQ_Q5_K, true>(a, batch, grid, lds, s) : launch_b<KQ_Q5_K, false>(a, batch, grid, lds, s);
-    case KQ_Q6_K: return f32 ? launch_b<KQ_Q6_K, true>(a, batch, grid, lds, s) : launch_b<KQ_Q6_K, false>(a, batch, grid, lds, s);
+    case KQ_Q4_K: return f32 ? launch_b<KQ_Q4_K, true>(a, batch, nw, grid, lds, s) : launch_b<KQ_Q4_K, false>(a, batch, nw, grid, lds, s);
+    case KQ_Q5_K: return f32 ? launch_b<KQ_Q5_K, true>(a, batch, nw, grid, lds, s) : launch_b<KQ_Q5_K, false>(a, batch, nw, grid, lds, s);
+    case KQ_Q6_K: return f32 ? launch_b<KQ_Q6_K, true>(a, batch, nw, grid, lds, s) : launch_b<KQ_Q6_K, false>(a, batch, nw, grid, lds, s);
     default: return hipErrorInvalidValue;
   }
 }

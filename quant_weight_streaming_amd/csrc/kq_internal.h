@@ -26,7 +26,14 @@ struct GemvArgs {
   uint32_t* counters;                  // scratch: [workgroups] arrival counters, zero between calls
 };
 
-hipError_t launch_gemv(int type, int xtype, int batch, const GemvArgs& a, int grid, size_t lds, hipStream_t s);
+// Launch the GEMV with workgroups of `nw` (4 or 8) wavefronts.
+hipError_t launch_gemv(int type, int xtype, int batch, int nw, const GemvArgs& a, int grid, size_t lds,
+                       hipStream_t s);
+// Whether launch_gemv runs this activation type and batch on the matrix cores,
+// and the dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols`
+// columns needs.
+bool gemv_uses_mfma(int xtype, int batch);
+size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, int staged_cols);
 hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s);
 hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo,
                           hipStream_t s);

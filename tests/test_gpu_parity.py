@@ -195,3 +195,13 @@ def test_strided_x():
     y = kq.gemv("q4k", w, rows, cols, xfull.to(DEV)[:, :cols])
     yo, ao = O.gemv("q4k", rows, cols, g.numpy(), x_host(x))
     check_y(y.cpu().numpy(), yo, ao, "strided x")
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("batch", [2, 5, 6, 7])
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_workgroup_sizes(qtype, batch, waves, monkeypatch):
+    """Both workgroup shapes (4 and 8 wavefronts, KQ_WG_WAVES) on the matrix-core path, including
+    batches that leave some of an instruction's four result registers unread (5, 6, 7)."""
+    monkeypatch.setenv("KQ_WG_WAVES", waves)
+    run_case(qtype, 5 * 64 + 9, 7 * 256, batch, "bf16", 400 + batch, check_w=False)
