@@ -86,6 +86,13 @@ static int waves_per_cu() {
 
 constexpr int kWideBatch = 2;
 
+// Batches from which column windows are used (KQ_WINDOWS_FROM overrides; 9 = never).
+static int windows_from_batch() {
+  const char* e = getenv("KQ_WINDOWS_FROM");
+  const int x = e ? atoi(e) : 0;
+  return (x >= 1 && x <= 9) ? x : 4;
+}
+
 static int wg_waves(int batch) {
   const char* e = getenv("KQ_WG_WAVES");
   const int x = e ? atoi(e) : 0;
@@ -153,7 +160,30 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
     if ((n_cols > max_cols && nw * upw > max_cols) || upw > n_cols + 1) return KQ_ERR_RANGE;
     n_groups = (n_units + nw * upw - 1) / (nw * upw);
   }
-  const int64_t tcols = n_cols < nw * upw ? n_cols : nw * upw;
+  int64_t tcols = n_cols < nw * upw ? n_cols : nw * upw;
+  int64_t grid = (n_groups + 7) / 8 * 8;  // whole XCD rounds for the block remap
+
+  // Column windows: when a long row does not fit the staging budget, split the
+  // columns into n_win windows of at most max_cols and give each workgroup whole
+  // tiles of one window, so its staged activations serve several row tiles
+  // (worth it where the activations are large next to the weights).
+  a.n_win = 1;
+  a.n_tiles = (int32_t)tiles;
+  const int64_t n_win = (n_cols + max_cols - 1) / max_cols;
+  if (batch >= windows_from_batch() && n_win > 1 && tiles <= kMaxGroups && n_win * tiles <= 2 * (int64_t)kMaxGroups) {
+    const int64_t g_target = (int64_t)st->cus * waves_per_cu() / nw;
+    int64_t g_win = g_target / n_win > 0 ? g_target / n_win : 1;
+    int64_t r = (tiles + g_win - 1) / g_win;
+    if (r > nw) r = nw;                      // a wavefront's run then touches at most two tiles
+    g_win = (tiles + r - 1) / r;
+    a.n_win = (int32_t)n_win;
+    a.win_base = (int32_t)(n_cols / n_win);
+    a.win_extra = (int32_t)(n_cols % n_win);
+    a.wg_per_win = (int32_t)g_win;
+    a.tiles_per_wg = (int32_t)r;
+    tcols = a.win_base + (a.win_extra ? 1 : 0);
+    grid = (n_win * g_win + 7) / 8 * 8;
+  }
   a.nproj = n;
   a.n_cols = (int32_t)n_cols;
   a.x = x;
@@ -164,7 +194,6 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   a.partial = st->partial;
   a.counters = st->counters;
   const size_t lds = gemv_lds_bytes(type, xtype, batch, nw, (int)tcols);
-  const int64_t grid = (n_groups + 7) / 8 * 8;  // whole XCD rounds for the block remap
   if (launch_gemv(type, xtype, batch, nw, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;

@@ -372,6 +372,45 @@ __device__ __forceinline__ void hand_off(const GemvArgs& a, int t, int L, int wg
   if (lane == 0) __hip_atomic_store(&a.counters[la], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Windowed variant: the workgroup of window w holds tile t's sum over that
+// window's columns.  Every window contributes one piece per tile; the last to
+// arrive adds them in window order.  Same publication protocol as hand_off.
+template <int B>
+__device__ __forceinline__ void hand_off_windows(const GemvArgs& a, int t, int w, int lane, const float* v) {
+  float* mine = a.partial + (int64_t)(w * a.n_tiles + t) * kPartialStride;
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+    __hip_atomic_store(mine + b * kTileRows + lane, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old != (uint32_t)(a.n_win - 1)) return;
+  asm volatile("" ::: "memory");
+  float s[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) s[b] = 0.0f;
+  for (int w0 = 0; w0 < a.n_win; w0 += 4) {
+    float q[4][B];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* pp = a.partial + (int64_t)((w0 + j) * a.n_tiles + t) * kPartialStride;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        q[j][b] = w0 + j < a.n_win
+                      ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (w0 + j < a.n_win) s[b] += q[j][b];
+  }
+  write_tile<B>(a, t, lane, s);
+  if (lane == 0) __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH>
 __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   using F = Fmt<QT>;
@@ -385,12 +424,30 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   // blocks (which share split tiles) go to one XCD.
   const int nb8 = gridDim.x >> 3;
   const int lblock = (blockIdx.x & 7) * nb8 + (blockIdx.x >> 3);
-  const int n_cols = a.n_cols, upw = a.upw, wgu = NW * upw;
-  const int U0 = lblock * wgu;                     // the workgroup's run of units [U0, U1)
-  if (U0 >= a.n_units) return;                     // whole workgroup idle
-  const int U1 = min(U0 + wgu, a.n_units);
-  const int c0w = U0 % n_cols;
-  const int len = min(n_cols, U1 - U0);
+  const int n_cols = a.n_cols;
+  // The workgroup's columns [cs, cs + cw) and its run of units [U0, U1),
+  // numbered tile-major inside those columns (unit u: tile u / cw, column
+  // cs + u % cw).  Without windows cs = 0, cw = n_cols and the runs split the
+  // whole unit range evenly; with windows each workgroup takes whole tiles of
+  // one window.
+  int cs = 0, cw = n_cols, w = 0, U0, U1, upw;
+  if (a.n_win > 1) {
+    w = lblock / a.wg_per_win;
+    const int t_first = (lblock - w * a.wg_per_win) * a.tiles_per_wg;
+    if (w >= a.n_win || t_first >= a.n_tiles) return;   // whole workgroup idle
+    cs = w * a.win_base + min(w, a.win_extra);
+    cw = a.win_base + (w < a.win_extra ? 1 : 0);
+    U0 = t_first * cw;
+    U1 = min(t_first + a.tiles_per_wg, a.n_tiles) * cw;
+    upw = (a.tiles_per_wg * cw + NW - 1) / NW;
+  } else {
+    upw = a.upw;
+    U0 = lblock * NW * upw;
+    if (U0 >= a.n_units) return;                     // whole workgroup idle
+    U1 = min(U0 + NW * upw, a.n_units);
+  }
+  const int c0w = cs + U0 % cw;                    // staged columns c0w, c0w+1, ... (mod n_cols)
+  const int len = min(cw, U1 - U0);
   uint32_t* X = lds_words;
   float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);
   // per-wavefront tile sums [NW][kTilesPerWave][B][64] follow the staged columns
@@ -400,7 +457,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   const int u0 = U0 + wid * upw;
   const int u1 = min(u0 + upw, U1);
   const bool active = u0 < U1;
-  const int t0 = u0 / n_cols;                      // first tile of this wavefront
+  const int t0 = u0 / cw;                          // first tile of this wavefront
   const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
 
   // The weight stream runs DEPTH-1 units ahead of the unit being computed.
@@ -410,11 +467,11 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   uint32_t d6[DEPTH];
 #pragma unroll
   for (int k = 0; k < DEPTH; ++k) d6[k] = 0;       // Q4_K / Q5_K never load it
-  int ul = u0, tl = t0, cl = u0 % n_cols;          // next unit to load
+  int ul = u0, tl = t0, cl = cs + u0 % cw;         // next unit to load
   auto refill = [&](int k) {
     load_unit<QT>(unit_rsrc<QT>(a, tl, cl, ul < u1), lane, buf[k], d6[k]);
     ++ul;
-    if (++cl == n_cols) { cl = 0; ++tl; }
+    if (++cl == cs + cw) { cl = cs; ++tl; }
     // keep the loads ahead of the computation that follows: neither the IR
     // passes nor the machine scheduler may move work across this point
     asm volatile("" ::: "memory");
@@ -430,9 +487,9 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-    int t = t0, c = u0 % n_cols;
+    int t = t0, c = cs + u0 % cw;
     int ic = c - c0w;
-    if (ic < 0) ic += n_cols;
+    if (ic < 0) ic += cw;
     int u = u0;
     // consume buf[k] (unit u); at a tile's last unit or the run's end park the sum in LDS
     auto consume = [&](int k) {
@@ -449,7 +506,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
       } else {
         process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
       }
-      if (c == n_cols - 1 || u + 1 == u1) {
+      if (c == cs + cw - 1 || u + 1 == u1) {
         float* pw = P + ((wid * kTilesPerWave + (t - t0)) * B) * kTileRows;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -458,8 +515,8 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
         }
       }
       ++u;
-      if (++c == n_cols) { c = 0; ++t; }
-      if (++ic == n_cols) ic = 0;
+      if (++c == cs + cw) { c = cs; ++t; }
+      if (++ic == cw) ic = 0;
     };
     // Each step issues the load of unit u+DEPTH-1 into the buffer the previous
     // step freed, then computes unit u.  Loads past the run are issued too,
@@ -477,21 +534,22 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
 
   // Each tile of the workgroup: add the wavefronts' sums in wavefront order;
   // write y if the workgroup covered the whole tile, else hand it over.
-  const int tA = U0 / n_cols, tB = (U1 - 1) / n_cols;
+  const int tA = U0 / cw, tB = (U1 - 1) / cw;
   for (int t = tA + wid; t <= tB; t += NW) {
-    const int ts = t * n_cols, te = ts + n_cols;
+    const int ts = t * cw, te = ts + cw;
     float s[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) s[b] = 0.0f;
     for (int i = 0; i < NW; ++i) {
       const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
       if (max(a0, ts) >= min(a1, te)) continue;
-      const float* pw = P + ((i * kTilesPerWave + (t - a0 / n_cols)) * B) * kTileRows;
+      const float* pw = P + ((i * kTilesPerWave + (t - a0 / cw)) * B) * kTileRows;
 #pragma unroll
       for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
     }
-    if (ts >= U0 && te <= U1) write_tile<B>(a, t, lane, s);
-    else hand_off<B>(a, t, lblock, wgu, lane, s);
+    if (a.n_win > 1) hand_off_windows<B>(a, t, w, lane, s);
+    else if (ts >= U0 && te <= U1) write_tile<B>(a, t, lane, s);
+    else hand_off<B>(a, t, lblock, NW * upw, lane, s);
   }
 }
 

@@ -21,9 +21,12 @@ struct GemvArgs {
   int64_t ldx;                         // activation row stride (elements)
   int32_t n_units;                     // total tiles * n_cols
   int32_t upw;                         // units per wavefront
-  int32_t tsb;                         // columns staged in LDS per workgroup: min(n_cols, 4 * upw)
-  float* partial;                      // scratch: [workgroups][2][KQ_MAX_BATCH][64] partial sums
-  uint32_t* counters;                  // scratch: [workgroups] arrival counters, zero between calls
+  int32_t tsb;                         // LDS capacity in staged columns per workgroup
+  // Column windows (n_win > 1): window w covers win_base (+1 for w < win_extra)
+  // columns; wg_per_win workgroups per window each take tiles_per_wg whole tiles.
+  int32_t n_win, win_base, win_extra, wg_per_win, tiles_per_wg, n_tiles;
+  float* partial;                      // scratch: [workgroups][2] (windows: [n_win][n_tiles]) x [KQ_MAX_BATCH][64]
+  uint32_t* counters;                  // scratch: arrival counters per split tile, zero between calls
 };
 
 // Launch the GEMV with workgroups of `nw` (4 or 8) wavefronts.

@@ -205,3 +205,14 @@ def test_workgroup_sizes(qtype, batch, waves, monkeypatch):
     batches that leave some of an instruction's four result registers unread (5, 6, 7)."""
     monkeypatch.setenv("KQ_WG_WAVES", waves)
     run_case(qtype, 5 * 64 + 9, 7 * 256, batch, "bf16", 400 + batch, check_w=False)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("batch,xdtype,windows_from", [(4, "bf16", None), (8, "bf16", None), (2, "bf16", "2"),
+                                                       (4, "f32", None), (1, "bf16", "1")])
+def test_column_windows(qtype, batch, xdtype, windows_from, monkeypatch):
+    """Rows longer than the staging budget: each workgroup takes whole tiles of one column window and
+    the windows' pieces of a tile are added in window order (K = 31232, the down projection's)."""
+    if windows_from:
+        monkeypatch.setenv("KQ_WINDOWS_FROM", windows_from)
+    run_case(qtype, 5 * 64 + 9, 122 * 256, batch, xdtype, 500 + batch, check_w=False)
