@@ -86,6 +86,13 @@ static int waves_per_cu() {
 
 constexpr int kWideBatch = 2;
 
+// Whole tiles per workgroup forced for every shape (KQ_ALIGNED_TILES; 0 = automatic).
+static int aligned_tiles() {
+  const char* e = getenv("KQ_ALIGNED_TILES");
+  const int x = e ? atoi(e) : 0;
+  return (x >= 1 && x <= 8) ? x : 0;
+}
+
 // Batches from which column windows are used (KQ_WINDOWS_FROM overrides; 9 = never).
 static int windows_from_batch() {
   const char* e = getenv("KQ_WINDOWS_FROM");
@@ -169,11 +176,14 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   // (worth it where the activations are large next to the weights).
   a.n_win = 1;
   a.n_tiles = (int32_t)tiles;
+  a.tiles_per_wg = 0;
   const int64_t n_win = (n_cols + max_cols - 1) / max_cols;
-  if (batch >= windows_from_batch() && n_win > 1 && tiles <= kMaxGroups && n_win * tiles <= 2 * (int64_t)kMaxGroups) {
+  const int forced_r = aligned_tiles();
+  if (((batch >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
+      n_win * tiles <= 2 * (int64_t)kMaxGroups) {
     const int64_t g_target = (int64_t)st->cus * waves_per_cu() / nw;
     int64_t g_win = g_target / n_win > 0 ? g_target / n_win : 1;
-    int64_t r = (tiles + g_win - 1) / g_win;
+    int64_t r = forced_r > 0 ? forced_r : (tiles + g_win - 1) / g_win;
     if (r > nw) r = nw;                      // a wavefront's run then touches at most two tiles
     g_win = (tiles + r - 1) / r;
     a.n_win = (int32_t)n_win;

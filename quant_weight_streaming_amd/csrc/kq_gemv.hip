@@ -74,48 +74,75 @@ __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, int lane, u3
     d6 = __builtin_amdgcn_raw_buffer_load_b16(r, 13 * kChunkStride + 2 * lane, 0, kCacheNT);
 }
 
-// Stage the activations of the workgroup's columns c0, c0+1, ... (mod n_cols)
-// in LDS, and T, the per-sub-block activation sums in the dot product's own
-// order (bf16: the same dot2 chain over (128,128), Q6_K (160,160); fp32: sum x).
-// X layout: [ic][b][256 elements]; T layout: [ic * sub-blocks + g][b].
-template <int QT, int B, bool XF32, int NT>
-__device__ __forceinline__ void stage_x_T(const GemvArgs& a, uint32_t* X, float* T, int c0, int len) {
+// Staging of the activations of the workgroup's columns c0, c0+1, ... (mod
+// n_cols) in LDS: X [ic][b][256 elements], rows RS bytes apart.  The work is cut into items of one
+// sub-block of one batch row; each thread issues the loads of IPT items (128
+// bytes) before it stores any of them, so a round costs one memory round trip,
+// and the first round is issued ahead of the weight prologue so that waiting
+// for it does not wait for the weights.  On the dot2 path the store also forms
+// T, the item's activation sum in the dot product's own order (bf16: the same
+// dot2 chain over (128,128), Q6_K (160,160); fp32: sum x), at T[ic * SB + g][b].
+template <int QT, int B, bool XF32, int NW, int RS>
+struct XStage {
   using F = Fmt<QT>;
-  constexpr int XW = XF32 ? 256 : 128;              // 32-bit words of x per column and batch row
-  constexpr int SW = XF32 ? F::kSubW : F::kSubW / 2;  // words per sub-block
-  const int n = len * F::kSubBlocks;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const int ic = i / F::kSubBlocks, g = i - ic * F::kSubBlocks;
-    int c = c0 + ic;
-    if (c >= a.n_cols) c -= a.n_cols;
-    const int64_t k0 = (int64_t)c * 256 + g * F::kSubW;
+  static constexpr int SB = F::kSubBlocks;
+  static constexpr int ES = XF32 ? 4 : 2;                   // bytes per element
+  static constexpr int VPI = F::kSubW * ES / 16;            // 16-byte vectors per item
+  static constexpr int IPT = VPI >= 8 ? 1 : 8 / VPI;        // items per thread and round
+  static constexpr int NT = 64 * NW;
+  u32x4 v[IPT][VPI];
+
+  __device__ __forceinline__ static int rounds(int len) { return (len * B * SB + IPT * NT - 1) / (IPT * NT); }
+
+  __device__ __forceinline__ void load(const GemvArgs& a, int c0, int len, int r) {
+    const int n = len * B * SB;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const u32x4* xp = XF32 ? reinterpret_cast<const u32x4*>(static_cast<const float*>(a.x) + b * a.ldx + k0)
-                             : reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + b * a.ldx + k0);
-      u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * XW + g * SW);
-      float t = 0.0f;
-      const uint32_t Kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;  // bf16 (160,160) / (128,128)
+    for (int j = 0; j < IPT; ++j) {
+      const int i = (r * IPT + j) * NT + threadIdx.x;
+      if (i < n) {
+        const int g = i % SB, q = i / SB, b = q % B, ic = q / B;
+        int c = c0 + ic;
+        if (c >= a.n_cols) c -= a.n_cols;
+        const uint8_t* xp = static_cast<const uint8_t*>(a.x) +
+                            ((int64_t)b * a.ldx + (int64_t)c * 256 + g * F::kSubW) * ES;
 #pragma unroll
-      for (int v = 0; v < SW / 4; ++v) {
-        const u32x4 xv = xp[v];
-        xl[v] = xv;
-        if constexpr (!XF32) {
-          t = dot2_bf16(Kc, xv.x, t);
-          t = dot2_bf16(Kc, xv.y, t);
-          t = dot2_bf16(Kc, xv.z, t);
-          t = dot2_bf16(Kc, xv.w, t);
-        } else {
-          t += __uint_as_float(xv.x);
-          t += __uint_as_float(xv.y);
-          t += __uint_as_float(xv.z);
-          t += __uint_as_float(xv.w);
-        }
+        for (int e = 0; e < VPI; ++e) v[j][e] = reinterpret_cast<const u32x4*>(xp)[e];
       }
-      T[i * B + b] = t;
     }
   }
-}
+
+  template <bool WITH_T>
+  __device__ __forceinline__ void store(uint8_t* X, float* T, int len, int r) const {
+    const int n = len * B * SB;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = (r * IPT + j) * NT + threadIdx.x;
+      if (i < n) {
+        const int g = i % SB, q = i / SB, b = q % B, ic = q / B;
+        u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * ES);
+        float t = 0.0f;
+        const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;  // bf16 (160,160) / (128,128)
+#pragma unroll
+        for (int e = 0; e < VPI; ++e) {
+          const u32x4 xv = v[j][e];
+          xl[e] = xv;
+          if constexpr (WITH_T && !XF32) {
+            t = dot2_bf16(kc, xv.x, t);
+            t = dot2_bf16(kc, xv.y, t);
+            t = dot2_bf16(kc, xv.z, t);
+            t = dot2_bf16(kc, xv.w, t);
+          } else if constexpr (WITH_T) {
+            t += __uint_as_float(xv.x);
+            t += __uint_as_float(xv.y);
+            t += __uint_as_float(xv.z);
+            t += __uint_as_float(xv.w);
+          }
+        }
+        if constexpr (WITH_T) T[(ic * SB + g) * B + b] = t;
+      }
+    }
+  }
+};
 
 // Accumulate one unit into acc[B].  Xc / Tc: the staged activations and sums of
 // the unit's column.  The (sub-block, batch row) steps are software-pipelined:
@@ -209,12 +236,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Byte offsets inside the workgroup's LDS for the matrix-core path:
-//   X [ic][b][256] bf16 (B * 512 bytes per column), then T [ic][g][NB][4] floats,
-//   then Z, 512 zero bytes that the inactive operand lanes read.
+//   X [ic][b][256] bf16 in rows of kXRow = 528 bytes (the 16-byte pad puts the
+//   four batch rows one instruction reads in different LDS banks), then
+//   T [ic][g][NB][4] floats, then Z, 512 zero bytes that the inactive operand
+//   lanes read.
 template <int QT, int B>
 struct MfmaLds {
   static constexpr int NB = (B + 3) / 4;                       // operand sets of 4 batch rows
-  static constexpr int kXCol = B * 512;                        // bytes of x per column
+  static constexpr int kXRow = 528;                            // bytes per staged row of x
+  static constexpr int kXCol = B * kXRow;                      // bytes of x per column
   static constexpr int kTCol = Fmt<QT>::kSubBlocks * NB * 16;  // bytes of T per column
   static constexpr int kPerCol = kXCol + kTCol;
 };
@@ -224,42 +254,54 @@ template <int B>
 __device__ __forceinline__ int a_operand_offset(int lane, int gb, int ic, int x_base, int z_base) {
   const int b = 4 * gb + (lane & 3);
   const bool active = ((lane & 15) >> 2) == (lane >> 4) && b < B;
-  return active ? x_base + ic * B * 512 + b * 512 : z_base;
+  return active ? x_base + (ic * B + b) * 528 : z_base;
 }
 
+// T for the matrix-core path, from the staged activations (after a barrier):
+// T[ic][g][gb][b'] = the sub-block's products with every weight equal to the
+// offset, as the same instruction sequence computes them.  The matrix core
+// gives every output position the same arithmetic (the value does not depend
+// on the lane group that holds it), so one chain serves four items: lane group
+// j = lane / 16 takes item 4c + j's activations into its block of the operand.
+// A wavefront runs two chains interleaved.
 template <int QT, int B, int NW>
-__device__ __forceinline__ void stage_x_mfma(const GemvArgs& a, uint8_t* lds, int c0, int len, int wid, int lane) {
+__device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int lane) {
   using F = Fmt<QT>;
   using L = MfmaLds<QT, B>;
   constexpr int NB = L::NB, SB = F::kSubBlocks, KB = F::kSubW / 8;
   const int t_base = len * L::kXCol, z_base = t_base + len * L::kTCol;
-  // x of the workgroup's columns, 16 bytes per thread and step
-  const int nv = len * B * 32;
-  for (int i = threadIdx.x; i < nv; i += 64 * NW) {
-    const int ic = i / (B * 32), r = i - ic * (B * 32), b = r >> 5, v = r & 31;
-    int c = c0 + ic;
-    if (c >= a.n_cols) c -= a.n_cols;
-    const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + b * a.ldx +
-                                                     (int64_t)c * 256) + v;
-    *reinterpret_cast<u32x4*>(lds + (ic * B + b) * 512 + v * 16) = *xp;
-  }
-  if (threadIdx.x < 32) *reinterpret_cast<u32x4*>(lds + z_base + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
-  // T[ic][g][gb][b'] = the sub-block's products with every weight = the offset
   const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;
   const bf16x8 bconst = __builtin_bit_cast(bf16x8, u32x4{kc, kc, kc, kc});
-  for (int i = wid; i < len * SB; i += NW) {
-    const int ic = i / SB, g = i - ic * SB;
+  const int nt = len * SB, nch = (nt + 3) / 4;
+  for (int c0 = wid; c0 < nch; c0 += 2 * NW) {
+    int it[2];
+    const uint8_t* ap[2][NB];
+    f32x4 t[2][NB];
 #pragma unroll
-    for (int gb = 0; gb < NB; ++gb) {
-      const uint8_t* ap = lds + a_operand_offset<B>(lane, gb, ic, 0, z_base) + g * F::kSubW * 2;
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      const int ch = min(c0 + h * NW, nch - 1);
+      it[h] = min(4 * ch + (lane >> 4), nt - 1);
+      const int ic = it[h] / SB, g = it[h] - ic * SB;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(ap + kb * 16), bconst, t,
-                                                    0, 0, 0);
-      if (lane == 0) *reinterpret_cast<f32x4*>(lds + t_base + ((ic * SB + g) * NB + gb) * 16) = t;
+      for (int gb = 0; gb < NB; ++gb) {
+        ap[h][gb] = lds + a_operand_offset<B>(lane, gb, ic, 0, z_base) + g * F::kSubW * 2;
+        t[h][gb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int gb = 0; gb < NB; ++gb)
+          t[h][gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(ap[h][gb] + kb * 16),
+                                                             bconst, t[h][gb], 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (c0 + h * NW < nch && 4 * (c0 + h * NW) + (lane >> 4) < nt && (lane & 15) == 0)
+#pragma unroll
+        for (int gb = 0; gb < NB; ++gb)
+          *reinterpret_cast<f32x4*>(lds + t_base + (it[h] * NB + gb) * 16) = t[h][gb];
   }
 }
 
@@ -431,7 +473,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   // whole unit range evenly; with windows each workgroup takes whole tiles of
   // one window.
   int cs = 0, cw = n_cols, w = 0, U0, U1, upw;
-  if (a.n_win > 1) {
+  if (a.tiles_per_wg > 0) {
     w = lblock / a.wg_per_win;
     const int t_first = (lblock - w * a.wg_per_win) * a.tiles_per_wg;
     if (w >= a.n_win || t_first >= a.n_tiles) return;   // whole workgroup idle
@@ -477,10 +519,27 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // first round of activation loads, then the weight prologue, then the stores
+  constexpr int kRS = MF ? MfmaLds<QT, B>::kXRow : 256 * (XF32 ? 4 : 2);
+  XStage<QT, B, XF32, NW, kRS> xs;
+  xs.load(a, c0w, len, 0);
 #pragma unroll
   for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
-  if constexpr (MF) stage_x_mfma<QT, B, NW>(a, reinterpret_cast<uint8_t*>(lds_words), c0w, len, wid, lane);
-  else stage_x_T<QT, B, XF32, 64 * NW>(a, X, T, c0w, len);
+  {
+    uint8_t* Xb = reinterpret_cast<uint8_t*>(lds_words);
+    xs.template store<!MF>(Xb, T, len, 0);
+    const int nr = XStage<QT, B, XF32, NW, kRS>::rounds(len);
+    for (int r = 1; r < nr; ++r) {
+      xs.load(a, c0w, len, r);
+      xs.template store<!MF>(Xb, T, len, r);
+    }
+    if constexpr (MF) {
+      const int z_base = len * MfmaLds<QT, B>::kPerCol;
+      if (threadIdx.x < 32) *reinterpret_cast<u32x4*>(Xb + z_base + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+      stage_T_mfma<QT, B, NW>(Xb, len, wid, lane);
+    }
+  }
   __syncthreads();
 
   if (active) {
@@ -548,7 +607,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
       for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
     }
     if (a.n_win > 1) hand_off_windows<B>(a, t, w, lane, s);
-    else if (ts >= U0 && te <= U1) write_tile<B>(a, t, lane, s);
+    else if (ts >= U0 && te <= U1) write_tile<B>(a, t, lane, s);   // every tile when tiles_per_wg > 0
     else hand_off<B>(a, t, lblock, NW * upw, lane, s);
   }
 }
@@ -585,7 +644,7 @@ size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, int staged_cols) {
   const int sb = type == KQ_Q6_K ? 16 : 8;
   if (gemv_uses_mfma(xtype, batch)) {
     const int nb = (batch + 3) / 4;
-    return (size_t)staged_cols * (batch * 512 + sb * nb * 16) + 512 + partials;
+    return (size_t)staged_cols * (batch * 528 + sb * nb * 16) + 512 + partials;
   }
   const int xwords = xtype == KQ_X_F32 ? 256 : 128;
   return (size_t)staged_cols * batch * 4 * (xwords + sb) + partials;

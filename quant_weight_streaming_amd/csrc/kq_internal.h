@@ -22,8 +22,10 @@ struct GemvArgs {
   int32_t n_units;                     // total tiles * n_cols
   int32_t upw;                         // units per wavefront
   int32_t tsb;                         // LDS capacity in staged columns per workgroup
-  // Column windows (n_win > 1): window w covers win_base (+1 for w < win_extra)
-  // columns; wg_per_win workgroups per window each take tiles_per_wg whole tiles.
+  // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
+  // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
+  // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even
+  // runs of upw units per wavefront over the whole unit range.
   int32_t n_win, win_base, win_extra, wg_per_win, tiles_per_wg, n_tiles;
   float* partial;                      // scratch: [workgroups][2] (windows: [n_win][n_tiles]) x [KQ_MAX_BATCH][64]
   uint32_t* counters;                  // scratch: arrival counters per split tile, zero between calls
