@@ -235,6 +235,56 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Chains of v_mfma_f32_16x16x32_bf16 accumulating over KB blocks of 8 columns,
+// one or two accumulators (operand sets), each chain a single inline-assembly
+// statement: the result registers are the accumulator registers (left to
+// itself this compiler can give a chained instruction a result that partially
+// overlaps its own accumulator input), and nothing else touches them before the
+// chain has completed.  The hazard waits are therefore ours: two wait states
+// before the first instruction (for a VALU write of an operand just before it)
+// and eight after the last one before the result may be read (measured on the
+// device: seven suffice).
+#define KQ_MF(D, A, B, C) "v_mfma_f32_16x16x32_bf16 " D ", " A ", " B ", " C "\n\t"
+template <int KB>
+__device__ __forceinline__ void mfma_chain(f32x4& s, const bf16x8* a, const bf16x8* b);
+template <>
+__device__ __forceinline__ void mfma_chain<4>(f32x4& s, const bf16x8* a, const bf16x8* b) {
+  asm volatile("s_nop 1\n\t" KQ_MF("%0", "%1", "%5", "0") KQ_MF("%0", "%2", "%6", "%0") KQ_MF("%0", "%3", "%7", "%0")
+                   KQ_MF("%0", "%4", "%8", "%0") "s_nop 7"
+               : "=&v"(s)
+               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+}
+template <>
+__device__ __forceinline__ void mfma_chain<2>(f32x4& s, const bf16x8* a, const bf16x8* b) {
+  asm volatile("s_nop 1\n\t" KQ_MF("%0", "%1", "%3", "0") KQ_MF("%0", "%2", "%4", "%0") "s_nop 7"
+               : "=&v"(s)
+               : "v"(a[0]), "v"(a[1]), "v"(b[0]), "v"(b[1]));
+}
+// Two accumulators sharing the weight operands b: s0 with a0[kb], s1 with a1[kb].
+template <int KB>
+__device__ __forceinline__ void mfma_chain2(f32x4& s0, f32x4& s1, const bf16x8* a0, const bf16x8* a1,
+                                            const bf16x8* b);
+template <>
+__device__ __forceinline__ void mfma_chain2<4>(f32x4& s0, f32x4& s1, const bf16x8* a0, const bf16x8* a1,
+                                               const bf16x8* b) {
+  asm volatile("s_nop 1\n\t" KQ_MF("%0", "%2", "%10", "0") KQ_MF("%1", "%6", "%10", "0")
+                   KQ_MF("%0", "%3", "%11", "%0") KQ_MF("%1", "%7", "%11", "%1")
+                   KQ_MF("%0", "%4", "%12", "%0") KQ_MF("%1", "%8", "%12", "%1")
+                   KQ_MF("%0", "%5", "%13", "%0") KQ_MF("%1", "%9", "%13", "%1") "s_nop 7"
+               : "=&v"(s0), "=&v"(s1)
+               : "v"(a0[0]), "v"(a0[1]), "v"(a0[2]), "v"(a0[3]), "v"(a1[0]), "v"(a1[1]), "v"(a1[2]), "v"(a1[3]),
+                 "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+}
+template <>
+__device__ __forceinline__ void mfma_chain2<2>(f32x4& s0, f32x4& s1, const bf16x8* a0, const bf16x8* a1,
+                                               const bf16x8* b) {
+  asm volatile("s_nop 1\n\t" KQ_MF("%0", "%2", "%6", "0") KQ_MF("%1", "%4", "%6", "0")
+                   KQ_MF("%0", "%3", "%7", "%0") KQ_MF("%1", "%5", "%7", "%1") "s_nop 7"
+               : "=&v"(s0), "=&v"(s1)
+               : "v"(a0[0]), "v"(a0[1]), "v"(a1[0]), "v"(a1[1]), "v"(b[0]), "v"(b[1]));
+}
+#undef KQ_MF
+
 // Byte offsets inside the workgroup's LDS for the matrix-core path:
 //   X [ic][b][256] bf16 in rows of kXRow = 528 bytes (the 16-byte pad puts the
 //   four batch rows one instruction reads in different LDS banks), then
@@ -285,17 +335,22 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
 #pragma unroll
       for (int gb = 0; gb < NB; ++gb) {
         ap[h][gb] = lds + a_operand_offset<B>(lane, gb, ic, 0, z_base) + g * F::kSubW * 2;
-        t[h][gb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
+    bf16x8 av[2][NB][KB], bc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) bc[kb] = bconst;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int gb = 0; gb < NB; ++gb)
-          t[h][gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(ap[h][gb] + kb * 16),
-                                                             bconst, t[h][gb], 0, 0, 0);
+        for (int gb = 0; gb < NB; ++gb) av[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[h][gb] + kb * 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (NB == 1) mfma_chain<KB>(t[h][0], av[h][0], bc);
+      else mfma_chain2<KB>(t[h][0], t[h][NB - 1], av[h][0], av[h][NB - 1], bc);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (c0 + h * NW < nch && 4 * (c0 + h * NW) + (lane >> 4) < nt && (lane & 15) == 0)
@@ -306,7 +361,9 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
 }
 
 // One unit on the matrix cores: ap[gb] are this lane's A-operand pointers for
-// the unit's column, Tc the column's T block.
+// the unit's column, Tc the column's T block.  The operands and T of sub-block
+// g+1 are read from LDS while sub-block g is on the matrix core, so the read
+// latency is not paid per instruction.
 template <int QT, int B>
 __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6, const uint8_t* const* ap,
                                                   const float* Tc, float* acc, uint32_t M, uint32_t K) {
@@ -314,24 +371,34 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
   constexpr int SB = F::kSubBlocks, NP = F::kPairs, KB = F::kSubW / 8, NB = MfmaLds<QT, B>::NB;
   float ca[SB], cm[SB];
   sb_coeffs<QT>(buf, d6, 0.0078125f, ca, cm);
+  bf16x8 A[2][NB][KB];
+  f32x4 Tv[2][NB];
+  auto read_operands = [&](int g, int h) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int gb = 0; gb < NB; ++gb)
+        A[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
+#pragma unroll
+    for (int gb = 0; gb < NB; ++gb) Tv[h][gb] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+  };
+  read_operands(0, 0);
   uint32_t pr[NP];
 #pragma unroll
   for (int g = 0; g < SB; ++g) {
+    const int h = g & 1;
+    if (g + 1 < SB) read_operands(g + 1, h ^ 1);
     unpack_pairs<QT>(buf, g, M, K, pr);
+    bf16x8 bop[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      bop[kb] = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
     f32x4 S[NB];
-#pragma unroll
-    for (int gb = 0; gb < NB; ++gb) S[gb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
-#pragma unroll
-      for (int gb = 0; gb < NB; ++gb)
-        S[gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2), bop, S[gb], 0, 0, 0);
-    }
+    if constexpr (NB == 1) mfma_chain<KB>(S[0], A[h][0], bop);
+    else mfma_chain2<KB>(S[0], S[NB - 1], A[h][0], A[h][NB - 1], bop);
 #pragma unroll
     for (int gb = 0; gb < NB; ++gb) {
-      const f32x4 t = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+      const f32x4 t = Tv[h][gb];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (4 * gb + r < B) {
@@ -340,11 +407,6 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
           if constexpr (QT != KQ_Q6_K) v = __builtin_fmaf(-cm[g], t[r], v);
         }
       }
-      // The instruction writes all four result registers when it completes;
-      // keep all four allocated until here, also when fewer than four batch
-      // rows of this set are read, so that nothing else is placed in them
-      // while the write is still pending.
-      asm volatile("" ::"v"(S[gb]));
     }
   }
 }
