@@ -253,8 +253,9 @@ def load_traffic(name: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def profile_kernel(n: int):
-    """Only the dominant kernel (gate+up Q4_K, batch 1): n launches over 8 distinct weight copies."""
+def profile_kernel(n: int, batch: int = 1):
+    """Only the dominant kernel (gate+up Q4_K, batch 1 unless asked otherwise): n launches over 8
+    distinct weight copies."""
     import torch
     from quant_weight_streaming_amd import kq, synth
     spec = synth.GATE_UP
@@ -265,12 +266,12 @@ def profile_kernel(n: int):
         copies.append([kq.repack("q4k", g[:spec.parts[0]].contiguous(), spec.parts[0], spec.cols),
                        kq.repack("q4k", g[spec.parts[0]:].contiguous(), spec.parts[1], spec.cols)])
         del g
-    x = synth.gen_x(1, spec.cols, 1, device="cuda:0")
-    ys = [torch.empty((1, r), device="cuda:0") for r in spec.parts]
+    x = synth.gen_x(batch, spec.cols, 1, device="cuda:0")
+    ys = [torch.empty((batch, r), device="cuda:0") for r in spec.parts]
     for i in range(n):
         kq.kq_gemv_multi("q4k", copies[i % 8], list(spec.parts), spec.cols, x, ys)
     torch.cuda.synchronize()
-    log(f"[bench] profile-kernel: {n} launches done")
+    log(f"[bench] profile-kernel: {n} launches at batch {batch} done")
 
 
 def copy_calibration(n: int):
@@ -348,6 +349,7 @@ def main():
     ap.add_argument("--no-c4", action="store_true", help="skip the Q5_K / merged-sub-block sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--profile-kernel", type=int, default=0)
+    ap.add_argument("--profile-batch", type=int, default=1, help="batch of the --profile-kernel launches")
     ap.add_argument("--copy-calibration", type=int, default=0, help="N plain 1 GiB device copies")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("ROCPROF_DIR", "COMMAND"),
                     help="print a text summary of a rocprofv3 kernel-trace run of this benchmark")
@@ -369,7 +371,7 @@ def main():
         sys.exit(2)
     sys.path.insert(0, ROOT)
     if args.profile_kernel:
-        return profile_kernel(args.profile_kernel)
+        return profile_kernel(args.profile_kernel, args.profile_batch)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
 

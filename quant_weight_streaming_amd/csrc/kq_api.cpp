@@ -1,6 +1,7 @@
 // C ABI of the K-quant GEMV library: argument validation, launch geometry and
 // the per-device scratch area.  Every step of the computation runs in the HIP
-// kernels of kq_gemv.hip / kq_repack.hip.
+// kernels of kq_gemv.h (instantiated per weight type in kq_gemv_q*.hip) and
+// kq_repack.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -72,6 +73,16 @@ static int device_state(int dev, DeviceState** out) {
   return KQ_OK;
 }
 
+static hipError_t launch_gemv(int type, int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid,
+                              size_t lds, hipStream_t s) {
+  switch (type) {
+    case KQ_Q4_K: return launch_gemv_type<KQ_Q4_K>(xtype, batch, nw, mf, a, grid, lds, s);
+    case KQ_Q5_K: return launch_gemv_type<KQ_Q5_K>(xtype, batch, nw, mf, a, grid, lds, s);
+    case KQ_Q6_K: return launch_gemv_type<KQ_Q6_K>(xtype, batch, nw, mf, a, grid, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Tuning knobs, read per call: target wavefronts per CU (KQ_WAVES_PER_CU, default
@@ -98,6 +109,16 @@ static int windows_from_batch() {
   const char* e = getenv("KQ_WINDOWS_FROM");
   const int x = e ? atoi(e) : 0;
   return (x >= 1 && x <= 9) ? x : 4;
+}
+
+// Batches (bf16 activations) from which the matrix cores compute the products
+// (KQ_MATRIX_CORES_FROM, 2..9; 9 = never, every batch on the dot2 VALU path).
+// The default, 3, is where the dot2 path becomes VALU-issue bound: at batch 2
+// it is as fast or faster on every sweep shape, from batch 3 on it is slower.
+static int matrix_cores_from() {
+  const char* e = getenv("KQ_MATRIX_CORES_FROM");
+  const int x = e ? atoi(e) : 0;
+  return (x >= 2 && x <= 9) ? x : 3;
 }
 
 static int wg_waves(int batch) {
@@ -153,11 +174,12 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   // 4-wavefront workgroups per CU, 112 KiB is for one 8-wavefront workgroup),
   // plus its wavefronts' partial sums.
   const int nw = wg_waves(batch);
+  const bool mf = xtype == KQ_X_BF16 && batch >= matrix_cores_from();
   const int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
   const int64_t target = (int64_t)st->cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
-  const int64_t per_col = (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, 1) - gemv_lds_bytes(type, xtype, batch, nw, 0));
+  const int64_t per_col = (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0));
   const int64_t max_cols = budget / per_col;
   if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
   if (upw > n_cols + 1) upw = n_cols + 1;   // a wavefront's run then touches at most two tiles
@@ -203,8 +225,8 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   a.tsb = (int32_t)tcols;
   a.partial = st->partial;
   a.counters = st->counters;
-  const size_t lds = gemv_lds_bytes(type, xtype, batch, nw, (int)tcols);
-  if (launch_gemv(type, xtype, batch, nw, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
+  const size_t lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols);
+  if (launch_gemv(type, xtype, batch, nw, mf, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;
 }

@@ -30,20 +30,17 @@
 // computation that needs the oldest buffer, unconditionally, and keeps global
 // stores out of the loop, so the compiler waits for exactly the unit it
 // consumes instead of for every load in flight.
+#pragma once
+
 #include "kq_common.h"
 #include "kq_internal.h"
 
 #ifndef KQ_DEPTH
 #define KQ_DEPTH 2
 #endif
-#ifndef KQ_MFMA_MIN_BATCH
-#define KQ_MFMA_MIN_BATCH 2
-#endif
 
 namespace kq {
 
-constexpr int kTilesPerWave = 2;   // a wavefront's run of units touches at most this many tiles
-constexpr int kMfmaMinBatch = KQ_MFMA_MIN_BATCH;  // bf16 batches from this size use the matrix cores
 
 // Buffer resource over unit (t, c): base = its first byte, size = one unit, or
 // size 0 when `live` is false, which turns every load through it into a
@@ -674,53 +671,47 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   }
 }
 
-template <int QT, int B, bool XF32>
-static hipError_t launch_one(const GemvArgs& a, int nw, int grid, size_t lds, hipStream_t s) {
-  constexpr bool kMf = !XF32 && B >= kMfmaMinBatch;
+template <int QT, int B, bool XF32, bool MF>
+static hipError_t launch_nw(const GemvArgs& a, int nw, int grid, size_t lds, hipStream_t s) {
   if (nw == 8)
-    hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, kMf, 8, KQ_DEPTH>), dim3(grid), dim3(512), lds, s, a);
+    hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, MF, 8, KQ_DEPTH>), dim3(grid), dim3(512), lds, s, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, kMf, 4, KQ_DEPTH>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, MF, 4, KQ_DEPTH>), dim3(grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
+// The matrix-core variant exists for bf16 activations and batch >= 2.
+template <int QT, int B, bool XF32>
+static hipError_t launch_one(const GemvArgs& a, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
+  if constexpr (!XF32 && B >= 2) {
+    if (mf) return launch_nw<QT, B, XF32, true>(a, nw, grid, lds, s);
+  }
+  if (mf) return hipErrorInvalidValue;
+  return launch_nw<QT, B, XF32, false>(a, nw, grid, lds, s);
+}
+
 template <int QT, bool XF32>
-static hipError_t launch_b(const GemvArgs& a, int batch, int nw, int grid, size_t lds, hipStream_t s) {
+static hipError_t launch_b(const GemvArgs& a, int batch, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
   switch (batch) {
-    case 1: return launch_one<QT, 1, XF32>(a, nw, grid, lds, s);
-    case 2: return launch_one<QT, 2, XF32>(a, nw, grid, lds, s);
-    case 3: return launch_one<QT, 3, XF32>(a, nw, grid, lds, s);
-    case 4: return launch_one<QT, 4, XF32>(a, nw, grid, lds, s);
-    case 5: return launch_one<QT, 5, XF32>(a, nw, grid, lds, s);
-    case 6: return launch_one<QT, 6, XF32>(a, nw, grid, lds, s);
-    case 7: return launch_one<QT, 7, XF32>(a, nw, grid, lds, s);
-    case 8: return launch_one<QT, 8, XF32>(a, nw, grid, lds, s);
+    case 1: return launch_one<QT, 1, XF32>(a, nw, mf, grid, lds, s);
+    case 2: return launch_one<QT, 2, XF32>(a, nw, mf, grid, lds, s);
+    case 3: return launch_one<QT, 3, XF32>(a, nw, mf, grid, lds, s);
+    case 4: return launch_one<QT, 4, XF32>(a, nw, mf, grid, lds, s);
+    case 5: return launch_one<QT, 5, XF32>(a, nw, mf, grid, lds, s);
+    case 6: return launch_one<QT, 6, XF32>(a, nw, mf, grid, lds, s);
+    case 7: return launch_one<QT, 7, XF32>(a, nw, mf, grid, lds, s);
+    case 8: return launch_one<QT, 8, XF32>(a, nw, mf, grid, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-bool gemv_uses_mfma(int xtype, int batch) { return xtype == KQ_X_BF16 && batch >= kMfmaMinBatch; }
-
-size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, int staged_cols) {
-  const size_t partials = (size_t)nw * kTilesPerWave * batch * kTileRows * sizeof(float);
-  const int sb = type == KQ_Q6_K ? 16 : 8;
-  if (gemv_uses_mfma(xtype, batch)) {
-    const int nb = (batch + 3) / 4;
-    return (size_t)staged_cols * (batch * 528 + sb * nb * 16) + 512 + partials;
-  }
-  const int xwords = xtype == KQ_X_F32 ? 256 : 128;
-  return (size_t)staged_cols * batch * 4 * (xwords + sb) + partials;
-}
-
-hipError_t launch_gemv(int type, int xtype, int batch, int nw, const GemvArgs& a, int grid, size_t lds,
-                       hipStream_t s) {
-  const bool f32 = xtype == KQ_X_F32;
-  switch (type) {
-    case KQ_Q4_K: return f32 ? launch_b<KQ_Q4_K, true>(a, batch, nw, grid, lds, s) : launch_b<KQ_Q4_K, false>(a, batch, nw, grid, lds, s);
-    case KQ_Q5_K: return f32 ? launch_b<KQ_Q5_K, true>(a, batch, nw, grid, lds, s) : launch_b<KQ_Q5_K, false>(a, batch, nw, grid, lds, s);
-    case KQ_Q6_K: return f32 ? launch_b<KQ_Q6_K, true>(a, batch, nw, grid, lds, s) : launch_b<KQ_Q6_K, false>(a, batch, nw, grid, lds, s);
-    default: return hipErrorInvalidValue;
-  }
+// Host entry for one weight type; each type is instantiated in its own
+// translation unit (kq_gemv_q4k.hip, ...), which keeps the build parallel.
+template <int QT>
+hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
+                            hipStream_t s) {
+  return xtype == KQ_X_F32 ? launch_b<QT, true>(a, batch, nw, mf, grid, lds, s)
+                           : launch_b<QT, false>(a, batch, nw, mf, grid, lds, s);
 }
 
 }  // namespace kq

@@ -8,6 +8,8 @@
 
 namespace kq {
 
+constexpr int kTilesPerWave = 2;   // a wavefront's run of units touches at most this many tiles
+
 // Kernel arguments of one GEMV launch (one or several projections sharing x).
 struct GemvArgs {
   const uint8_t* w[KQ_MAX_PROJ];       // repacked weights of each projection
@@ -31,14 +33,27 @@ struct GemvArgs {
   uint32_t* counters;                  // scratch: arrival counters per split tile, zero between calls
 };
 
-// Launch the GEMV with workgroups of `nw` (4 or 8) wavefronts.
-hipError_t launch_gemv(int type, int xtype, int batch, int nw, const GemvArgs& a, int grid, size_t lds,
-                       hipStream_t s);
-// Whether launch_gemv runs this activation type and batch on the matrix cores,
-// and the dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols`
-// columns needs.
-bool gemv_uses_mfma(int xtype, int batch);
-size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, int staged_cols);
+// Launch the GEMV of one weight type with workgroups of `nw` (4 or 8)
+// wavefronts, on the matrix cores (`mf`, bf16 activations and batch >= 2 only)
+// or on the dot2 VALU path.
+template <int QT>
+hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
+                            hipStream_t s);
+
+// The dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols` columns
+// needs on the chosen path: per column the activations of every batch row and
+// their sub-block sums (matrix cores: rows padded to 528 bytes, then a 512-byte
+// zero block), plus each wavefront's partial sums of up to two tiles.
+inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols) {
+  const size_t partials = (size_t)nw * kTilesPerWave * batch * 64 * sizeof(float);
+  const int sb = type == KQ_Q6_K ? 16 : 8;
+  if (mf) {
+    const int nb = (batch + 3) / 4;
+    return (size_t)staged_cols * (batch * 528 + sb * nb * 16) + 512 + partials;
+  }
+  const int xwords = xtype == KQ_X_F32 ? 256 : 128;
+  return (size_t)staged_cols * batch * 4 * (xwords + sb) + partials;
+}
 hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s);
 hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo,
                           hipStream_t s);

@@ -112,12 +112,14 @@ def _run_fields(qtype, f, rows, cols, x, where):
 
 
 @pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
-def test_zero_rows_are_exactly_zero(qtype, xdtype):
+@pytest.mark.parametrize("xdtype,batch,path", [("bf16", 2, "mfma"), ("bf16", 8, "mfma"), ("bf16", 2, "dot2"),
+                                               ("bf16", 8, "dot2"), ("f32", 2, "dot2")])
+def test_zero_rows_are_exactly_zero(qtype, xdtype, batch, path, monkeypatch):
     """Rows whose weights are all zero give exactly 0: zero super-blocks (d = dmin = 0),
-    zero quants with zero mins (Q4_K/Q5_K), all quants 32 (Q6_K)."""
+    zero quants with zero mins (Q4_K/Q5_K), all quants 32 (Q6_K); on the matrix-core and the dot2 path."""
+    monkeypatch.setenv("KQ_MATRIX_CORES_FROM", "2" if path == "mfma" else "9")
     rows, cols = 130, 768
-    say(f"case zero rows {qtype} {xdtype}")
+    say(f"case zero rows {qtype} {xdtype} B={batch} {path}")
     rng = np.random.default_rng(1)
     f = _fields(qtype, rows * 3, rng)
     sb = lambda r: slice(3 * r, 3 * r + 3)
@@ -132,7 +134,7 @@ def test_zero_rows_are_exactly_zero(qtype, xdtype):
         f["q"][sb(5)] = 32
         f["q"][sb(64)] = 32
         f["sc"][sb(129)] = 0
-    x = synth.gen_x(2, cols, 3, xdtype)
+    x = synth.gen_x(batch, cols, 3, xdtype)
     y, yo, ao = _run_fields(qtype, f, rows, cols, x, f"zero rows {qtype} {xdtype}")
     for r in zero_rows:
         assert np.all(ao[:, r] == 0) and np.all(y[:, r] == 0), f"row {r} not exactly zero"
@@ -204,6 +206,7 @@ def test_workgroup_sizes(qtype, batch, waves, monkeypatch):
     """Both workgroup shapes (4 and 8 wavefronts, KQ_WG_WAVES) on the matrix-core path, including
     batches that leave some of an instruction's four result registers unread (5, 6, 7)."""
     monkeypatch.setenv("KQ_WG_WAVES", waves)
+    monkeypatch.setenv("KQ_MATRIX_CORES_FROM", "2")
     run_case(qtype, 5 * 64 + 9, 7 * 256, batch, "bf16", 400 + batch, check_w=False)
 
 
@@ -216,3 +219,14 @@ def test_column_windows(qtype, batch, xdtype, windows_from, monkeypatch):
     if windows_from:
         monkeypatch.setenv("KQ_WINDOWS_FROM", windows_from)
     run_case(qtype, 5 * 64 + 9, 122 * 256, batch, xdtype, 500 + batch, check_w=False)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("batch", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("cols", [7 * 256, 122 * 256])
+def test_vector_path_bf16(qtype, batch, cols, monkeypatch):
+    """bf16 activations at batch >= 2 on the dot2 VALU path (KQ_MATRIX_CORES_FROM=9) instead of the
+    matrix cores, with even unit runs (7 columns) and with column windows (122 columns)."""
+    monkeypatch.setenv("KQ_MATRIX_CORES_FROM", "9")
+    run_case(qtype, 5 * 64 + 9, cols, batch, "bf16", 600 + batch, check_w=False)
+
