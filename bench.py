@@ -340,6 +340,36 @@ def summarize_counters(kfetch: str, kwrite: str, cfetch: str, cwrite: str) -> di
                 hbm_bytes_per_launch=round(fetch_b + write_b))
 
 
+def summarize_pmc(dirs: list) -> str:
+    """Per-dispatch means of every counter of the GEMV dispatches in rocprofv3 --pmc runs (one column per
+    run directory), plus the VALU issue floor: wavefront VALU instructions / (CUs x 1 per clock)."""
+    import csv
+    cols, names = [], set()
+    for d in dirs:
+        f = glob.glob(os.path.join(d, "*_counter_collection.csv"))[0]
+        per, kname = {}, ""
+        for r in csv.DictReader(open(f)):
+            if "kq::gemv_kernel" not in r["Kernel_Name"]:
+                continue
+            kname = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        by = {}
+        for (_, c), v in per.items():
+            by.setdefault(c, []).append(v)
+        cols.append((d, kname, {c: sum(v) / len(v) for c, v in by.items()}))
+        names |= set(by)
+    out = [f"{'counter':28s}" + "".join(f" {os.path.basename(d.rstrip('/')):>22s}" for d, _, _ in cols)]
+    out.append(f"{'kernel':28s}" + "".join(f" {k.replace('kq::gemv_kernel', 'gemv'):>22s}" for _, k, _ in cols))
+    for c in sorted(names):
+        out.append(f"{c:28s}" + "".join(f" {m.get(c, float('nan')):22.0f}" for _, _, m in cols))
+    cus = 256
+    for ghz in (2.1, 2.4):
+        out.append(f"{'VALU floor us @' + str(ghz) + ' GHz':28s}" +
+                   "".join(f" {m.get('SQ_INSTS_VALU', 0) / cus / (ghz * 1e3):22.2f}" for _, _, m in cols))
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,7 +385,12 @@ def main():
                     help="print a text summary of a rocprofv3 kernel-trace run of this benchmark")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("GEMV_FETCH", "GEMV_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="print the HBM-traffic JSON of the dominant kernel from four rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ROCPROF_DIR",
+                    help="print per-dispatch counter means of the GEMV dispatches of rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        sys.stdout.write(summarize_pmc(args.summarize_pmc))
+        return
     if args.summarize_trace:
         sys.path.insert(0, ROOT)
         sys.stdout.write(summarize_trace(*args.summarize_trace))

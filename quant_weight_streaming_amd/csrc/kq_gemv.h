@@ -3,13 +3,15 @@
 // Work decomposition.  A "unit" is one tile column: 64 rows (lane == row) x one
 // 256-weight super-block column, 9 / 11 / 13 KiB of weights read as coalesced
 // 1 KiB wavefront loads.  Units are ordered tile-major (all columns of tile 0,
-// then tile 1, ...); each wavefront takes a contiguous run of `upw` units and a
-// workgroup the runs of its 4 wavefronts, so the chip gets an even share per
-// wavefront whatever the matrix shape.  Per-tile sums go to LDS; after the
-// main loop the workgroup adds its wavefronts' pieces of each tile in
-// wavefront order, writes y for tiles it covered completely, and hands the
-// rest to the other workgroups sharing the tile (the last to arrive adds all
-// pieces in workgroup order).  Fixed summation orders make y deterministic.
+// then tile 1, ...).  By default each wavefront takes a contiguous run of `upw`
+// units and a workgroup the runs of its NW (4 or 8) wavefronts, so the chip
+// gets an even share per wavefront whatever the matrix shape; with column
+// windows a workgroup instead takes whole tiles of one window of columns.
+// Per-tile sums go to LDS; after the main loop the workgroup adds its
+// wavefronts' pieces of each tile in wavefront order, writes y for tiles it
+// covered completely, and hands the rest to the other workgroups sharing the
+// tile (the last to arrive adds all pieces in workgroup or window order).
+// Fixed summation orders make y deterministic.
 //
 // Per super-block and lane the 4/5/6-bit quants become bf16 pairs (128 + q)
 // with shift/and-or only, and v_dot2_f32_bf16 dots them with the activation
