@@ -75,6 +75,8 @@ extern "C" {
 #define KQ_ERR_HIP 6    /* a HIP runtime call or kernel launch failed */
 #define KQ_ERR_NOMEM 7  /* scratch allocation failed */
 #define KQ_ERR_RANGE 8  /* problem too large for 32-bit tile indexing */
+#define KQ_ERR_TIMEOUT 9 /* a chain step's wait for the previous step gave up (kq_chain_status) */
+#define KQ_ERR_DEVICE 10 /* a chain was run with another device current than the one it was made on */
 
 /* Version of this ABI (KQ_ABI_VERSION). */
 int kq_abi_version(void);
@@ -143,6 +145,66 @@ int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, in
  * out 4-byte aligned.  Used to check the repack and unpack bit-exactly.
  */
 int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
+
+/*
+ * Chains: a dependent sequence of GEMV steps in ONE persistent launch.
+ *
+ * Every token runs the decoder's projections one after the other, each reading
+ * what an earlier one produced, and its cost is the weight bytes streamed
+ * ("Muse-Glimmer-30B (text decoder) - Apple Core AI", decode table and the
+ * paragraph after it).  Launched one by one, each product pays a launch gap and
+ * fills and drains the GPU on its own.  A chain runs all steps in one launch:
+ * step j+1 issues its first weight loads while step j drains, and reads its
+ * activations only after every output of step j has been written.  So x of step
+ * j+1 may be y of step j (or of any earlier step): fp32 activations, with ldx
+ * = ldy.  The results are those of the same kq_gemv_multi calls made in order
+ * (bitwise: each step runs the same arithmetic in the same order).
+ *
+ * kq_chain_step describes one step exactly as kq_gemv_multi takes it (n = 1 for
+ * a single matrix).  All steps share xtype and batch.
+ */
+typedef struct kq_chain_step {
+  int32_t type;                   /* KQ_Q4_K / KQ_Q5_K / KQ_Q6_K */
+  int32_t n;                      /* row segments sharing x, 1..KQ_MAX_PROJ */
+  int64_t cols;                   /* K, a positive multiple of 256 */
+  const void *w[KQ_MAX_PROJ];     /* device, repacked weights of each segment */
+  int64_t rows[KQ_MAX_PROJ];      /* rows of each segment */
+  float *y[KQ_MAX_PROJ];          /* device, fp32 outputs */
+  int64_t ldy[KQ_MAX_PROJ];       /* output row strides (elements), >= rows */
+  const void *x;                  /* device activations, batch rows of stride ldx */
+  int64_t ldx;                    /* activation row stride (elements), >= cols */
+} kq_chain_step;
+
+typedef struct kq_chain kq_chain;
+
+/*
+ * Plan a chain of n_steps (1..65536) steps on the current device: validates
+ * every step as kq_gemv_multi would, sizes the persistent grid from the
+ * kernel's occupancy, and allocates the chain's device memory (partial sums,
+ * 16.1 MB, plus about 2.4 KB per step for the step table and the step
+ * barrier's words).  Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
+ * Every x must also satisfy ((batch-1)*ldx + cols) * element size < 2^31.
+ * On success *out owns the plan; release it with kq_chain_destroy.
+ */
+int kq_chain_create(int n_steps, const kq_chain_step *steps, int xtype, int batch, kq_chain **out);
+
+/*
+ * Enqueue one run of the chain on `stream` (one kernel launch, no allocation;
+ * may be captured in a HIP graph).  Runs of one chain must not overlap in time
+ * (they share its control words); different chains are independent.  The
+ * device current at the call must be the chain's (else KQ_ERR_DEVICE).
+ */
+int kq_chain_run(kq_chain *c, void *stream);
+
+/*
+ * Synchronous: waits for the device, then returns KQ_ERR_TIMEOUT if a step's
+ * wait in any run since the last call gave up (its results are then invalid;
+ * a wait gives up after about a second), else KQ_OK; clears the flag.
+ */
+int kq_chain_status(kq_chain *c);
+
+/* Free the chain's device memory (synchronous). NULL is accepted. */
+int kq_chain_destroy(kq_chain *c);
 
 #ifdef __cplusplus
 }

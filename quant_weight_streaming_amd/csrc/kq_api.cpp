@@ -7,6 +7,8 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <new>
+#include <vector>
 
 #include "../../include/kq.h"
 #include "kq_internal.h"
@@ -128,8 +130,9 @@ static int wg_waves(int batch) {
   return batch >= kWideBatch ? 8 : 4;
 }
 
-static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
-                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream) {
+// Argument checks shared by every GEMV entry point and every chain step.
+static int validate(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                    int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy) {
   if (type != KQ_Q4_K && type != KQ_Q5_K && type != KQ_Q6_K) return KQ_ERR_TYPE;
   if (xtype != KQ_X_F32 && xtype != KQ_X_BF16) return KQ_ERR_TYPE;
   if (batch < 1 || batch > KQ_MAX_BATCH || n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
@@ -143,7 +146,23 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   if (!aligned(x, 16) || (ldx * esize) % 16 != 0) return KQ_ERR_ALIGN;
   for (int i = 0; i < n; ++i)
     if (!aligned(w[i], 16) || !aligned(y[i], 4)) return KQ_ERR_ALIGN;
+  return KQ_OK;
+}
 
+// Launch plan of one GEMV (or multi-projection) call.
+struct Plan {
+  GemvArgs a;
+  int nw;        // wavefronts per workgroup
+  bool mf;       // matrix-core path
+  int64_t grid;  // workgroups, a multiple of 8
+  size_t lds;    // dynamic LDS per workgroup
+};
+
+// Launch geometry of a validated call on a device with `cus` CUs, using at most
+// `max_grid` workgroups (a multiple of 8).
+static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
+                     int64_t max_grid, float* partial, uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
   GemvArgs a{};
   int64_t tiles = 0;
@@ -160,33 +179,29 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   for (int i = n; i <= KQ_MAX_PROJ; ++i) a.tile_begin[i] = (int32_t)tiles;
   const int64_t n_units = tiles * n_cols;
   if (n_units + 2 * n_cols + 8 * (int64_t)kMaxGroups >= INT32_MAX) return KQ_ERR_RANGE;
+  const int64_t max_groups = max_grid < kMaxGroups ? max_grid : kMaxGroups;
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
-  DeviceState* st = nullptr;
-  int rc = device_state(dev, &st);
-  if (rc != KQ_OK) return rc;
-
-  // Launch geometry: an even run of `upw` units per wavefront, about
-  // waves_per_cu() wavefronts per CU, nw wavefronts per workgroup.  A
-  // workgroup stages the activations (and sub-block sums) of the columns its
-  // nw*upw units touch in LDS, within `budget` bytes (64 KiB leaves room for two
-  // 4-wavefront workgroups per CU, 112 KiB is for one 8-wavefront workgroup),
-  // plus its wavefronts' partial sums.
+  // An even run of `upw` units per wavefront, about waves_per_cu() wavefronts
+  // per CU, nw wavefronts per workgroup.  A workgroup stages the activations
+  // (and sub-block sums) of the columns its nw*upw units touch in LDS, within
+  // `budget` bytes (64 KiB leaves room for two 4-wavefront workgroups per CU,
+  // 112 KiB is for one 8-wavefront workgroup), plus its wavefronts' partial sums.
   const int nw = wg_waves(batch);
   const bool mf = xtype == KQ_X_BF16 && batch >= matrix_cores_from();
   const int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
-  const int64_t target = (int64_t)st->cus * waves_per_cu();
+  const int64_t target = (int64_t)cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
-  const int64_t per_col = (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0));
+  const int64_t per_col =
+      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0));
   const int64_t max_cols = budget / per_col;
   if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
   if (upw > n_cols + 1) upw = n_cols + 1;   // a wavefront's run then touches at most two tiles
   int64_t n_groups = (n_units + nw * upw - 1) / (nw * upw);
-  if (n_groups > kMaxGroups) {
-    upw = (n_units + nw * (int64_t)kMaxGroups - 1) / (nw * (int64_t)kMaxGroups);
-    if ((n_cols > max_cols && nw * upw > max_cols) || upw > n_cols + 1) return KQ_ERR_RANGE;
+  bool even_ok = true;   // even runs fit the staging budget within max_groups workgroups
+  if ((n_groups + 7) / 8 * 8 > max_groups) {
+    upw = (n_units + nw * (max_groups / 8 * 8) - 1) / (nw * (max_groups / 8 * 8));
+    even_ok = !((n_cols > max_cols && nw * upw > max_cols) || upw > n_cols + 1);
     n_groups = (n_units + nw * upw - 1) / (nw * upw);
   }
   int64_t tcols = n_cols < nw * upw ? n_cols : nw * upw;
@@ -203,19 +218,25 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   const int forced_r = aligned_tiles();
   if (((batch >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
       n_win * tiles <= 2 * (int64_t)kMaxGroups) {
-    const int64_t g_target = (int64_t)st->cus * waves_per_cu() / nw;
+    int64_t g_target = (int64_t)cus * waves_per_cu() / nw;
+    if (g_target > max_groups) g_target = max_groups;
     int64_t g_win = g_target / n_win > 0 ? g_target / n_win : 1;
     int64_t r = forced_r > 0 ? forced_r : (tiles + g_win - 1) / g_win;
     if (r > nw) r = nw;                      // a wavefront's run then touches at most two tiles
     g_win = (tiles + r - 1) / r;
-    a.n_win = (int32_t)n_win;
-    a.win_base = (int32_t)(n_cols / n_win);
-    a.win_extra = (int32_t)(n_cols % n_win);
-    a.wg_per_win = (int32_t)g_win;
-    a.tiles_per_wg = (int32_t)r;
-    tcols = a.win_base + (a.win_extra ? 1 : 0);
-    grid = (n_win * g_win + 7) / 8 * 8;
+    const int64_t wgrid = (n_win * g_win + 7) / 8 * 8;
+    if (wgrid <= max_groups) {
+      even_ok = true;
+      a.n_win = (int32_t)n_win;
+      a.win_base = (int32_t)(n_cols / n_win);
+      a.win_extra = (int32_t)(n_cols % n_win);
+      a.wg_per_win = (int32_t)g_win;
+      a.tiles_per_wg = (int32_t)r;
+      tcols = a.win_base + (a.win_extra ? 1 : 0);
+      grid = wgrid;
+    }
   }
+  if (!even_ok) return KQ_ERR_RANGE;
   a.nproj = n;
   a.n_cols = (int32_t)n_cols;
   a.x = x;
@@ -223,15 +244,73 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   a.n_units = (int32_t)n_units;
   a.upw = (int32_t)upw;
   a.tsb = (int32_t)tcols;
-  a.partial = st->partial;
-  a.counters = st->counters;
-  const size_t lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols);
-  if (launch_gemv(type, xtype, batch, nw, mf, a, (int)grid, lds, static_cast<hipStream_t>(stream)) != hipSuccess)
+  a.partial = partial;
+  a.counters = counters;
+  out->a = a;
+  out->nw = nw;
+  out->mf = mf;
+  out->grid = grid;
+  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols);
+  return KQ_OK;
+}
+
+static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream) {
+  int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
+  if (rc != KQ_OK) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  DeviceState* st = nullptr;
+  rc = device_state(dev, &st);
+  if (rc != KQ_OK) return rc;
+  Plan p;
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, st->partial,
+                 st->counters, &p);
+  if (rc != KQ_OK) return rc;
+  if (launch_gemv(type, xtype, batch, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;
 }
 
+// ---------------------------------------------------------------- chains
+
+static hipError_t launch_chain(int xtype, int batch, const ChainArgs& c, int nw, bool mf, int grid, size_t lds,
+                               hipStream_t s, int* occupancy) {
+  const bool f32 = xtype == KQ_X_F32;
+  switch (batch) {
+#define KQ_CHAIN_CASE(B) \
+  case B: return f32 ? launch_chain_b<B, true>(c, nw, mf, grid, lds, s, occupancy) \
+                     : launch_chain_b<B, false>(c, nw, mf, grid, lds, s, occupancy);
+    KQ_CHAIN_CASE(1) KQ_CHAIN_CASE(2) KQ_CHAIN_CASE(3) KQ_CHAIN_CASE(4)
+    KQ_CHAIN_CASE(5) KQ_CHAIN_CASE(6) KQ_CHAIN_CASE(7) KQ_CHAIN_CASE(8)
+#undef KQ_CHAIN_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Polls before a chain step's wait gives up (KQ_CHAIN_SPIN overrides; about a
+// second at the default).
+static uint32_t chain_spin() {
+  const char* e = getenv("KQ_CHAIN_SPIN");
+  if (e) {
+    const long v = atol(e);
+    if (v >= 0 && v <= 0x7fffffffL) return (uint32_t)v;
+  }
+  return 1u << 20;
+}
+
 }  // namespace kq
+
+struct kq_chain {
+  int dev = 0;
+  int xtype = 0, batch = 0, nw = 4;
+  bool mf = false;
+  int grid = 0;
+  size_t lds = 0;
+  kq::ChainArgs args{};
+  void* mem = nullptr;   // one allocation: step table, control words, partial sums, tile counters
+};
 
 using namespace kq;
 
@@ -250,6 +329,8 @@ const char* kq_status_str(int status) {
     case KQ_ERR_HIP: return "HIP runtime error";
     case KQ_ERR_NOMEM: return "device allocation failed";
     case KQ_ERR_RANGE: return "problem too large";
+    case KQ_ERR_TIMEOUT: return "a chain step's wait for the previous step gave up";
+    case KQ_ERR_DEVICE: return "chain run on another device than the one it was made on";
     default: return "unknown status";
   }
 }
@@ -305,6 +386,148 @@ int kq_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, 
   if (launch_dequant(type, w, rows, cols, out, ldo, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;
+}
+
+static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batch, kq_chain** out) {
+  if (!out) return KQ_ERR_NULL;
+  *out = nullptr;
+  if (n_steps < 1 || n_steps > (1 << 16)) return KQ_ERR_BATCH;
+  if (!steps) return KQ_ERR_NULL;
+  if (xtype != KQ_X_F32 && xtype != KQ_X_BF16) return KQ_ERR_TYPE;
+  if (batch < 1 || batch > KQ_MAX_BATCH) return KQ_ERR_BATCH;
+  const int64_t esize = xtype == KQ_X_F32 ? 4 : 2;
+  for (int j = 0; j < n_steps; ++j) {
+    const kq_chain_step& st = steps[j];
+    const int rc = validate(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy);
+    if (rc != KQ_OK) return rc;
+    if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return KQ_ERR_HIP;
+
+  // Persistent grid: the designed workgroups per CU (two of 4 wavefronts, one
+  // of 8), fewer if the occupancy of the chain kernel says so.
+  kq_chain* c = new (std::nothrow) kq_chain;
+  if (!c) return KQ_ERR_NOMEM;
+  std::vector<Plan> plans(n_steps);
+  auto plan_all = [&](int64_t max_grid, size_t* lds) {
+    *lds = 0;
+    for (int j = 0; j < n_steps; ++j) {
+      const kq_chain_step& st = steps[j];
+      const int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
+                               max_grid, nullptr, nullptr, &plans[j]);
+      if (rc != KQ_OK) return rc;
+      if (plans[j].lds > *lds) *lds = plans[j].lds;
+    }
+    return (int)KQ_OK;
+  };
+  const int nw = wg_waves(batch);
+  int64_t groups = (int64_t)cus * (8 / nw);
+  size_t lds = 0;
+  int rc = plan_all(groups, &lds);
+  int occ = 0;
+  if (rc == KQ_OK &&
+      launch_chain(xtype, batch, ChainArgs{}, nw, plans[0].mf, 0, lds, nullptr, &occ) != hipSuccess)
+    rc = KQ_ERR_HIP;
+  if (rc == KQ_OK && occ < 1) rc = KQ_ERR_RANGE;
+  if (rc == KQ_OK && (int64_t)occ * cus < groups) {
+    groups = (int64_t)occ * cus / 8 * 8;
+    if (groups < 8) rc = KQ_ERR_RANGE;
+    else rc = plan_all(groups, &lds);
+  }
+  if (rc != KQ_OK) {
+    delete c;
+    return rc;
+  }
+
+  const size_t steps_bytes = round_up((size_t)n_steps * sizeof(ChainStep), 256);
+  // control words: arrive[n_steps][groups], done[n_steps], epoch, error
+  const size_t ctl_bytes = round_up(((size_t)n_steps * (groups + 1) + 2) * sizeof(uint32_t), 256);
+  const size_t total = steps_bytes + ctl_bytes + kPartialBytes + kCounterBytes;
+  if (hipMalloc(&c->mem, total) != hipSuccess) {
+    delete c;
+    return KQ_ERR_NOMEM;
+  }
+  uint8_t* base = static_cast<uint8_t*>(c->mem);
+  ChainStep* d_steps = reinterpret_cast<ChainStep*>(base);
+  uint32_t* d_ctl = reinterpret_cast<uint32_t*>(base + steps_bytes);
+  float* d_partial = reinterpret_cast<float*>(base + steps_bytes + ctl_bytes);
+  uint32_t* d_counters = reinterpret_cast<uint32_t*>(base + steps_bytes + ctl_bytes + kPartialBytes);
+  std::vector<ChainStep> h(n_steps);
+  for (int j = 0; j < n_steps; ++j) {
+    h[j].a = plans[j].a;
+    h[j].a.partial = d_partial;
+    h[j].a.counters = d_counters;
+    h[j].type = steps[j].type;
+    h[j].grid = (int32_t)plans[j].grid;
+  }
+  rc = KQ_OK;
+  if (hipMemcpy(d_steps, h.data(), (size_t)n_steps * sizeof(ChainStep), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_counters, 0, kCounterBytes) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    rc = KQ_ERR_HIP;
+  if (rc != KQ_OK) {
+    (void)hipFree(c->mem);
+    delete c;
+    return rc;
+  }
+  c->dev = dev;
+  c->xtype = xtype;
+  c->batch = batch;
+  c->nw = nw;
+  c->mf = plans[0].mf;
+  c->grid = (int)groups;
+  c->lds = lds;
+  c->args.steps = d_steps;
+  c->args.n_steps = n_steps;
+  uint32_t* d_done = d_ctl + (size_t)n_steps * groups;
+  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_steps, d_done + n_steps + 1, (uint32_t)groups, chain_spin()};
+  *out = c;
+  return KQ_OK;
+}
+
+int kq_chain_run(kq_chain* c, void* stream) {
+  if (!c) return KQ_ERR_NULL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  if (dev != c->dev) return KQ_ERR_DEVICE;
+  if (launch_chain(c->xtype, c->batch, c->args, c->nw, c->mf, c->grid, c->lds, static_cast<hipStream_t>(stream),
+                   nullptr) != hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+int kq_chain_status(kq_chain* c) {
+  if (!c) return KQ_ERR_NULL;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(c->dev) != hipSuccess) return KQ_ERR_HIP;
+  uint32_t err = 0;
+  int rc = KQ_OK;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(&err, c->args.ctl.error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
+    rc = KQ_ERR_HIP;
+  if (rc == KQ_OK && err) {
+    rc = hipMemset(c->args.ctl.error, 0, sizeof(err)) == hipSuccess && hipDeviceSynchronize() == hipSuccess
+             ? KQ_ERR_TIMEOUT
+             : KQ_ERR_HIP;
+  }
+  (void)hipSetDevice(prev);
+  return rc;
+}
+
+int kq_chain_destroy(kq_chain* c) {
+  if (!c) return KQ_OK;
+  int prev = 0, rc = KQ_OK;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(c->dev) != hipSuccess) rc = KQ_ERR_HIP;
+  if (rc == KQ_OK && (hipDeviceSynchronize() != hipSuccess || hipFree(c->mem) != hipSuccess)) rc = KQ_ERR_HIP;
+  (void)hipSetDevice(prev);
+  delete c;
+  return rc;
 }
 
 }  // extern "C"

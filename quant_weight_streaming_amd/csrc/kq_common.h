@@ -46,6 +46,8 @@ constexpr int kPartialStride = KQ_MAX_BATCH * kTileRows;  // floats per partial-
 constexpr int kBufferFlags = 0x00020000;
 // Cache-policy operand of buffer loads: nontemporal (the weights are read once).
 constexpr int kCacheNT = 2;
+// buffer-load cache policy: sc1, read through the device coherence point
+constexpr int kCacheCoherent = 16;
 
 template <int QT> struct Fmt;
 template <> struct Fmt<KQ_Q4_K> {

@@ -47,8 +47,8 @@ namespace kq {
 // Buffer resource over unit (t, c): base = its first byte, size = one unit, or
 // size 0 when `live` is false, which turns every load through it into a
 // zero-filled no-op that moves no data (loads past the wavefront's last unit).
-template <int QT>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const GemvArgs& a, int t, int c, bool live) {
+template <int QT, class GA>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(GA& a, int t, int c, bool live) {
   int p = 0;
 #pragma unroll
   for (int i = 1; i < KQ_MAX_PROJ; ++i)
@@ -93,7 +93,10 @@ struct XStage {
 
   __device__ __forceinline__ static int rounds(int len) { return (len * B * SB + IPT * NT - 1) / (IPT * NT); }
 
-  __device__ __forceinline__ void load(const GemvArgs& a, int c0, int len, int r) {
+  // COH: read through the device coherence point (the activations may have been
+  // written by another XCD earlier in the same launch).
+  template <bool COH, class GA>
+  __device__ __forceinline__ void load(GA& a, int c0, int len, int r) {
     const int n = len * B * SB;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
@@ -102,10 +105,18 @@ struct XStage {
         const int g = i % SB, q = i / SB, b = q % B, ic = q / B;
         int c = c0 + ic;
         if (c >= a.n_cols) c -= a.n_cols;
-        const uint8_t* xp = static_cast<const uint8_t*>(a.x) +
-                            ((int64_t)b * a.ldx + (int64_t)c * 256 + g * F::kSubW) * ES;
+        const int64_t off = ((int64_t)b * a.ldx + (int64_t)c * 256 + g * F::kSubW) * ES;
+        if constexpr (COH) {
+          const __amdgpu_buffer_rsrc_t xr =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, 0x7fffffff, kBufferFlags);
 #pragma unroll
-        for (int e = 0; e < VPI; ++e) v[j][e] = reinterpret_cast<const u32x4*>(xp)[e];
+          for (int e = 0; e < VPI; ++e)
+            v[j][e] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off + 16 * e, 0, kCacheCoherent);
+        } else {
+          const uint8_t* xp = static_cast<const uint8_t*>(a.x) + off;
+#pragma unroll
+          for (int e = 0; e < VPI; ++e) v[j][e] = reinterpret_cast<const u32x4*>(xp)[e];
+        }
       }
     }
   }
@@ -410,9 +421,10 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
   }
 }
 
-// Write finished row sums of tile t (all of its columns) to y.
-template <int B>
-__device__ __forceinline__ void write_tile(const GemvArgs& a, int t, int lane, const float* v) {
+// Write finished row sums of tile t (all of its columns) to y; COH: write
+// through to the device coherence point (read later in the same launch).
+template <int B, bool COH, class GA>
+__device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* v) {
   int p = 0;
 #pragma unroll
   for (int i = 1; i < KQ_MAX_PROJ; ++i)
@@ -422,7 +434,10 @@ __device__ __forceinline__ void write_tile(const GemvArgs& a, int t, int lane, c
     float* y = a.y[p];
     const int64_t ldy = a.ldy[p];
 #pragma unroll
-    for (int b = 0; b < B; ++b) y[b * ldy + row] = v[b];
+    for (int b = 0; b < B; ++b) {
+      if constexpr (COH) __hip_atomic_store(y + b * ldy + row, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else y[b * ldy + row] = v[b];
+    }
   }
 }
 
@@ -433,8 +448,8 @@ __device__ __forceinline__ void write_tile(const GemvArgs& a, int t, int lane, c
 // wavefront waits until they are acknowledged before bumping the tile's
 // counter, and the last arrival reads them with agent-scope atomic loads, which
 // bypass the per-XCD caches.  The counter is reset for the next call.
-template <int B>
-__device__ __forceinline__ void hand_off(const GemvArgs& a, int t, int L, int wgu, int lane, const float* v) {
+template <int B, bool COH, class GA>
+__device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane, const float* v) {
   const int n_cols = a.n_cols;
   const int slot = (t == (L * wgu) / n_cols) ? 0 : 1;
   float* mine = a.partial + (int64_t)(L * 2 + slot) * kPartialStride;
@@ -471,15 +486,15 @@ __device__ __forceinline__ void hand_off(const GemvArgs& a, int t, int L, int wg
       for (int b = 0; b < B; ++b)
         if (l0 + j <= lb) s[b] += v[j][b];
   }
-  write_tile<B>(a, t, lane, s);
+  write_tile<B, COH>(a, t, lane, s);
   if (lane == 0) __hip_atomic_store(&a.counters[la], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Windowed variant: the workgroup of window w holds tile t's sum over that
 // window's columns.  Every window contributes one piece per tile; the last to
 // arrive adds them in window order.  Same publication protocol as hand_off.
-template <int B>
-__device__ __forceinline__ void hand_off_windows(const GemvArgs& a, int t, int w, int lane, const float* v) {
+template <int B, bool COH, class GA>
+__device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, const float* v) {
   float* mine = a.partial + (int64_t)(w * a.n_tiles + t) * kPartialStride;
 #pragma unroll
   for (int b = 0; b < B; ++b)
@@ -510,12 +525,65 @@ __device__ __forceinline__ void hand_off_windows(const GemvArgs& a, int t, int w
       for (int b = 0; b < B; ++b)
         if (w0 + j < a.n_win) s[b] += q[j][b];
   }
-  write_tile<B>(a, t, lane, s);
+  write_tile<B, COH>(a, t, lane, s);
   if (lane == 0) __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH>
-__global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
+// Step barrier of a chain.  Workgroup g arrives at step j by storing the run's
+// tag in arrive[j][g]; workgroup 0 (the collector) polls the arrivals of the
+// step and then stores the tag in done[j]; the others poll done[j].  Plain
+// stores and loads through the device coherence point: no read-modify-write on
+// a shared word (hundreds of them on one address serialise at the memory).
+// Every poll loop is bounded by `spin`; one that gives up sets the error word.
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void chain_collect(const ChainCtl& c, int step, uint32_t tag) {
+  const uint32_t* arr = c.arrive + (size_t)step * c.groups;
+  uint32_t n = 0;
+  int all;
+  for (;;) {
+    int mine = 1;
+    for (uint32_t g = threadIdx.x; g < c.groups; g += blockDim.x) mine &= load_coherent(arr + g) == tag;
+    all = __syncthreads_and(mine);
+    if (all || ++n > c.spin) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (threadIdx.x == 0) {
+    if (!all) store_coherent(c.error, 1u);
+    store_coherent(c.done + step, tag);
+  }
+}
+
+// Wait before reading step `step`'s activations until every workgroup has
+// finished step - 1.
+__device__ __forceinline__ void chain_wait(const ChainCtl& c, int step, uint32_t tag) {
+  if (step == 0) return;
+  if (blockIdx.x == 0) {
+    chain_collect(c, step - 1, tag);
+  } else if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (load_coherent(c.done + step - 1) != tag) {
+      if (++n > c.spin) {
+        store_coherent(c.error, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup's share (logical block `lblock`) of one GEMV launch.  CHAIN:
+// the call is a step of a chain (chain_kernel): the weight prologue goes out
+// before the wait for the previous step, and the activations are read, and y
+// written, through the device coherence point.
+template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH, bool CHAIN, class GA>
+__device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ctl, int step, uint32_t tag) {
   using F = Fmt<QT>;
   constexpr int NCH = F::kChunks, SB = F::kSubBlocks;
   constexpr int XW = XF32 ? 256 : 128;
@@ -523,10 +591,6 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   // readfirstlane: the wavefront index is uniform across the wavefront; saying so
   // keeps all unit/column bookkeeping in SGPRs.
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Blocks are dispatched round-robin over the 8 XCDs; consecutive logical
-  // blocks (which share split tiles) go to one XCD.
-  const int nb8 = gridDim.x >> 3;
-  const int lblock = (blockIdx.x & 7) * nb8 + (blockIdx.x >> 3);
   const int n_cols = a.n_cols;
   // The workgroup's columns [cs, cs + cw) and its run of units [U0, U1),
   // numbered tile-major inside those columns (unit u: tile u / cw, column
@@ -537,7 +601,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   if (a.tiles_per_wg > 0) {
     w = lblock / a.wg_per_win;
     const int t_first = (lblock - w * a.wg_per_win) * a.tiles_per_wg;
-    if (w >= a.n_win || t_first >= a.n_tiles) return;   // whole workgroup idle
+    if (w >= a.n_win || t_first >= a.n_tiles) return false;   // whole workgroup idle
     cs = w * a.win_base + min(w, a.win_extra);
     cw = a.win_base + (w < a.win_extra ? 1 : 0);
     U0 = t_first * cw;
@@ -546,7 +610,7 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   } else {
     upw = a.upw;
     U0 = lblock * NW * upw;
-    if (U0 >= a.n_units) return;                     // whole workgroup idle
+    if (U0 >= a.n_units) return false;               // whole workgroup idle
     U1 = min(U0 + NW * upw, a.n_units);
   }
   const int c0w = cs + U0 % cw;                    // staged columns c0w, c0w+1, ... (mod n_cols)
@@ -583,15 +647,22 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
   // first round of activation loads, then the weight prologue, then the stores
   constexpr int kRS = MF ? MfmaLds<QT, B>::kXRow : 256 * (XF32 ? 4 : 2);
   XStage<QT, B, XF32, NW, kRS> xs;
-  xs.load(a, c0w, len, 0);
+  if constexpr (CHAIN) {
 #pragma unroll
-  for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
+    for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
+    chain_wait(*ctl, step, tag);
+    xs.template load<true>(a, c0w, len, 0);
+  } else {
+    xs.template load<false>(a, c0w, len, 0);
+#pragma unroll
+    for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
+  }
   {
     uint8_t* Xb = reinterpret_cast<uint8_t*>(lds_words);
     xs.template store<!MF>(Xb, T, len, 0);
     const int nr = XStage<QT, B, XF32, NW, kRS>::rounds(len);
     for (int r = 1; r < nr; ++r) {
-      xs.load(a, c0w, len, r);
+      xs.template load<CHAIN>(a, c0w, len, r);
       xs.template store<!MF>(Xb, T, len, r);
     }
     if constexpr (MF) {
@@ -667,10 +738,65 @@ __global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
 #pragma unroll
       for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
     }
-    if (a.n_win > 1) hand_off_windows<B>(a, t, w, lane, s);
-    else if (ts >= U0 && te <= U1) write_tile<B>(a, t, lane, s);   // every tile when tiles_per_wg > 0
-    else hand_off<B>(a, t, lblock, NW * upw, lane, s);
+    if (a.n_win > 1) hand_off_windows<B, CHAIN>(a, t, w, lane, s);
+    else if (ts >= U0 && te <= U1) write_tile<B, CHAIN>(a, t, lane, s);   // every tile when tiles_per_wg > 0
+    else hand_off<B, CHAIN>(a, t, lblock, NW * upw, lane, s);
   }
+  return true;
+}
+
+// ---------------------------------------------------------------- chains
+//
+// A chain is a sequence of GEMV steps where step j+1 may read, as its
+// activations, what step j wrote (the decoder's projections, one after the
+// other).  One persistent launch runs them all: every workgroup of the grid (all
+// resident at once: the grid is sized from the occupancy) takes its share of
+// step 0, then of step 1, and so on.  Before reading a step's activations a
+// workgroup waits at the step barrier (chain_wait) for every workgroup to have
+// finished the previous step; the weight prologue of the step goes out before
+// that wait, so the weights stream in while the previous step drains, and
+// there is no launch gap between steps.  A workgroup arrives at step j (idle or
+// not) once its stores of the step are complete.  The barrier words carry the
+// run's tag (one more than the last completed run's, kept in `epoch`), so they
+// need no reset between runs; workgroup 0 bumps the epoch once every workgroup
+// has arrived at the last step.
+
+// The step table is read through the constant address space: it is not written
+// during the launch, so its fields load into SGPRs with scalar loads and stay
+// valid across the weight loop's compiler barriers.
+typedef const __attribute__((address_space(4))) ChainStep ConstChainStep;
+
+template <int B, bool XF32, bool MF, int NW>
+__global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
+  ConstChainStep* steps = (ConstChainStep*)(c.steps);
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(load_coherent(c.ctl.epoch)) + 1u;
+  for (int j = 0; j < c.n_steps; ++j) {
+    ConstChainStep& st = steps[j];
+    const int g = st.grid;
+    bool waited = false;
+    if ((int)blockIdx.x < g) {
+      const int lblock = (blockIdx.x & 7) * (g >> 3) + (blockIdx.x >> 3);
+      if (st.type == KQ_Q4_K) waited = gemv_block<KQ_Q4_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag);
+      else if (st.type == KQ_Q5_K) waited = gemv_block<KQ_Q5_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag);
+      else waited = gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag);
+    }
+    if (blockIdx.x == 0 && j > 0 && !waited) chain_collect(c.ctl, j - 1, tag);   // the collector never skips a step
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's y / partial stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent(c.ctl.arrive + (size_t)j * c.ctl.groups + blockIdx.x, tag);
+  }
+  if (blockIdx.x == 0) {
+    chain_collect(c.ctl, c.n_steps - 1, tag);
+    if (threadIdx.x == 0) store_coherent(c.ctl.epoch, tag);
+  }
+}
+
+template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH>
+__global__ void __launch_bounds__(64 * NW) gemv_kernel(const GemvArgs a) {
+  // Blocks are dispatched round-robin over the 8 XCDs; consecutive logical
+  // blocks (which share split tiles) go to one XCD.
+  const int nb8 = gridDim.x >> 3;
+  gemv_block<QT, B, XF32, MF, NW, DEPTH, false>(a, (blockIdx.x & 7) * nb8 + (blockIdx.x >> 3), nullptr, 0, 0u);
 }
 
 template <int QT, int B, bool XF32, bool MF>
@@ -705,6 +831,27 @@ static hipError_t launch_b(const GemvArgs& a, int batch, int nw, bool mf, int gr
     case 8: return launch_one<QT, 8, XF32>(a, nw, mf, grid, lds, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int B, bool XF32, bool MF>
+static hipError_t launch_chain_nw(const ChainArgs& c, int nw, int grid, size_t lds, hipStream_t s, int* occupancy) {
+  const void* k = nw == 8 ? reinterpret_cast<const void*>(&chain_kernel<B, XF32, MF, 8>)
+                          : reinterpret_cast<const void*>(&chain_kernel<B, XF32, MF, 4>);
+  if (occupancy) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, k, 64 * nw, lds);
+  if (nw == 8) hipLaunchKernelGGL((chain_kernel<B, XF32, MF, 8>), dim3(grid), dim3(512), lds, s, c);
+  else hipLaunchKernelGGL((chain_kernel<B, XF32, MF, 4>), dim3(grid), dim3(256), lds, s, c);
+  return hipGetLastError();
+}
+
+// Chain launch (or, with `occupancy`, the number of its workgroups one CU
+// holds) for one batch size and activation type.
+template <int B, bool XF32>
+hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t lds, hipStream_t s, int* occupancy) {
+  if constexpr (!XF32 && B >= 2) {
+    if (mf) return launch_chain_nw<B, XF32, true>(c, nw, grid, lds, s, occupancy);
+  }
+  if (mf) return hipErrorInvalidValue;
+  return launch_chain_nw<B, XF32, false>(c, nw, grid, lds, s, occupancy);
 }
 
 // Host entry for one weight type; each type is instantiated in its own

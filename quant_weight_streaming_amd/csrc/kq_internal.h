@@ -36,6 +36,33 @@ struct GemvArgs {
 // Launch the GEMV of one weight type with workgroups of `nw` (4 or 8)
 // wavefronts, on the matrix cores (`mf`, bf16 activations and batch >= 2 only)
 // or on the dot2 VALU path.
+// Control words of a chain launch (device memory owned by the chain).
+struct ChainCtl {
+  uint32_t* arrive;    // [step][workgroup]: the run's tag once the workgroup finished the step
+  uint32_t* done;      // [step]: the run's tag once every workgroup finished the step
+  uint32_t* epoch;     // tag of the last completed run
+  uint32_t* error;     // set when a wait gave up
+  uint32_t groups;     // workgroups of the launch
+  uint32_t spin;       // polls before a wait gives up
+};
+
+// One step of a chain, device-resident: its launch arguments, weight type and
+// logical workgroups (a multiple of 8, at most the launch's).
+struct ChainStep {
+  GemvArgs a;
+  int32_t type;
+  int32_t grid;
+};
+
+struct ChainArgs {
+  const ChainStep* steps;
+  int32_t n_steps;
+  ChainCtl ctl;
+};
+
+template <int B, bool XF32>
+hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t lds, hipStream_t s, int* occupancy);
+
 template <int QT>
 hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
                             hipStream_t s);

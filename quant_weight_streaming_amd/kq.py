@@ -21,9 +21,20 @@ KQ_MAX_BATCH, KQ_MAX_PROJ = 8, 8
 TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
-          5: "KQ_ERR_TYPE", 6: "KQ_ERR_HIP", 7: "KQ_ERR_NOMEM", 8: "KQ_ERR_RANGE"}
+          5: "KQ_ERR_TYPE", 6: "KQ_ERR_HIP", 7: "KQ_ERR_NOMEM", 8: "KQ_ERR_RANGE", 9: "KQ_ERR_TIMEOUT",
+          10: "KQ_ERR_DEVICE"}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
-           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant")
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant", "kq_chain_create", "kq_chain_run",
+           "kq_chain_status", "kq_chain_destroy")
+
+
+class ChainStep(ctypes.Structure):
+    """Mirror of kq_chain_step."""
+    _fields_ = [("type", ctypes.c_int32), ("n", ctypes.c_int32), ("cols", ctypes.c_int64),
+                ("w", ctypes.c_void_p * KQ_MAX_PROJ), ("rows", ctypes.c_int64 * KQ_MAX_PROJ),
+                ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
+                ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64)]
 
 
 class KQError(RuntimeError):
@@ -61,6 +72,13 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_multi.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
+        L.kq_chain_create.argtypes = [ci, ctypes.POINTER(ChainStep), ci, ci, ctypes.POINTER(vp)]
+        L.kq_chain_create.restype = ci
+        for n in ("kq_chain_status", "kq_chain_destroy"):
+            getattr(L, n).argtypes = [vp]
+            getattr(L, n).restype = ci
+        L.kq_chain_run.argtypes = [vp, vp]
+        L.kq_chain_run.restype = ci
         _lib = L
     return _lib
 
@@ -143,7 +161,64 @@ def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, 
                                           _stream(stream)))
 
 
+def kq_chain_create(steps, xtype: int, batch: int) -> int:
+    """steps: sequence of (qtype, ws, rows, cols, x, ys) as kq_gemv_multi takes them; returns the handle."""
+    arr = (ChainStep * len(steps))()
+    for st, (qtype, ws, rows, cols, x, ys) in zip(arr, steps):
+        n = len(ws)
+        if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ:
+            raise ValueError("ws, rows and ys must have the same length, at most KQ_MAX_PROJ")
+        st.type, st.n, st.cols = _type(qtype), n, cols
+        for i in range(n):
+            st.w[i], st.rows[i], st.y[i], st.ldy[i] = ws[i].data_ptr(), rows[i], ys[i].data_ptr(), ys[i].stride(0)
+        st.x, st.ldx = x.data_ptr(), x.stride(0)
+    h = ctypes.c_void_p()
+    _check("kq_chain_create", lib().kq_chain_create(len(steps), arr, xtype, batch, ctypes.byref(h)))
+    return h.value
+
+
+def kq_chain_run(handle: int, stream=None) -> None:
+    _check("kq_chain_run", lib().kq_chain_run(handle, _stream(stream)))
+
+
+def kq_chain_status(handle: int) -> int:
+    """KQ_OK, or the status code (KQ_ERR_TIMEOUT when a wait gave up); does not raise."""
+    return lib().kq_chain_status(handle)
+
+
+def kq_chain_destroy(handle: int) -> None:
+    _check("kq_chain_destroy", lib().kq_chain_destroy(handle))
+
+
 # ---------------------------------------------------------------- conveniences
+
+
+class Chain:
+    """A chain plan that keeps the tensors of its steps alive; run() enqueues one run."""
+
+    def __init__(self, steps, batch: int):
+        self.steps = list(steps)
+        xt = {_xtype(s[4]) for s in self.steps}
+        if len(xt) != 1:
+            raise ValueError("every step of a chain takes the same activation type")
+        self.handle = kq_chain_create(self.steps, xt.pop(), batch)
+
+    def run(self, stream=None) -> None:
+        kq_chain_run(self.handle, stream)
+
+    def status(self) -> int:
+        return kq_chain_status(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            kq_chain_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 GEMV = {"q4k": kq_gemv_q4k, "q5k": kq_gemv_q5k, "q6k": kq_gemv_q6k}
 

@@ -82,3 +82,59 @@ def test_multi_and_others_reject():
     assert L.kq_dequant(1, A16, 64, 256, A16, 100, None) == 2     # ldo < cols
     assert L.kq_dequant(3, A16 + 8, 64, 256, A16, 256, None) == 3
     assert kq.lib().kq_status_str(3) == b"misaligned pointer or stride"
+
+
+def test_chain_step_layout_matches_header(tmp_path):
+    """The ctypes mirror of kq_chain_step has the C layout (size and every field offset)."""
+    import subprocess
+    fields = [f[0] for f in kq.ChainStep._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "kq.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(kq_chain_step));\n' +
+                   "".join(f'  printf(" %zu", offsetof(kq_chain_step, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(kq.ChainStep)] + [getattr(kq.ChainStep, f).offset for f in fields]
+
+
+def _step(**kw):
+    st = kq.ChainStep()
+    st.type, st.n, st.cols, st.x, st.ldx = 1, 1, 256, A16, 256
+    st.w[0], st.rows[0], st.y[0], st.ldy[0] = A16, 64, A16, 64
+    for k, v in kw.items():
+        setattr(st, k, v)
+    return st
+
+
+@pytest.mark.parametrize("step,xtype,batch,code", [
+    (dict(type=9), 1, 1, 5),                 # weight type
+    (dict(), 7, 1, 5),                       # activation type
+    (dict(), 1, 0, 4),                       # batch
+    (dict(), 1, 9, 4),
+    (dict(n=0), 1, 1, 4),                    # segments
+    (dict(cols=300, ldx=300), 1, 1, 2),      # cols % 256
+    (dict(ldx=128), 1, 1, 2),                # ldx < cols
+    (dict(x=None), 1, 1, 1),
+    (dict(x=A16 + 2), 1, 1, 3),
+    (dict(ldx=1 << 30), 1, 2, 8),            # x rows beyond 31-bit offsets
+])
+def test_chain_create_rejects(step, xtype, batch, code):
+    arr = (kq.ChainStep * 2)(_step(), _step(**step))
+    h = ctypes.c_void_p(1234)
+    assert kq.lib().kq_chain_create(2, arr, xtype, batch, ctypes.byref(h)) == code
+    assert h.value is None                   # nothing was created
+
+
+def test_chain_other_rejects():
+    L = kq.lib()
+    arr = (kq.ChainStep * 1)(_step())
+    h = ctypes.c_void_p()
+    assert L.kq_chain_create(0, arr, 1, 1, ctypes.byref(h)) == 4
+    assert L.kq_chain_create(1, None, 1, 1, ctypes.byref(h)) == 1
+    assert L.kq_chain_create(1, arr, 1, 1, None) == 1
+    assert L.kq_chain_run(None, None) == 1
+    assert L.kq_chain_status(None) == 1
+    assert L.kq_chain_destroy(None) == 0
+    assert L.kq_status_str(9) == b"a chain step's wait for the previous step gave up"

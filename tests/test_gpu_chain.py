@@ -1,0 +1,217 @@
+"""Chains (kq_chain_*): a dependent sequence of GEMV steps in one persistent launch.
+
+Every step must give what the same kq_gemv_multi call gives on its own (same
+partition, so bitwise), within the oracle tolerance; a step whose x is the
+previous step's y must read it only after it is complete; a run may be replayed
+from a HIP graph; and a wait that gives up is reported, not hung on.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quant_weight_streaming_amd import kq, synth
+from tests.gpu_cases import check_y, say, x_host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+DEV = "cuda:0"
+SENTINEL = 1.0e30
+
+
+def _weights(qtype, parts, cols, tag):
+    gs = [synth.gen_weights(qtype, r, cols, synth.seed_of("chain", tag, i)) for i, r in enumerate(parts)]
+    ws = [kq.repack(qtype, g.to(DEV), r, cols) for g, r in zip(gs, parts)]
+    return gs, ws
+
+
+def _singles(steps):
+    """The same steps as separate kq_gemv_multi launches, into fresh outputs."""
+    outs = []
+    for qtype, ws, rows, cols, x, ys in steps:
+        yy = [torch.full_like(y, SENTINEL) for y in ys]
+        kq.kq_gemv_multi(qtype, ws, rows, cols, x, yy)
+        outs.append(yy)
+    torch.cuda.synchronize()
+    return outs
+
+
+def _independent_steps(specs, batch, xdtype, tag):
+    """specs: (qtype, parts, cols); each step gets its own x."""
+    steps, hosts = [], []
+    for j, (qtype, parts, cols) in enumerate(specs):
+        gs, ws = _weights(qtype, parts, cols, f"{tag}{j}")
+        x = synth.gen_x(batch, cols, synth.seed_of("chain-x", tag, j), xdtype)
+        ys = [torch.full((batch, r + 3), SENTINEL, device=DEV) for r in parts]
+        steps.append((qtype, ws, list(parts), cols, x.to(DEV), ys))
+        hosts.append((gs, x))
+    return steps, hosts
+
+
+def _check_steps(steps, hosts, singles, where):
+    for j, ((qtype, ws, parts, cols, x, ys), (gs, xh), ref) in enumerate(zip(steps, hosts, singles)):
+        for i, (g, r, y, y1) in enumerate(zip(gs, parts, ys, ref)):
+            yc = y[:, :r].cpu()
+            assert torch.equal(yc, y1[:, :r].cpu()), f"{where} step {j} part {i}: differs from its single launch"
+            assert (y[:, r:].cpu() == SENTINEL).all(), f"{where} step {j} part {i}: wrote outside [0, rows)"
+            yo, ao = O.gemv(qtype, r, cols, g.numpy(), x_host(xh))
+            check_y(yc.numpy(), yo, ao, f"{where} step {j} part {i}")
+
+
+MIXED = [("q4k", (100, 64, 37), 1024), ("q6k", (300,), 512), ("q5k", (129,), 2048),
+         ("q4k", (64,), 256), ("q6k", (5 * 64 + 9,), 122 * 256), ("q4k", (1,), 256)]
+
+
+@pytest.mark.parametrize("batch,xdtype", [(1, "bf16"), (2, "bf16"), (3, "bf16"), (5, "bf16"), (8, "bf16"),
+                                          (1, "f32"), (4, "f32")])
+def test_chain_matches_single_launches(batch, xdtype):
+    say(f"case chain mixed B={batch} x={xdtype}")
+    steps, hosts = _independent_steps(MIXED, batch, xdtype, f"mixed{batch}{xdtype}")
+    ch = kq.Chain(steps, batch)
+    for rep in range(2):                       # the second run starts from the counters the first left
+        for s in steps:
+            for y in s[5]:
+                y.fill_(SENTINEL)
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        _check_steps(steps, hosts, _singles(steps), f"mixed B={batch} {xdtype} run {rep}")
+    ch.close()
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_chain_sweep_layer(batch):
+    """One decoder layer at full size plus the head, as the sweep runs them."""
+    say(f"case chain sweep layer B={batch}")
+    specs = [(s.qtype, tuple(s.parts) or (s.rows,), s.cols)
+             for s in (synth.QKV, synth.O_PROJ, synth.GATE_UP, synth.DOWN, synth.HEAD)]
+    steps = []
+    for j, (qtype, parts, cols) in enumerate(specs):
+        ws = []
+        for i, r in enumerate(parts):
+            g = synth.gen_weights(qtype, r, cols, synth.seed_of("chain-layer", j, i), device=DEV)
+            ws.append(kq.repack(qtype, g, r, cols))
+            del g
+        x = synth.gen_x(batch, cols, synth.seed_of("chain-layer-x", j), device=DEV)
+        steps.append((qtype, ws, list(parts), cols, x, [torch.empty((batch, r), device=DEV) for r in parts]))
+    singles = _singles(steps)
+    ch = kq.Chain(steps, batch)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == 0
+    for j, (s, ref) in enumerate(zip(steps, singles)):
+        for i, (y, y1) in enumerate(zip(s[5], ref)):
+            assert torch.equal(y, y1), f"layer step {j} part {i}: differs from its single launch"
+    ch.close()
+
+
+def _dependent_chain(batch):
+    """fp32 chain where every step reads the previous step's y: K_{j+1} = M_j."""
+    specs = [("q4k", (512,), 1024), ("q6k", (768,), 512), ("q5k", (256,), 768), ("q4k", (300, 212), 256)]
+    x0 = synth.gen_x(batch, 1024, synth.seed_of("dep-x"), "f32").to(DEV)
+    steps, gs_all, x = [], [], x0
+    for j, (qtype, parts, cols) in enumerate(specs):
+        gs, ws = _weights(qtype, parts, cols, f"dep{j}")
+        ys = [torch.full((batch, r), SENTINEL, device=DEV) for r in parts]
+        steps.append((qtype, ws, list(parts), cols, x, ys))
+        gs_all.append(gs)
+        x = ys[0]                                   # the next step reads this step's (first) output
+    return steps, gs_all, x0
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_chain_reads_previous_output(batch):
+    say(f"case chain dependent fp32 B={batch}")
+    steps, gs_all, x0 = _dependent_chain(batch)
+    ch = kq.Chain(steps, batch)
+    for rep in range(3):
+        for s in steps:
+            for y in s[5]:
+                y.fill_(SENTINEL)                   # a step that read too early would see these
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        # each step against a single launch on the chain's own input, bitwise
+        for j, (qtype, ws, parts, cols, x, ys) in enumerate(steps):
+            ref = [torch.empty_like(y) for y in ys]
+            kq.kq_gemv_multi(qtype, ws, parts, cols, x, ref)
+            torch.cuda.synchronize()
+            for i, (y, y1) in enumerate(zip(ys, ref)):
+                assert torch.equal(y, y1), f"dependent run {rep} step {j} part {i}: differs from a single launch"
+    # against the oracle run step by step on its own outputs, with the error carried through: if the
+    # input of a step is off by at most E, its output is off by at most |W| (1.0001 E + 2e-4 |x|)
+    # (the inherited error, this step's 1e-4 * sum |w x| and the fp32 rounding of the oracle's input)
+    xh = x_host(x0).astype(np.float64)
+    e_prev = np.zeros_like(xh)
+    for j, (qtype, ws, parts, cols, x, ys) in enumerate(steps):
+        nxt = None
+        for i, (g, r, y) in enumerate(zip(gs_all[j], parts, ys)):
+            yo, ao = O.gemv(qtype, r, cols, g.numpy(), xh.astype(np.float32))
+            W = np.abs(O.dequant_f32(qtype, r, cols, g.numpy()).astype(np.float64))
+            bound = (1.0001 * e_prev + 2e-4 * np.abs(xh)) @ W.T
+            err = np.abs(y.cpu().numpy().astype(np.float64) - yo)
+            assert (err <= bound).all(), f"dependent step {j} part {i}: {int((err > bound).sum())} outputs off"
+            if i == 0:
+                nxt = (yo, bound)
+        xh, e_prev = nxt
+    ch.close()
+
+
+def test_chain_graph_replay():
+    """A captured run replayed several times, with eager work in between, equals the eager run."""
+    batch = 2
+    say("case chain graph replay")
+    steps, gs_all, x0 = _dependent_chain(batch)
+    ch = kq.Chain(steps, batch)
+    ch.run()
+    torch.cuda.synchronize()
+    want = [[y.clone() for y in s[5]] for s in steps]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ch.run(s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for st in steps:
+            for y in st[5]:
+                y.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (st, w) in enumerate(zip(steps, want)):
+            for i, (y, y1) in enumerate(zip(st[5], w)):
+                assert torch.equal(y, y1), f"replay {rep} step {j} part {i} differs from the eager run"
+    assert ch.status() == 0
+    del g
+    ch.close()
+
+
+def test_chain_wait_that_gives_up_is_reported(monkeypatch):
+    """With no polls allowed (KQ_CHAIN_SPIN=0) a wait that finds the previous step unfinished gives up:
+    the run ends and kq_chain_status says so (the results are then invalid); a chain made with the
+    default limit afterwards runs clean."""
+    batch = 1
+    say("case chain spin 0")
+    specs = [("q6k", (64 * 64,), 122 * 256), ("q4k", (256,), 1024), ("q4k", (256,), 1024)]
+    steps, hosts = _independent_steps(specs, batch, "bf16", "spin")
+    monkeypatch.setenv("KQ_CHAIN_SPIN", "0")
+    ch = kq.Chain(steps, batch)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == kq.STATUS_CODE["KQ_ERR_TIMEOUT"]
+    assert ch.status() == 0                    # reading the flag cleared it
+    ch.close()
+    monkeypatch.delenv("KQ_CHAIN_SPIN")
+    ch = kq.Chain(steps, batch)
+    for s in steps:
+        for y in s[5]:
+            y.fill_(SENTINEL)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == 0
+    _check_steps(steps, hosts, _singles(steps), "after a time-out")
+    ch.close()
