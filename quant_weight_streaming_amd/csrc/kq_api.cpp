@@ -88,16 +88,17 @@ static hipError_t launch_gemv(int type, int xtype, int batch, int nw, bool mf, c
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Tuning knobs, read per call: target wavefronts per CU (KQ_WAVES_PER_CU, default
-// 8) and wavefronts per workgroup (KQ_WG_WAVES, 4 or 8; default 8 from batch
-// kWideBatch up, where one workgroup per CU stages the activations of all its
-// columns once and reuses them across its row tiles, else 4).
+// 8) and wavefronts per workgroup (KQ_WG_WAVES, 4 or 8).  From batch 2 the
+// default is 8: one workgroup per CU stages the activations of its columns once
+// for all of its wavefronts.  At batch 1 it is 4 (two workgroups per CU, fixed
+// runs); 8 gives one workgroup per CU whose wavefronts share its units
+// dynamically, which evens out the CU's wavefronts but measured no faster.
 static int waves_per_cu() {
   const char* e = getenv("KQ_WAVES_PER_CU");
   const int x = e ? atoi(e) : 0;
   return (x >= 1 && x <= 32) ? x : 8;
 }
 
-constexpr int kWideBatch = 2;
 
 // Whole tiles per workgroup forced for every shape (KQ_ALIGNED_TILES; 0 = automatic).
 static int aligned_tiles() {
@@ -127,8 +128,10 @@ static int wg_waves(int batch) {
   const char* e = getenv("KQ_WG_WAVES");
   const int x = e ? atoi(e) : 0;
   if (x == 4 || x == 8) return x;
-  return batch >= kWideBatch ? 8 : 4;
+  return batch == 1 ? 4 : 8;
 }
+
+constexpr size_t kMaxLds = 160 * 1024;   // LDS of one CU
 
 // Argument checks shared by every GEMV entry point and every chain step.
 static int validate(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
@@ -162,7 +165,7 @@ struct Plan {
 // `max_grid` workgroups (a multiple of 8).
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
-                     int64_t max_grid, float* partial, uint32_t* counters, Plan* out) {
+                     int64_t max_grid, int force_nw, float* partial, uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
   GemvArgs a{};
   int64_t tiles = 0;
@@ -186,14 +189,14 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   // (and sub-block sums) of the columns its nw*upw units touch in LDS, within
   // `budget` bytes (64 KiB leaves room for two 4-wavefront workgroups per CU,
   // 112 KiB is for one 8-wavefront workgroup), plus its wavefronts' partial sums.
-  const int nw = wg_waves(batch);
+  const int nw = force_nw ? force_nw : wg_waves(batch);
   const bool mf = xtype == KQ_X_BF16 && batch >= matrix_cores_from();
   const int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
   const int64_t target = (int64_t)cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
   const int64_t per_col =
-      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0));
+      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1, 0) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0, 0));
   const int64_t max_cols = budget / per_col;
   if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
   if (upw > n_cols + 1) upw = n_cols + 1;   // a wavefront's run then touches at most two tiles
@@ -250,7 +253,9 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   out->nw = nw;
   out->mf = mf;
   out->grid = grid;
-  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols);
+  const int64_t run_units = a.tiles_per_wg > 0 ? (int64_t)a.tiles_per_wg * tcols : nw * upw;
+  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols, (int)run_units);
+  if (out->lds > kMaxLds) return KQ_ERR_RANGE;
   return KQ_OK;
 }
 
@@ -263,9 +268,12 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   DeviceState* st = nullptr;
   rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
-  Plan p;
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, st->partial,
+  Plan p{};
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, st->partial,
                  st->counters, &p);
+  if (rc == KQ_ERR_RANGE && wg_waves(batch) == 8)   // too many units per workgroup for per-unit slots: 4-wavefront runs
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, st->partial,
+                   st->counters, &p);
   if (rc != KQ_OK) return rc;
   if (launch_gemv(type, xtype, batch, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
@@ -415,21 +423,30 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   kq_chain* c = new (std::nothrow) kq_chain;
   if (!c) return KQ_ERR_NOMEM;
   std::vector<Plan> plans(n_steps);
+  int nw = wg_waves(batch);
   auto plan_all = [&](int64_t max_grid, size_t* lds) {
     *lds = 0;
     for (int j = 0; j < n_steps; ++j) {
       const kq_chain_step& st = steps[j];
-      const int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
-                               max_grid, nullptr, nullptr, &plans[j]);
+      int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
+                         max_grid, nw, nullptr, nullptr, &plans[j]);
+      if (rc == KQ_ERR_RANGE && nw == 8) {   // every step then runs with 4-wavefront workgroups
+        nw = 4;
+        return (int)KQ_ERR_RANGE;
+      }
       if (rc != KQ_OK) return rc;
       if (plans[j].lds > *lds) *lds = plans[j].lds;
     }
     return (int)KQ_OK;
   };
-  const int nw = wg_waves(batch);
-  int64_t groups = (int64_t)cus * (8 / nw);
+  int64_t groups = (int64_t)cus * (8 / nw);   // one 8-wavefront or two 4-wavefront workgroups per CU
   size_t lds = 0;
+  const int nw0 = nw;
   int rc = plan_all(groups, &lds);
+  if (rc == KQ_ERR_RANGE && nw != nw0) {
+    groups = (int64_t)cus * 2;
+    rc = plan_all(groups, &lds);
+  }
   int occ = 0;
   if (rc == KQ_OK &&
       launch_chain(xtype, batch, ChainArgs{}, nw, plans[0].mf, 0, lds, nullptr, &occ) != hipSuccess)

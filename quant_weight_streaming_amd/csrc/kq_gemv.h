@@ -621,8 +621,16 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   float* P = MF ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds_words) +
                                            a.tsb * MfmaLds<QT, B>::kPerCol + 512)
                 : T + a.tsb * SB * B;
-  const int u0 = U0 + wid * upw;
-  const int u1 = min(u0 + upw, U1);
+  // DYN (batch 1, one 8-wavefront workgroup per CU): instead of fixed runs the
+  // wavefronts take the workgroup's units one at a time from an LDS counter, so
+  // a wavefront that gets fewer issue slots than its neighbours simply computes
+  // fewer units; each unit's row sums go to an LDS slot of their own and a
+  // tile's slots are added in unit order, so y does not depend on which
+  // wavefront computed what.  P then holds the counter (16 bytes) and the slots
+  // [U1 - U0][B][64].
+  constexpr bool DYN = dyn_units<B, NW, MF>();
+  const int u0 = DYN ? U0 + wid : U0 + wid * upw;
+  const int u1 = DYN ? U1 : min(u0 + upw, U1);
   const bool active = u0 < U1;
   const int t0 = u0 / cw;                          // first tile of this wavefront
   const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
@@ -657,6 +665,9 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
 #pragma unroll
     for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
   }
+  if constexpr (DYN) {
+    if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(P) = (DEPTH - 1) * NW;   // the prologue took units 0..NW-1
+  }
   {
     uint8_t* Xb = reinterpret_cast<uint8_t*>(lds_words);
     xs.template store<!MF>(Xb, T, len, 0);
@@ -674,7 +685,53 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   }
   __syncthreads();
 
-  if (active) {
+  if constexpr (DYN) {
+    // unit indices (relative to U0) held by the buffers; >= n: nothing
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(P);
+    float* S = P + 4;
+    const int n = U1 - U0;
+    int kb[DEPTH];
+#pragma unroll
+    for (int k = 0; k + 1 < DEPTH; ++k) kb[k] = wid + k * NW;
+    auto grab = [&]() -> int {
+      uint32_t v = 0;
+      if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return (int)__builtin_amdgcn_readfirstlane(v);
+    };
+    auto refill_unit = [&](int k, int idx) {
+      const int U = U0 + idx;
+      const int tu = U / cw;
+      load_unit<QT>(unit_rsrc<QT>(a, tu, cs + (U - tu * cw), idx < n), lane, buf[k], d6[k]);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // the index for the next refill is taken one step early, so the LDS
+    // atomic's latency hides behind a unit's arithmetic
+    int nxt = grab();
+    bool more = true;
+    while (more) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        const int nk = (k + DEPTH - 1) % DEPTH;
+        kb[nk] = nxt;
+        refill_unit(nk, nxt);
+        nxt = grab();
+        if (kb[k] >= n) {
+          more = false;
+          break;
+        }
+        const int U = U0 + kb[k];
+        int ic = cs + U % cw - c0w;
+        if (ic < 0) ic += cw;
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+        process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+#pragma unroll
+        for (int b = 0; b < B; ++b) S[(kb[k] * B + b) * kTileRows + lane] = acc[b];
+      }
+    }
+  } else if (active) {
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
@@ -731,12 +788,19 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     float s[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) s[b] = 0.0f;
-    for (int i = 0; i < NW; ++i) {
-      const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
-      if (max(a0, ts) >= min(a1, te)) continue;
-      const float* pw = P + ((i * kTilesPerWave + (t - a0 / cw)) * B) * kTileRows;
+    if constexpr (DYN) {
+      const float* S = P + 4;
+      for (int U = max(U0, ts); U < min(U1, te); ++U)
 #pragma unroll
-      for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
+        for (int b = 0; b < B; ++b) s[b] += S[((U - U0) * B + b) * kTileRows + lane];
+    } else {
+      for (int i = 0; i < NW; ++i) {
+        const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
+        if (max(a0, ts) >= min(a1, te)) continue;
+        const float* pw = P + ((i * kTilesPerWave + (t - a0 / cw)) * B) * kTileRows;
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
+      }
     }
     if (a.n_win > 1) hand_off_windows<B, CHAIN>(a, t, w, lane, s);
     else if (ts >= U0 && te <= U1) write_tile<B, CHAIN>(a, t, lane, s);   // every tile when tiles_per_wg > 0

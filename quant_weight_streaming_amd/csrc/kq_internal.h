@@ -70,9 +70,17 @@ hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArg
 // The dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols` columns
 // needs on the chosen path: per column the activations of every batch row and
 // their sub-block sums (matrix cores: rows padded to 528 bytes, then a 512-byte
-// zero block), plus each wavefront's partial sums of up to two tiles.
-inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols) {
-  const size_t partials = (size_t)nw * kTilesPerWave * batch * 64 * sizeof(float);
+// zero block), plus each wavefront's partial sums of up to two tiles (dynamic
+// workgroups: a counter and one slot per unit).
+// Workgroups whose wavefronts take units dynamically (see gemv_block).
+template <int B, int NW, bool MF>
+__host__ __device__ constexpr bool dyn_units() { return B == 1 && NW == 8 && !MF; }
+inline bool dyn_units(int batch, int nw, bool mf) { return batch == 1 && nw == 8 && !mf; }
+
+// `run_units`: units of one workgroup (the per-unit slots of dynamic workgroups).
+inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols, int run_units) {
+  const size_t partials = dyn_units(batch, nw, mf) ? 16 + (size_t)run_units * batch * 64 * sizeof(float)
+                                                   : (size_t)nw * kTilesPerWave * batch * 64 * sizeof(float);
   const int sb = type == KQ_Q6_K ? 16 : 8;
   if (mf) {
     const int nb = (batch + 3) / 4;

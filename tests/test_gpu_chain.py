@@ -215,3 +215,17 @@ def test_chain_wait_that_gives_up_is_reported(monkeypatch):
     assert ch.status() == 0
     _check_steps(steps, hosts, _singles(steps), "after a time-out")
     ch.close()
+
+
+def test_chain_dynamic_units(monkeypatch):
+    """Batch 1 with 8-wavefront workgroups (KQ_WG_WAVES=8): the chain's steps take units dynamically
+    and still match their single launches bitwise."""
+    monkeypatch.setenv("KQ_WG_WAVES", "8")
+    say("case chain dynamic units")
+    steps, hosts = _independent_steps(MIXED, 1, "bf16", "dyn")
+    ch = kq.Chain(steps, 1)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == 0
+    _check_steps(steps, hosts, _singles(steps), "chain dynamic units")
+    ch.close()

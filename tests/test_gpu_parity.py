@@ -174,6 +174,25 @@ def test_one_hot_picks_columns_exactly(qtype, xdtype):
         assert np.array_equal(y[b], W[:, k]), f"column {k}"
 
 
+@pytest.mark.parametrize("qtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+def test_dynamic_units_deterministic(qtype, xdtype):
+    """Batch 1: the wavefronts of a workgroup take units in whatever order they get to them, yet y is
+    bitwise the same on every call (a tile's unit sums are added in unit order) and within tolerance."""
+    rows, cols = 40 * 64 + 7, 48 * 256
+    say(f"case dynamic units {qtype} {xdtype}")
+    g = synth.gen_weights(qtype, rows, cols, synth.seed_of("dyn", qtype))
+    x = synth.gen_x(1, cols, synth.seed_of("dyn-x", qtype), xdtype)
+    w = kq.repack(qtype, g.to(DEV), rows, cols)
+    xd = x.to(DEV)
+    ys = [kq.gemv(qtype, w, rows, cols, xd) for _ in range(4)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0]), "batch-1 results differ between calls"
+    yo, ao = O.gemv(qtype, rows, cols, g.numpy(), x_host(x))
+    check_y(ys[0].cpu().numpy(), yo, ao, f"dynamic units {qtype} {xdtype}")
+
+
 def test_zero_x_and_determinism():
     rows, cols = 500, 2048
     say("case zero-x / determinism")
@@ -200,11 +219,12 @@ def test_strided_x():
 
 
 @pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
-@pytest.mark.parametrize("batch", [2, 5, 6, 7])
+@pytest.mark.parametrize("batch", [1, 2, 5, 6, 7])
 @pytest.mark.parametrize("waves", ["4", "8"])
 def test_workgroup_sizes(qtype, batch, waves, monkeypatch):
-    """Both workgroup shapes (4 and 8 wavefronts, KQ_WG_WAVES) on the matrix-core path, including
-    batches that leave some of an instruction's four result registers unread (5, 6, 7)."""
+    """Both workgroup shapes (4 and 8 wavefronts, KQ_WG_WAVES): at batch 1 the fixed runs and the
+    dynamic unit distribution, from batch 2 the matrix-core path, including batches that leave some of
+    an instruction's four result registers unread (5, 6, 7)."""
     monkeypatch.setenv("KQ_WG_WAVES", waves)
     monkeypatch.setenv("KQ_MATRIX_CORES_FROM", "2")
     run_case(qtype, 5 * 64 + 9, 7 * 256, batch, "bf16", 400 + batch, check_w=False)
