@@ -466,12 +466,13 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
-  // read the pieces four workgroups at a time (one round trip per four), then
-  // add them in workgroup order
-  for (int l0 = la; l0 <= lb; l0 += 4) {
-    float v[4][B];
+  // read the pieces PR workgroups at a time (one round trip per PR), then add
+  // them in workgroup order
+  constexpr int PR = B <= 2 ? 8 : 4;
+  for (int l0 = la; l0 <= lb; l0 += PR) {
+    float v[PR][B];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PR; ++j) {
       const int l = l0 + j;
       const int sl = (t == (l * wgu) / n_cols) ? 0 : 1;
       const float* pp = a.partial + (int64_t)(l * 2 + sl) * kPartialStride;
@@ -481,7 +482,7 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
                           : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < PR; ++j)
 #pragma unroll
       for (int b = 0; b < B; ++b)
         if (l0 + j <= lb) s[b] += v[j][b];
@@ -508,10 +509,11 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
-  for (int w0 = 0; w0 < a.n_win; w0 += 4) {
-    float q[4][B];
+  constexpr int PR = B <= 2 ? 8 : 4;
+  for (int w0 = 0; w0 < a.n_win; w0 += PR) {
+    float q[PR][B];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PR; ++j) {
       const float* pp = a.partial + (int64_t)((w0 + j) * a.n_tiles + t) * kPartialStride;
 #pragma unroll
       for (int b = 0; b < B; ++b)
@@ -520,7 +522,7 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
                       : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < PR; ++j)
 #pragma unroll
       for (int b = 0; b < B; ++b)
         if (w0 + j < a.n_win) s[b] += q[j][b];
@@ -656,8 +658,11 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   constexpr int kRS = MF ? MfmaLds<QT, B>::kXRow : 256 * (XF32 ? 4 : 2);
   XStage<QT, B, XF32, NW, kRS> xs;
   if constexpr (CHAIN) {
+    // before the step barrier every buffer is filled (DYN: the first unit), so
+    // twice as many weights stream in while the previous step drains
 #pragma unroll
     for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
+    if constexpr (!DYN) refill(DEPTH - 1);
     chain_wait(*ctl, step, tag);
     xs.template load<true>(a, c0w, len, 0);
   } else {
@@ -770,11 +775,23 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     // step freed, then computes unit u.  Loads past the run are issued too,
     // through a zero-size resource, so every step has the same loads in flight
     // and the wait before a computation is for its own unit only.
-    while (u < u1) {
+    if constexpr (CHAIN) {
+      // every buffer was filled before the barrier: compute, then refill the
+      // buffer just freed (the same loads in flight as below, one step later)
+      while (u < u1) {
 #pragma unroll
-      for (int k = 0; k < DEPTH; ++k) {
-        refill((k + DEPTH - 1) % DEPTH);
-        if (u < u1) consume(k);
+        for (int k = 0; k < DEPTH; ++k) {
+          if (u < u1) consume(k);
+          refill(k);
+        }
+      }
+    } else {
+      while (u < u1) {
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+          refill((k + DEPTH - 1) % DEPTH);
+          if (u < u1) consume(k);
+        }
       }
     }
   }
