@@ -61,7 +61,7 @@ def kernel_source_hash() -> str:
 class Sweep:
     """Device-resident weights, activations and outputs of one sweep, with the launch list."""
 
-    def __init__(self, cfg: int, gate_up_type: str, batches, merge: float, sample_frac: float):
+    def __init__(self, cfg, gate_up_type: str, batches, merge: float, sample_frac: float, entries=None):
         import torch
         from quant_weight_streaming_amd import kq, synth
         self.torch, self.kq, self.synth = torch, kq, synth
@@ -71,7 +71,7 @@ class Sweep:
         self.weight_bytes = 0
         dev = "cuda:0"
         t0 = time.time()
-        for layer, spec in synth.sweep(gate_up_type):
+        for layer, spec in (entries if entries is not None else synth.sweep(gate_up_type)):
             g = synth.gen_weights(spec.qtype, spec.rows, spec.cols, synth.seed_of(cfg, layer, spec.name),
                                   device=dev, merge_frac=merge if spec.qtype == "q4k" else 0.0)
             parts = list(spec.parts) or [spec.rows]
@@ -399,6 +399,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-c4", action="store_true", help="skip the Q5_K / merged-sub-block sweep")
+    ap.add_argument("--no-p4", action="store_true", help="skip the 6656-hidden decoder's sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--profile-kernel", type=int, default=0)
     ap.add_argument("--profile-batch", type=int, default=1, help="batch of the --profile-kernel launches")
@@ -486,9 +487,30 @@ def main():
                 f"({sw4.weight_bytes / best / 1e6:.0f} GB/s)")
         c4["weight_bytes"] = sw4.weight_bytes
         c4["kernels_b8"] = kernel_times(sw4, 8)
+        del sw4
         sw = None
     else:
         bytes3 = sw.weight_bytes
+
+    # the 6656-hidden decoder of the Core AI card (its own sweep; not the headline workload)
+    p4 = None
+    if not args.no_p4:
+        sw = None
+        torch.cuda.empty_cache()
+        swp = Sweep("p4", "q4k", (1, 8), 0.0, 0.0, entries=synth.sweep_p4())
+        p4 = {"workload": "52 x {QKVG Q4_K 8704x6656, O Q4_K 6656x4096, gate+up Q4_K 39936x6656, down Q6_K "
+                          "6656x19968} + head Q6_K 202048x6656", "weight_bytes": swp.weight_bytes}
+        for B in (1, 8):
+            plain, graph = time_sweep(swp, B, max(3, args.steps // 2), args.warmup)
+            chain = time_chain(swp, B, max(3, args.steps // 2), args.warmup)
+            best = min(graph, chain)
+            p4[f"b{B}"] = dict(graph_ms=round(graph, 4), chain_ms=round(chain, 4), plain_ms=round(plain, 4),
+                               weight_gbs=round(weight_gbs(swp.weight_bytes, best), 1),
+                               pct_of_hbm_peak=round(100 * weight_gbs(swp.weight_bytes, best) / HBM_PEAK_GBS, 2),
+                               tok_s=round(tok_s(best, B), 1))
+            log(f"[bench] p4 B={B}: graph {graph:.3f} ms, chain {chain:.3f} ms "
+                f"({swp.weight_bytes / best / 1e6:.0f} GB/s)")
+        del swp
 
     # the sweep's time per token: the faster of the two ways of running the same dependent sequence
     def best(r):
@@ -529,6 +551,7 @@ def main():
         "kernels_b1": kt1,
         "kernels_b8": kt8,
         "c4_q5k_merged": c4,
+        "hidden6656_sweep": p4,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_hash": kernel_source_hash(),

@@ -196,15 +196,14 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
   const int64_t per_col =
-      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1, 0) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0, 0));
+      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1, 0, 0) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0, 0, 0));
   const int64_t max_cols = budget / per_col;
   if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
-  if (upw > n_cols + 1) upw = n_cols + 1;   // a wavefront's run then touches at most two tiles
   int64_t n_groups = (n_units + nw * upw - 1) / (nw * upw);
   bool even_ok = true;   // even runs fit the staging budget within max_groups workgroups
   if ((n_groups + 7) / 8 * 8 > max_groups) {
     upw = (n_units + nw * (max_groups / 8 * 8) - 1) / (nw * (max_groups / 8 * 8));
-    even_ok = !((n_cols > max_cols && nw * upw > max_cols) || upw > n_cols + 1);
+    even_ok = !(n_cols > max_cols && nw * upw > max_cols);
     n_groups = (n_units + nw * upw - 1) / (nw * upw);
   }
   int64_t tcols = n_cols < nw * upw ? n_cols : nw * upw;
@@ -225,7 +224,9 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     if (g_target > max_groups) g_target = max_groups;
     int64_t g_win = g_target / n_win > 0 ? g_target / n_win : 1;
     int64_t r = forced_r > 0 ? forced_r : (tiles + g_win - 1) / g_win;
-    if (r > nw) r = nw;                      // a wavefront's run then touches at most two tiles
+    // at most nw tiles per workgroup (a wavefront's run then touches at most two
+    // tiles) unless that needs more than max_groups workgroups
+    if (r > nw && ((tiles + nw - 1) / nw * n_win + 7) / 8 * 8 <= max_groups) r = nw;
     g_win = (tiles + r - 1) / r;
     const int64_t wgrid = (n_win * g_win + 7) / 8 * 8;
     if (wgrid <= max_groups) {
@@ -254,7 +255,16 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   out->mf = mf;
   out->grid = grid;
   const int64_t run_units = a.tiles_per_wg > 0 ? (int64_t)a.tiles_per_wg * tcols : nw * upw;
-  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols, (int)run_units);
+  // a run of u units starting anywhere in a tile of c columns touches at most
+  // ceil((u - 1) / c) + 1 tiles
+  if (a.tiles_per_wg > 0) {
+    const int64_t uw = ((int64_t)a.tiles_per_wg * (a.win_base + 1) + nw - 1) / nw;
+    a.tpw = (int32_t)((uw - 1 + a.win_base - 1) / a.win_base + 1);
+  } else {
+    a.tpw = (int32_t)((upw - 1 + n_cols - 1) / n_cols + 1);
+  }
+  out->a.tpw = a.tpw;
+  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols, (int)run_units, a.tpw);
   if (out->lds > kMaxLds) return KQ_ERR_RANGE;
   return KQ_OK;
 }

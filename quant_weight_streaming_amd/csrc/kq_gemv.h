@@ -619,7 +619,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   const int len = min(cw, U1 - U0);
   uint32_t* X = lds_words;
   float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);
-  // per-wavefront tile sums [NW][kTilesPerWave][B][64] follow the staged columns
+  // per-wavefront tile sums [NW][tpw][B][64] follow the staged columns
   float* P = MF ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds_words) +
                                            a.tsb * MfmaLds<QT, B>::kPerCol + 512)
                 : T + a.tsb * SB * B;
@@ -760,7 +760,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
       }
       if (c == cs + cw - 1 || u + 1 == u1) {
-        float* pw = P + ((wid * kTilesPerWave + (t - t0)) * B) * kTileRows;
+        float* pw = P + ((wid * a.tpw + (t - t0)) * B) * kTileRows;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           pw[b * kTileRows + lane] = acc[b];
@@ -814,7 +814,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
       for (int i = 0; i < NW; ++i) {
         const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
         if (max(a0, ts) >= min(a1, te)) continue;
-        const float* pw = P + ((i * kTilesPerWave + (t - a0 / cw)) * B) * kTileRows;
+        const float* pw = P + ((i * a.tpw + (t - a0 / cw)) * B) * kTileRows;
 #pragma unroll
         for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
       }

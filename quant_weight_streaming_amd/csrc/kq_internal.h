@@ -8,7 +8,6 @@
 
 namespace kq {
 
-constexpr int kTilesPerWave = 2;   // a wavefront's run of units touches at most this many tiles
 
 // Kernel arguments of one GEMV launch (one or several projections sharing x).
 struct GemvArgs {
@@ -24,6 +23,7 @@ struct GemvArgs {
   int32_t n_units;                     // total tiles * n_cols
   int32_t upw;                         // units per wavefront
   int32_t tsb;                         // LDS capacity in staged columns per workgroup
+  int32_t tpw;                         // tiles a wavefront's run of units can touch (its LDS tile sums)
   // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
   // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even
@@ -70,17 +70,19 @@ hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArg
 // The dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols` columns
 // needs on the chosen path: per column the activations of every batch row and
 // their sub-block sums (matrix cores: rows padded to 528 bytes, then a 512-byte
-// zero block), plus each wavefront's partial sums of up to two tiles (dynamic
-// workgroups: a counter and one slot per unit).
+// zero block), plus each wavefront's partial sums of the tiles its run touches
+// (dynamic workgroups: a counter and one slot per unit).
 // Workgroups whose wavefronts take units dynamically (see gemv_block).
 template <int B, int NW, bool MF>
 __host__ __device__ constexpr bool dyn_units() { return B == 1 && NW == 8 && !MF; }
 inline bool dyn_units(int batch, int nw, bool mf) { return batch == 1 && nw == 8 && !mf; }
 
-// `run_units`: units of one workgroup (the per-unit slots of dynamic workgroups).
-inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols, int run_units) {
+// `run_units`: units of one workgroup (the per-unit slots of dynamic workgroups);
+// `tpw`: tiles one wavefront's run can touch (its tile sums otherwise).
+inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols, int run_units,
+                             int tpw) {
   const size_t partials = dyn_units(batch, nw, mf) ? 16 + (size_t)run_units * batch * 64 * sizeof(float)
-                                                   : (size_t)nw * kTilesPerWave * batch * 64 * sizeof(float);
+                                                   : (size_t)nw * tpw * batch * 64 * sizeof(float);
   const int sb = type == KQ_Q6_K ? 16 : 8;
   if (mf) {
     const int nb = (batch + 3) / 4;

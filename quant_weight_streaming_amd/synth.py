@@ -239,6 +239,32 @@ def sweep_bytes(gate_up_type: str = "q4k") -> int:
     return sum(g.rows * g.cols // QK * SB_BYTES[g.qtype] for _, g in sweep(gate_up_type))
 
 
+# The text decoder described on the "Muse-Glimmer-30B (text decoder) - Apple Core AI" card, section
+# "The architecture, and what the port had to do about it": 52 layers, hidden 6656, 32 q / 2 kv heads of
+# 128, a sigmoid output gate read from the same hidden state as Q/K/V (so one fused qkvg projection of
+# 4096 + 256 + 256 + 4096 rows), SwiGLU intermediate 19968, an untied 202048-row head.  The type mix is
+# the one above (Q4_K projections, Q6_K down and head).
+HIDDEN_P4, INTER_P4, VOCAB_P4 = 6656, 19968, 202048
+QKVG_P4 = Gemv("qkvg", "q4k", 8704, HIDDEN_P4, (4096, 256, 256, 4096))
+O_P4 = Gemv("o", "q4k", HIDDEN_P4, 4096)
+GATE_UP_P4 = Gemv("gate_up", "q4k", 2 * INTER_P4, HIDDEN_P4, (INTER_P4, INTER_P4))
+DOWN_P4 = Gemv("down", "q6k", HIDDEN_P4, INTER_P4)
+HEAD_P4 = Gemv("head", "q6k", VOCAB_P4, HIDDEN_P4)
+
+
+def sweep_p4():
+    """The same decode-step sweep for the 6656-hidden decoder."""
+    out = []
+    for layer in range(N_LAYERS):
+        out += [(layer, QKVG_P4), (layer, O_P4), (layer, GATE_UP_P4), (layer, DOWN_P4)]
+    out.append((N_LAYERS, HEAD_P4))
+    return out
+
+
+def sweep_p4_bytes() -> int:
+    return sum(g.rows * g.cols // QK * SB_BYTES[g.qtype] for _, g in sweep_p4())
+
+
 CONFIGS = {
     0: dict(name="q4k_256x1024_b1_f32", gemv=Gemv("c0", "q4k", 256, 1024), batch=(1,), xdtype="f32"),
     1: dict(name="q4k_gate_up_62464x5120_b1", gemv=GATE_UP, batch=(1,), xdtype="bf16"),

@@ -229,3 +229,32 @@ def test_chain_dynamic_units(monkeypatch):
     assert ch.status() == 0
     _check_steps(steps, hosts, _singles(steps), "chain dynamic units")
     ch.close()
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_chain_p4_layer(batch):
+    """One layer and the head of the 6656-hidden decoder as a chain.  The resident grid forces longer
+    runs than a single launch picks (the head at batch 8 takes 25 whole tiles of a column window per
+    workgroup), so the steps are checked against the oracle on sampled rows."""
+    from tests.gpu_cases import oracle_rows, sample_rows
+    say(f"case chain p4 layer B={batch}")
+    steps, gens = [], []
+    for j, spec in enumerate((synth.QKVG_P4, synth.O_P4, synth.GATE_UP_P4, synth.DOWN_P4, synth.HEAD_P4)):
+        parts = list(spec.parts) or [spec.rows]
+        g = synth.gen_weights(spec.qtype, spec.rows, spec.cols, synth.seed_of("chain-p4", j), device=DEV)
+        starts = np.cumsum([0] + parts)
+        ws = [kq.repack(spec.qtype, g[starts[i]:starts[i + 1]].contiguous(), r, spec.cols) for i, r in enumerate(parts)]
+        x = synth.gen_x(batch, spec.cols, synth.seed_of("chain-p4-x", j), device=DEV)
+        steps.append((spec.qtype, ws, parts, spec.cols, x, [torch.empty((batch, r), device=DEV) for r in parts]))
+        gens.append(g)
+    ch = kq.Chain(steps, batch)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == 0
+    for j, ((qtype, ws, parts, cols, x, ys), g) in enumerate(zip(steps, gens)):
+        rows = sum(parts)
+        idx = sample_rows(rows, 96, 600 + j)
+        y = torch.cat(ys, dim=1)[:, torch.as_tensor(idx, device=DEV)].cpu().numpy()
+        _, yo, ao = oracle_rows(qtype, g, idx, cols, x)
+        check_y(y, yo, ao, f"chain p4 step {j} B={batch}")
+    ch.close()

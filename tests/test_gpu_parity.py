@@ -54,6 +54,13 @@ def test_units_span_tiles(qtype, batch):
 
 
 @pytest.mark.parametrize("qtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_runs_span_many_tiles(qtype, batch):
+    # one super-block column and 3000 tiles: a wavefront's run covers several whole tiles
+    run_case(qtype, 3000 * 64 + 5, 256, batch, "bf16", 250 + batch, check_w=False)
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q6k"])
 def test_long_rows_split_many_ways(qtype):
     # 5 tiles x 122 columns (the down projection's K): one unit per wavefront, 122 partials per tile
     run_case(qtype, 300, 31232, 2, "bf16", 300)

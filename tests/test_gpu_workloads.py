@@ -66,3 +66,10 @@ def test_config4_sweep_gemvs(spec):
     if spec.name == "gate_up":
         spec = dataclasses.replace(spec, qtype="q5k")
     run_gemv(spec, [2, 4, 8], 4, merge=0.25)
+
+
+@pytest.mark.parametrize("spec", [synth.QKVG_P4, synth.O_P4, synth.GATE_UP_P4, synth.DOWN_P4, synth.HEAD_P4],
+                         ids=lambda s: s.name)
+def test_p4_sweep_gemvs(spec):
+    """The 6656-hidden decoder's projections (K = 26, 16 and 78 super-blocks, a four-way fused qkvg)."""
+    run_gemv(spec, [1, 3, 8], 5)
