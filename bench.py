@@ -142,6 +142,39 @@ def time_chain(sw: Sweep, B: int, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def time_gather(rows: int, cols: int, batches, reps: int = 64) -> dict:
+    """Mean time of one embedding lookup (kq_gather_rows of `batch` token rows of a Q6_K rows x cols table),
+    from HIP events around a graph of `reps` lookups."""
+    import torch
+    from quant_weight_streaming_amd import kq, synth
+    g = synth.gen_weights("q6k", rows, cols, synth.seed_of("bench-emb"), device="cuda:0")
+    w = kq.repack("q6k", g, rows, cols)
+    del g
+    out = {}
+    for B in batches:
+        ids = torch.randint(0, rows, (B,), dtype=torch.int32, device="cuda:0")
+        o = torch.empty((B, cols), device="cuda:0")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            kq.kq_gather_rows("q6k", w, rows, cols, ids, o, s)
+            with torch.cuda.graph(graph, stream=s):
+                for _ in range(reps):
+                    kq.kq_gather_rows("q6k", w, rows, cols, ids, o, s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"b{B}"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    return out
+
+
 def run_calls(calls):
     for fn, args, name in calls:
         rc = fn(*args)
@@ -511,6 +544,8 @@ def main():
             log(f"[bench] p4 B={B}: graph {graph:.3f} ms, chain {chain:.3f} ms "
                 f"({swp.weight_bytes / best / 1e6:.0f} GB/s)")
         del swp
+        p4["embedding_gather_us"] = time_gather(synth.VOCAB_P4, synth.HIDDEN_P4, (1, 8))
+        log(f"[bench] p4 embedding gather: {p4['embedding_gather_us']}")
 
     # the sweep's time per token: the faster of the two ways of running the same dependent sequence
     def best(r):

@@ -147,6 +147,21 @@ int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, in
 int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
 
 /*
+ * Row gather: the embedding lookup of a token, the step before layer 0 of a
+ * decoder whose embedding is a K-quant matrix of its own (an untied vocabulary
+ * table: "Muse-Glimmer-30B (text decoder) - Apple Core AI", section "The
+ * architecture, and what the port had to do about it", 202 048 rows).
+ *   out[i*ldo + k] = dequant(W)[ids[i], k]   for i < n, k < cols
+ *   w   : repacked weights (kq_repack with the same type, rows, cols), 16-byte aligned.
+ *   ids : device, n int32 row indices, 4-byte aligned; any order, repeats allowed.
+ *   out : device fp32 [n][ldo], ldo >= cols, 4-byte aligned.
+ * Values are bitwise those of kq_dequant.  An id outside [0, rows) yields a row
+ * of quiet NaNs (nothing outside w is read).  n = 0 enqueues nothing.
+ */
+int kq_gather_rows(int type, const void *w, int64_t rows, int64_t cols, const int32_t *ids, int64_t n, float *out,
+                   int64_t ldo, void *stream);
+
+/*
  * Chains: a dependent sequence of GEMV steps in ONE persistent launch.
  *
  * Every token runs the decoder's projections one after the other, each reading

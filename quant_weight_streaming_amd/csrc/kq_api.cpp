@@ -406,6 +406,20 @@ int kq_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, 
   return KQ_OK;
 }
 
+int kq_gather_rows(int type, const void* w, int64_t rows, int64_t cols, const int32_t* ids, int64_t n, float* out,
+                   int64_t ldo, void* stream) {
+  if (!sb_bytes(type)) return KQ_ERR_TYPE;
+  if (n < 0 || n > INT32_MAX) return KQ_ERR_BATCH;
+  if (!w || (n > 0 && (!ids || !out))) return KQ_ERR_NULL;
+  if (rows < 1 || cols <= 0 || cols % 256 != 0 || ldo < cols) return KQ_ERR_SHAPE;
+  if (!aligned(w, 16) || (n > 0 && (!aligned(out, 4) || !aligned(ids, 4)))) return KQ_ERR_ALIGN;
+  if (rows > (int64_t)INT32_MAX - 64 || cols / 256 > INT32_MAX) return KQ_ERR_RANGE;
+  if (n == 0) return KQ_OK;
+  if (launch_gather(type, w, rows, cols, ids, n, out, ldo, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batch, kq_chain** out) {

@@ -94,6 +94,8 @@ inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, in
 hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s);
 hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo,
                           hipStream_t s);
+hipError_t launch_gather(int type, const void* w, int64_t rows, int64_t cols, const int32_t* ids, int64_t n,
+                         float* out, int64_t ldo, hipStream_t s);
 
 int64_t sb_bytes(int type);
 

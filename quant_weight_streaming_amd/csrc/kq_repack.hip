@@ -167,10 +167,40 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint8_t* __restrict__
 
 // out[row*ldo + 256c + e] = fp32 dequantised weight, from the repacked layout,
 // through the same unpacking the GEMV uses.
+// fp32 dequantisation of one super-block (row 64t + lane, column c) of the
+// repacked layout, whose unit starts at `tb`, into o[0..255].
+template <int QT>
+__device__ __forceinline__ void dequant_superblock(const uint8_t* tb, int lane, float* o, uint32_t M, uint32_t K) {
+  using F = Fmt<QT>;
+  u32x4 ch[F::kChunks];
+#pragma unroll
+  for (int k = 0; k < F::kChunks; ++k)
+    ch[k] = *reinterpret_cast<const u32x4*>(tb + k * kChunkStride + lane * kChunk);
+  uint32_t d6 = 0;
+  if constexpr (QT == KQ_Q6_K) d6 = reinterpret_cast<const uint16_t*>(tb + 13 * kChunkStride)[lane];
+  float a[F::kSubBlocks], cm[F::kSubBlocks];
+  sb_coeffs<QT>(ch, d6, 1.0f, a, cm);
+#pragma unroll
+  for (int g = 0; g < F::kSubBlocks; ++g) {
+    uint32_t pr[F::kPairs];
+    unpack_pairs<QT>(ch, g, M, K, pr);
+#pragma unroll
+    for (int i = 0; i < F::kPairs; ++i) {
+      const int e = g * F::kSubW + 2 * i;
+      if constexpr (QT == KQ_Q6_K) {
+        o[e] = a[g] * (bf16_lo(pr[i]) - 160.0f);
+        o[e + 1] = a[g] * (bf16_hi(pr[i]) - 160.0f);
+      } else {
+        o[e] = __builtin_fmaf(a[g], bf16_lo(pr[i]) - 128.0f, -cm[g]);
+        o[e + 1] = __builtin_fmaf(a[g], bf16_hi(pr[i]) - 128.0f, -cm[g]);
+      }
+    }
+  }
+}
+
 template <int QT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
                                                       int64_t rows, int n_cols, int64_t total, int64_t ldo) {
-  using F = Fmt<QT>;
   const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
   for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
     const int lane = (int)(gid & 63);
@@ -178,33 +208,31 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
     const int64_t t = unit / n_cols;
     const int c = (int)(unit - t * n_cols);
     const int64_t row = t * kTileRows + lane;
-    const uint8_t* tb = w + unit * tile_bytes<QT>();
-    u32x4 ch[F::kChunks];
-#pragma unroll
-    for (int k = 0; k < F::kChunks; ++k)
-      ch[k] = *reinterpret_cast<const u32x4*>(tb + k * kChunkStride + lane * kChunk);
-    uint32_t d6 = 0;
-    if constexpr (QT == KQ_Q6_K) d6 = reinterpret_cast<const uint16_t*>(tb + 13 * kChunkStride)[lane];
-    float a[F::kSubBlocks], cm[F::kSubBlocks];
-    sb_coeffs<QT>(ch, d6, 1.0f, a, cm);
     if (row >= rows) continue;
-    float* o = out + row * ldo + (int64_t)c * 256;
-#pragma unroll
-    for (int g = 0; g < F::kSubBlocks; ++g) {
-      uint32_t pr[F::kPairs];
-      unpack_pairs<QT>(ch, g, M, K, pr);
-#pragma unroll
-      for (int i = 0; i < F::kPairs; ++i) {
-        const int e = g * F::kSubW + 2 * i;
-        if constexpr (QT == KQ_Q6_K) {
-          o[e] = a[g] * (bf16_lo(pr[i]) - 160.0f);
-          o[e + 1] = a[g] * (bf16_hi(pr[i]) - 160.0f);
-        } else {
-          o[e] = __builtin_fmaf(a[g], bf16_lo(pr[i]) - 128.0f, -cm[g]);
-          o[e + 1] = __builtin_fmaf(a[g], bf16_hi(pr[i]) - 128.0f, -cm[g]);
-        }
-      }
+    dequant_superblock<QT>(w + unit * tile_bytes<QT>(), lane, out + row * ldo + (int64_t)c * 256, M, K);
+  }
+}
+
+// Row gather (the embedding lookup): out[i*ldo + k] = dequant(W)[ids[i], k] for
+// i < n, one thread per (i, super-block column).  An id outside [0, rows) gives
+// a row of quiet NaNs and reads nothing.  (One thread per sub-block measured
+// slower for a single token.)
+template <int QT>
+__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ w, const int32_t* __restrict__ ids,
+                                                     float* __restrict__ out, int64_t rows, int n_cols, int64_t total,
+                                                     int64_t ldo) {
+  const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+    const int64_t i = gid / n_cols;
+    const int c = (int)(gid - i * n_cols);
+    const int64_t row = ids[i];
+    float* o = out + i * ldo + (int64_t)c * 256;
+    if (row < 0 || row >= rows) {
+      for (int e = 0; e < 256; ++e) o[e] = __builtin_nanf("");
+      continue;
     }
+    const int64_t t = row / kTileRows;
+    dequant_superblock<QT>(w + (t * n_cols + c) * tile_bytes<QT>(), (int)(row - t * kTileRows), o, M, K);
   }
 }
 
@@ -237,6 +265,20 @@ hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, f
     case KQ_Q4_K: hipLaunchKernelGGL(dequant_kernel<KQ_Q4_K>, dim3(grid_for(total)), dim3(256), 0, s, in, out, rows, n_cols, total, ldo); break;
     case KQ_Q5_K: hipLaunchKernelGGL(dequant_kernel<KQ_Q5_K>, dim3(grid_for(total)), dim3(256), 0, s, in, out, rows, n_cols, total, ldo); break;
     case KQ_Q6_K: hipLaunchKernelGGL(dequant_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, out, rows, n_cols, total, ldo); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int type, const void* w, int64_t rows, int64_t cols, const int32_t* ids, int64_t n,
+                         float* out, int64_t ldo, hipStream_t s) {
+  const int n_cols = (int)(cols / 256);
+  const int64_t total = n * n_cols;
+  const uint8_t* in = static_cast<const uint8_t*>(w);
+  switch (type) {
+    case KQ_Q4_K: hipLaunchKernelGGL(gather_kernel<KQ_Q4_K>, dim3(grid_for(total)), dim3(256), 0, s, in, ids, out, rows, n_cols, total, ldo); break;
+    case KQ_Q5_K: hipLaunchKernelGGL(gather_kernel<KQ_Q5_K>, dim3(grid_for(total)), dim3(256), 0, s, in, ids, out, rows, n_cols, total, ldo); break;
+    case KQ_Q6_K: hipLaunchKernelGGL(gather_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, ids, out, rows, n_cols, total, ldo); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -25,7 +25,7 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4:
           10: "KQ_ERR_DEVICE"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
-           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant", "kq_chain_create", "kq_chain_run",
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant", "kq_gather_rows", "kq_chain_create", "kq_chain_run",
            "kq_chain_status", "kq_chain_destroy")
 
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_multi.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
+        L.kq_gather_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, vp]
+        L.kq_gather_rows.restype = ci
         L.kq_chain_create.argtypes = [ci, ctypes.POINTER(ChainStep), ci, ci, ctypes.POINTER(vp)]
         L.kq_chain_create.restype = ci
         for n in ("kq_chain_status", "kq_chain_destroy"):
@@ -161,6 +163,14 @@ def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, 
                                           _stream(stream)))
 
 
+def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tensor, out: torch.Tensor,
+                   stream=None) -> None:
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    _check("kq_gather_rows", lib().kq_gather_rows(_type(qtype), w.data_ptr(), rows, cols, ids.data_ptr(), ids.numel(),
+                                                  out.data_ptr(), out.stride(0), _stream(stream)))
+
+
 def kq_chain_create(steps, xtype: int, batch: int) -> int:
     """steps: sequence of (qtype, ws, rows, cols, x, ys) as kq_gemv_multi takes them; returns the handle."""
     arr = (ChainStep * len(steps))()
@@ -236,6 +246,12 @@ def gemv(qtype: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: 
         y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=x.device)
     GEMV[qtype](w, rows, cols, x, y, stream)
     return y
+
+
+def gather_rows(qtype: str, w: torch.Tensor, rows: int, cols: int, ids: torch.Tensor, stream=None) -> torch.Tensor:
+    out = torch.empty((ids.numel(), cols), dtype=torch.float32, device=w.device)
+    kq_gather_rows(qtype, w, rows, cols, ids, out, stream)
+    return out
 
 
 def dequant(qtype: str, w: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:

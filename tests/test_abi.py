@@ -138,3 +138,19 @@ def test_chain_other_rejects():
     assert L.kq_chain_status(None) == 1
     assert L.kq_chain_destroy(None) == 0
     assert L.kq_status_str(9) == b"a chain step's wait for the previous step gave up"
+
+
+def test_gather_rejects():
+    L = kq.lib()
+    ids = A16
+    assert L.kq_gather_rows(9, A16, 64, 256, ids, 4, A16, 256, None) == 5       # type
+    assert L.kq_gather_rows(1, None, 64, 256, ids, 4, A16, 256, None) == 1      # w
+    assert L.kq_gather_rows(1, A16, 64, 256, None, 4, A16, 256, None) == 1      # ids
+    assert L.kq_gather_rows(1, A16, 64, 256, ids, 4, None, 256, None) == 1      # out
+    assert L.kq_gather_rows(1, A16, 64, 300, ids, 4, A16, 300, None) == 2       # cols % 256
+    assert L.kq_gather_rows(1, A16, 0, 256, ids, 4, A16, 256, None) == 2        # rows
+    assert L.kq_gather_rows(1, A16, 64, 256, ids, 4, A16, 128, None) == 2       # ldo < cols
+    assert L.kq_gather_rows(1, A16 + 4, 64, 256, ids, 4, A16, 256, None) == 3   # w alignment
+    assert L.kq_gather_rows(1, A16, 64, 256, ids + 2, 4, A16, 256, None) == 3   # ids alignment
+    assert L.kq_gather_rows(1, A16, 64, 256, ids, -1, A16, 256, None) == 4      # n < 0
+    assert L.kq_gather_rows(1, A16, 64, 256, None, 0, None, 256, None) == 0     # n = 0: nothing to do
