@@ -175,6 +175,42 @@ def time_gather(rows: int, cols: int, batches, reps: int = 64) -> dict:
     return out
 
 
+def time_swiglu(inter: int, cols: int, batches, copies: int = 6, reps: int = 4) -> dict:
+    """Mean launch time of gate+up with the SwiGLU epilogue (kq_gemv_swiglu, Q4_K, one intermediate-size
+    output), over `copies` distinct weight pairs so no launch reads another's weights from cache."""
+    import torch
+    from quant_weight_streaming_amd import kq, synth
+    ws = []
+    for i in range(copies):
+        gate = synth.gen_weights("q4k", inter, cols, synth.seed_of("bench-swiglu", i, "gate"), device="cuda:0")
+        up = synth.gen_weights("q4k", inter, cols, synth.seed_of("bench-swiglu", i, "up"), device="cuda:0")
+        ws.append(kq.repack_swiglu("q4k", gate, up, inter, cols))
+        del gate, up
+    out = {}
+    for B in batches:
+        x = synth.gen_x(B, cols, synth.seed_of("bench-swiglu-x", B), device="cuda:0")
+        y = torch.empty((B, inter), device="cuda:0")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            kq.kq_gemv_swiglu("q4k", ws[0], inter, cols, x, y, s)
+            with torch.cuda.graph(graph, stream=s):
+                for w in ws:
+                    kq.kq_gemv_swiglu("q4k", w, inter, cols, x, y, s)
+        torch.cuda.current_stream().wait_stream(s)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"b{B}"] = round(e0.elapsed_time(e1) * 1e3 / (reps * copies), 2)
+    return out
+
+
 def run_calls(calls):
     for fn, args, name in calls:
         rc = fn(*args)
@@ -489,6 +525,9 @@ def main():
     kt1 = kernel_times(sw, 1)
     kt8 = kernel_times(sw, 8)
     cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
+    swiglu_us = time_swiglu(synth.INTER, synth.HIDDEN, (1, 8))
+    log(f"[bench] gate+up with SwiGLU epilogue (Q4_K 2 x {synth.INTER}x{synth.HIDDEN}): {swiglu_us} us "
+        f"(plain gate+up: {kt1['gate_up']['avg_us']} / {kt8['gate_up']['avg_us']} us)")
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads over {cpu['seconds']} s")
 
@@ -583,6 +622,7 @@ def main():
         "batch1_all": {"chain_ms": round(res[1]["chain_ms"], 4), "graph_ms": round(res[1]["graph_ms"], 4),
                        "plain_ms": round(res[1]["plain_ms"], 4),
                        "graph_weight_gbs": round(weight_gbs(bytes3, res[1]["graph_ms"]), 1)},
+        "gate_up_swiglu_epilogue_us": swiglu_us,
         "kernels_b1": kt1,
         "kernels_b8": kt8,
         "c4_q5k_merged": c4,

@@ -65,6 +65,10 @@ extern "C" {
 #define KQ_MAX_BATCH 8
 #define KQ_MAX_PROJ 8
 
+/* epilogues */
+#define KQ_EPI_NONE 0
+#define KQ_EPI_SWIGLU 1
+
 /* status codes */
 #define KQ_OK 0
 #define KQ_ERR_NULL 1   /* a required pointer is NULL */
@@ -147,6 +151,28 @@ int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, in
 int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
 
 /*
+ * SwiGLU epilogue: the gate and up projections of the feed-forward block in one
+ * launch whose output is already the block's hidden activation,
+ *     y[b*ldy + r] = silu(g) * u,  g = sum_k Wg[r, k] x[b, k],  u = sum_k Wu[r, k] x[b, k],
+ * silu(g) = g / (1 + exp(-g)), r < inter (the SwiGLU feed-forward of "Muse-
+ * Glimmer-30B (text decoder) - Apple Core AI", section "The architecture, and
+ * what the port had to do about it"; fusing the gate+up epilogue halves the
+ * launch's output and removes the activation pass).
+ * kq_repack_swiglu packs the pair so that 64-row tile t holds rows 32t..32t+31
+ * of the gate matrix followed by the same rows of the up matrix:
+ *   gate, up : device GGUF super-blocks, inter x cols each (alignment as kq_repack).
+ *   out      : device, kq_repacked_bytes(type, 64 * ceil(inter / 32), cols) bytes,
+ *              16-byte aligned; rows past inter are zero.
+ * kq_gemv_swiglu then takes that buffer (w) with the same inter and cols; x, y
+ * and the other arguments as kq_gemv_q4k.  Deterministic; y is within the GEMV
+ * tolerance of g and u carried through silu(g) * u (see the tests).
+ */
+int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void *gate, const void *up, void *out,
+                     void *stream);
+int kq_gemv_swiglu(int type, const void *w, int64_t inter, int64_t cols, const void *x, int xtype, int64_t ldx,
+                   int batch, float *y, int64_t ldy, void *stream);
+
+/*
  * Row gather: the embedding lookup of a token, the step before layer 0 of a
  * decoder whose embedding is a K-quant matrix of its own (an untied vocabulary
  * table: "Muse-Glimmer-30B (text decoder) - Apple Core AI", section "The
@@ -188,6 +214,8 @@ typedef struct kq_chain_step {
   int64_t ldy[KQ_MAX_PROJ];       /* output row strides (elements), >= rows */
   const void *x;                  /* device activations, batch rows of stride ldx */
   int64_t ldx;                    /* activation row stride (elements), >= cols */
+  int32_t epilogue;               /* KQ_EPI_NONE, or KQ_EPI_SWIGLU: n = 1, w from kq_repack_swiglu, rows[0] = inter */
+  int32_t reserved;               /* set to 0 */
 } kq_chain_step;
 
 typedef struct kq_chain kq_chain;

@@ -10,6 +10,8 @@ Functions:
                                         or w = d*sc*(q-32) (Q6_K), [rows, cols]
   dequant_f32(...)                      the same rounded once to fp32 (RNE)
   gemv(qtype, rows, cols, gguf, x)      y = W x^T and a = sum |w x| in fp64, [batch, rows]
+  silu(g), swiglu(g, u)                 the SwiGLU feed-forward's activation in fp64
+  gather(qtype, rows, cols, gguf, ids)  rows ids of dequant_f32 (the embedding lookup)
 """
 from __future__ import annotations
 
@@ -129,3 +131,23 @@ def dequant_f32(qtype, rows, cols, gguf):
 
 def gemv(qtype, rows, cols, gguf, x):
     return default().gemv(qtype, rows, cols, gguf, x)
+
+
+def silu(g):
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), in fp64: the gate activation of the SwiGLU
+    feed-forward named on the "Muse-Glimmer-30B (text decoder) - Apple Core AI" card (section "The
+    architecture, and what the port had to do about it"); the pages name it without a formula, and this
+    is the standard one.  exp(-g) overflows to inf for g < -709, which gives -0 as the limit."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(g, u):
+    """The SwiGLU hidden activation silu(g) * u for gate output g and up output u, in fp64."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def gather(qtype, rows, cols, gguf, ids):
+    """The embedding lookup: rows `ids` of the fp32 dequantised matrix."""
+    return dequant_f32(qtype, rows, cols, gguf)[np.asarray(ids)]

@@ -163,11 +163,14 @@ struct Plan {
 
 // Launch geometry of a validated call on a device with `cus` CUs, using at most
 // `max_grid` workgroups (a multiple of 8).
+// epi == KQ_EPI_SWIGLU: one matrix (n == 1) from kq_repack_swiglu, rows[0] =
+// the intermediate size, 32 outputs per 64-row tile.
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
-                     int64_t max_grid, int force_nw, float* partial, uint32_t* counters, Plan* out) {
+                     int64_t max_grid, int force_nw, int epi, float* partial, uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
   GemvArgs a{};
+  a.epi = epi;
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) {
     if (rows[i] > (int64_t)INT32_MAX - 64) return KQ_ERR_RANGE;
@@ -176,7 +179,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     a.ldy[i] = ldy[i];
     a.rows[i] = (int32_t)rows[i];
     a.tile_begin[i] = (int32_t)tiles;
-    tiles += (rows[i] + 63) / 64;
+    tiles += epi == KQ_EPI_SWIGLU ? (rows[i] + 31) / 32 : (rows[i] + 63) / 64;
     if (tiles > INT32_MAX) return KQ_ERR_RANGE;
   }
   for (int i = n; i <= KQ_MAX_PROJ; ++i) a.tile_begin[i] = (int32_t)tiles;
@@ -270,7 +273,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
 }
 
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
-                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream) {
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream,
+                     int epi = KQ_EPI_NONE) {
   int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
   if (rc != KQ_OK) return rc;
   int dev = 0;
@@ -279,10 +283,10 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
   Plan p{};
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, st->partial,
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, st->partial,
                  st->counters, &p);
   if (rc == KQ_ERR_RANGE && wg_waves(batch) == 8)   // too many units per workgroup for per-unit slots: 4-wavefront runs
-    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, st->partial,
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, st->partial,
                    st->counters, &p);
   if (rc != KQ_OK) return rc;
   if (launch_gemv(type, xtype, batch, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
@@ -371,8 +375,28 @@ int kq_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out,
   if (rows < 1 || cols <= 0 || cols % 256 != 0) return KQ_ERR_SHAPE;
   if (!aligned(out, 16) || !aligned(gguf, type == KQ_Q6_K ? 2 : 4)) return KQ_ERR_ALIGN;
   if (rows > (int64_t)INT32_MAX - 64 || cols / 256 > INT32_MAX) return KQ_ERR_RANGE;
-  if (launch_repack(type, rows, cols, gguf, out, static_cast<hipStream_t>(stream)) != hipSuccess) return KQ_ERR_HIP;
+  if (launch_repack(type, rows, cols, gguf, nullptr, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KQ_ERR_HIP;
   return KQ_OK;
+}
+
+int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void* gate, const void* up, void* out,
+                     void* stream) {
+  if (!sb_bytes(type)) return KQ_ERR_TYPE;
+  if (!gate || !up || !out) return KQ_ERR_NULL;
+  if (inter < 1 || cols <= 0 || cols % 256 != 0) return KQ_ERR_SHAPE;
+  const int align = type == KQ_Q6_K ? 2 : 4;
+  if (!aligned(out, 16) || !aligned(gate, align) || !aligned(up, align)) return KQ_ERR_ALIGN;
+  if (inter > (int64_t)INT32_MAX / 2 - 64 || cols / 256 > INT32_MAX) return KQ_ERR_RANGE;
+  if (launch_repack(type, inter, cols, gate, up, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,
+                   int batch, float* y, int64_t ldy, void* stream) {
+  if (inter > (int64_t)INT32_MAX / 2 - 64) return KQ_ERR_RANGE;
+  return gemv_impl(type, 1, &w, &inter, cols, x, xtype, ldx, batch, &y, &ldy, stream, KQ_EPI_SWIGLU);
 }
 
 int kq_gemv_q4k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
@@ -434,6 +458,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     const kq_chain_step& st = steps[j];
     const int rc = validate(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy);
     if (rc != KQ_OK) return rc;
+    if (st.epilogue != KQ_EPI_NONE && (st.epilogue != KQ_EPI_SWIGLU || st.n != 1)) return KQ_ERR_TYPE;
     if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
   int dev = 0;
@@ -453,7 +478,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     for (int j = 0; j < n_steps; ++j) {
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
-                         max_grid, nw, nullptr, nullptr, &plans[j]);
+                         max_grid, nw, st.epilogue, nullptr, nullptr, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;

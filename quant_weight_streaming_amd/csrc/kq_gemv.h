@@ -425,6 +425,25 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
 // through to the device coherence point (read later in the same launch).
 template <int B, bool COH, class GA>
 __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* v) {
+  if (a.epi == KQ_EPI_SWIGLU) {
+    // lanes 0..31 hold the gate sums of outputs 32t .. 32t+31, lanes 32..63
+    // the up sums of the same outputs: y = silu(gate) * up
+    float u[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) u[b] = __shfl(v[b], lane + 32);
+    const int row = t * (kTileRows / 2) + lane;
+    if (lane < 32 && row < a.rows[0]) {
+      float* y = a.y[0];
+      const int64_t ldy = a.ldy[0];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float h = v[b] / (1.0f + expf(-v[b])) * u[b];
+        if constexpr (COH) __hip_atomic_store(y + b * ldy + row, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else y[b * ldy + row] = h;
+      }
+    }
+    return;
+  }
   int p = 0;
 #pragma unroll
   for (int i = 1; i < KQ_MAX_PROJ; ++i)

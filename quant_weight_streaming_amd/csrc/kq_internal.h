@@ -24,6 +24,7 @@ struct GemvArgs {
   int32_t upw;                         // units per wavefront
   int32_t tsb;                         // LDS capacity in staged columns per workgroup
   int32_t tpw;                         // tiles a wavefront's run of units can touch (its LDS tile sums)
+  int32_t epi;                         // KQ_EPI_NONE, or KQ_EPI_SWIGLU: tile t holds 32 gate and 32 up rows
   // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
   // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even
@@ -91,7 +92,8 @@ inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, in
   const int xwords = xtype == KQ_X_F32 ? 256 : 128;
   return (size_t)staged_cols * batch * 4 * (xwords + sb) + partials;
 }
-hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s);
+hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, const void* gguf2, void* out,
+                         hipStream_t s);
 hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo,
                           hipStream_t s);
 hipError_t launch_gather(int type, const void* w, int64_t rows, int64_t cols, const int32_t* ids, int64_t n,

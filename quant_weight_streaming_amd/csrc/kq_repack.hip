@@ -139,20 +139,28 @@ template <> struct Repack<KQ_Q6_K> {
   }
 };
 
+// gguf2 == nullptr: tile t holds rows 64t .. 64t+63 of gguf.  Otherwise (the
+// SwiGLU pair) tile t holds rows 32t .. 32t+31 of gguf (gate) in lanes 0..31
+// and the same rows of gguf2 (up) in lanes 32..63.  Rows past `rows` are zero.
 template <int QT>
-__global__ void __launch_bounds__(256) repack_kernel(const uint8_t* __restrict__ gguf, uint8_t* __restrict__ out,
-                                                     int64_t rows, int n_cols, int64_t total) {
+__global__ void __launch_bounds__(256) repack_kernel(const uint8_t* __restrict__ gguf, const uint8_t* __restrict__ gguf2,
+                                                     uint8_t* __restrict__ out, int64_t rows, int n_cols, int64_t total) {
   using F = Fmt<QT>;
   for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
     const int lane = (int)(gid & 63);
     const int64_t unit = gid >> 6;               // tile * n_cols + column
     const int64_t t = unit / n_cols;
     const int c = (int)(unit - t * n_cols);
-    const int64_t row = t * kTileRows + lane;
+    const uint8_t* src = gguf;
+    int64_t row = t * kTileRows + lane;
+    if (gguf2) {
+      row = t * (kTileRows / 2) + (lane & 31);
+      if (lane >= 32) src = gguf2;
+    }
     u32x4 ch[F::kChunks];
     uint16_t d6 = 0;
     if (row < rows) {
-      Repack<QT>::run(gguf + (row * n_cols + c) * F::kSbBytes, ch, d6);
+      Repack<QT>::run(src + (row * n_cols + c) * F::kSbBytes, ch, d6);
     } else {
 #pragma unroll
       for (int k = 0; k < F::kChunks; ++k) ch[k] = u32x4{0u, 0u, 0u, 0u};
@@ -165,8 +173,6 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint8_t* __restrict__
   }
 }
 
-// out[row*ldo + 256c + e] = fp32 dequantised weight, from the repacked layout,
-// through the same unpacking the GEMV uses.
 // fp32 dequantisation of one super-block (row 64t + lane, column c) of the
 // repacked layout, whose unit starts at `tb`, into o[0..255].
 template <int QT>
@@ -198,6 +204,8 @@ __device__ __forceinline__ void dequant_superblock(const uint8_t* tb, int lane, 
   }
 }
 
+// out[row*ldo + 256c + e] = fp32 dequantised weight, from the repacked layout,
+// through the same unpacking the GEMV uses.
 template <int QT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
                                                       int64_t rows, int n_cols, int64_t total, int64_t ldo) {
@@ -241,16 +249,18 @@ static int grid_for(int64_t total) {
   return (int)(g < 65536 ? (g > 0 ? g : 1) : 65536);
 }
 
-hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, void* out, hipStream_t s) {
+hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, const void* gguf2, void* out,
+                         hipStream_t s) {
   const int n_cols = (int)(cols / 256);
-  const int64_t n_tiles = (rows + kTileRows - 1) / kTileRows;
+  const int64_t n_tiles = gguf2 ? (rows + kTileRows / 2 - 1) / (kTileRows / 2) : (rows + kTileRows - 1) / kTileRows;
   const int64_t total = n_tiles * n_cols * kTileRows;
   const uint8_t* in = static_cast<const uint8_t*>(gguf);
+  const uint8_t* in2 = static_cast<const uint8_t*>(gguf2);
   uint8_t* o = static_cast<uint8_t*>(out);
   switch (type) {
-    case KQ_Q4_K: hipLaunchKernelGGL(repack_kernel<KQ_Q4_K>, dim3(grid_for(total)), dim3(256), 0, s, in, o, rows, n_cols, total); break;
-    case KQ_Q5_K: hipLaunchKernelGGL(repack_kernel<KQ_Q5_K>, dim3(grid_for(total)), dim3(256), 0, s, in, o, rows, n_cols, total); break;
-    case KQ_Q6_K: hipLaunchKernelGGL(repack_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, o, rows, n_cols, total); break;
+    case KQ_Q4_K: hipLaunchKernelGGL(repack_kernel<KQ_Q4_K>, dim3(grid_for(total)), dim3(256), 0, s, in, in2, o, rows, n_cols, total); break;
+    case KQ_Q5_K: hipLaunchKernelGGL(repack_kernel<KQ_Q5_K>, dim3(grid_for(total)), dim3(256), 0, s, in, in2, o, rows, n_cols, total); break;
+    case KQ_Q6_K: hipLaunchKernelGGL(repack_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, in2, o, rows, n_cols, total); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

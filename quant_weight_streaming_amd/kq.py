@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkq.so")
 KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 1, 2, 3
 KQ_X_F32, KQ_X_BF16 = 0, 1
 KQ_MAX_BATCH, KQ_MAX_PROJ = 8, 8
+KQ_EPI_NONE, KQ_EPI_SWIGLU = 0, 1
 TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
@@ -25,7 +26,8 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4:
           10: "KQ_ERR_DEVICE"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
-           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant", "kq_gather_rows", "kq_chain_create", "kq_chain_run",
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant", "kq_gather_rows", "kq_repack_swiglu",
+           "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
            "kq_chain_status", "kq_chain_destroy")
 
 
@@ -34,7 +36,8 @@ class ChainStep(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int32), ("n", ctypes.c_int32), ("cols", ctypes.c_int64),
                 ("w", ctypes.c_void_p * KQ_MAX_PROJ), ("rows", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
-                ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64)]
+                ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("epilogue", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class KQError(RuntimeError):
@@ -74,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.kq_dequant.restype = ci
         L.kq_gather_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, vp]
         L.kq_gather_rows.restype = ci
+        L.kq_repack_swiglu.argtypes = [ci, i64, i64, vp, vp, vp, vp]
+        L.kq_repack_swiglu.restype = ci
+        L.kq_gemv_swiglu.argtypes = [ci, vp, i64, i64, vp, ci, i64, ci, vp, i64, vp]
+        L.kq_gemv_swiglu.restype = ci
         L.kq_chain_create.argtypes = [ci, ctypes.POINTER(ChainStep), ci, ci, ctypes.POINTER(vp)]
         L.kq_chain_create.restype = ci
         for n in ("kq_chain_status", "kq_chain_destroy"):
@@ -163,6 +170,19 @@ def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, 
                                           _stream(stream)))
 
 
+def kq_repack_swiglu(qtype, inter: int, cols: int, gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor,
+                     stream=None) -> None:
+    _check("kq_repack_swiglu", lib().kq_repack_swiglu(_type(qtype), inter, cols, gate.data_ptr(), up.data_ptr(),
+                                                      out.data_ptr(), _stream(stream)))
+
+
+def kq_gemv_swiglu(qtype, w: torch.Tensor, inter: int, cols: int, x: torch.Tensor, y: torch.Tensor,
+                   stream=None) -> None:
+    _check("kq_gemv_swiglu", lib().kq_gemv_swiglu(_type(qtype), w.data_ptr(), inter, cols, x.data_ptr(), _xtype(x),
+                                                  x.stride(0), x.shape[0], y.data_ptr(), y.stride(0),
+                                                  _stream(stream)))
+
+
 def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tensor, out: torch.Tensor,
                    stream=None) -> None:
     if ids.dtype != torch.int32:
@@ -174,7 +194,9 @@ def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tens
 def kq_chain_create(steps, xtype: int, batch: int) -> int:
     """steps: sequence of (qtype, ws, rows, cols, x, ys) as kq_gemv_multi takes them; returns the handle."""
     arr = (ChainStep * len(steps))()
-    for st, (qtype, ws, rows, cols, x, ys) in zip(arr, steps):
+    for st, step in zip(arr, steps):
+        qtype, ws, rows, cols, x, ys = step[:6]
+        st.epilogue = step[6] if len(step) > 6 else KQ_EPI_NONE
         n = len(ws)
         if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ:
             raise ValueError("ws, rows and ys must have the same length, at most KQ_MAX_PROJ")
@@ -245,6 +267,21 @@ def gemv(qtype: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: 
     if y is None:
         y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=x.device)
     GEMV[qtype](w, rows, cols, x, y, stream)
+    return y
+
+
+def repack_swiglu(qtype: str, gate: torch.Tensor, up: torch.Tensor, inter: int, cols: int, stream=None) -> torch.Tensor:
+    """GGUF bytes of the gate and up matrices on the device -> the interleaved repacked pair."""
+    out = torch.empty(kq_repacked_bytes(qtype, 64 * ((inter + 31) // 32), cols), dtype=torch.uint8, device=gate.device)
+    kq_repack_swiglu(qtype, inter, cols, gate, up, out, stream)
+    return out
+
+
+def gemv_swiglu(qtype: str, w: torch.Tensor, inter: int, cols: int, x: torch.Tensor, y: torch.Tensor = None,
+                stream=None) -> torch.Tensor:
+    if y is None:
+        y = torch.empty((x.shape[0], inter), dtype=torch.float32, device=x.device)
+    kq_gemv_swiglu(qtype, w, inter, cols, x, y, stream)
     return y
 
 

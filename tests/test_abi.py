@@ -154,3 +154,29 @@ def test_gather_rejects():
     assert L.kq_gather_rows(1, A16, 64, 256, ids + 2, 4, A16, 256, None) == 3   # ids alignment
     assert L.kq_gather_rows(1, A16, 64, 256, ids, -1, A16, 256, None) == 4      # n < 0
     assert L.kq_gather_rows(1, A16, 64, 256, None, 0, None, 256, None) == 0     # n = 0: nothing to do
+
+
+def test_swiglu_rejects():
+    L = kq.lib()
+    assert L.kq_repack_swiglu(9, 64, 256, A16, A16, A16, None) == 5
+    assert L.kq_repack_swiglu(1, 64, 256, None, A16, A16, None) == 1
+    assert L.kq_repack_swiglu(1, 64, 256, A16, None, A16, None) == 1
+    assert L.kq_repack_swiglu(1, 0, 256, A16, A16, A16, None) == 2
+    assert L.kq_repack_swiglu(1, 64, 300, A16, A16, A16, None) == 2
+    assert L.kq_repack_swiglu(1, 64, 256, A16, A16, A16 + 4, None) == 3
+    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 256, 9, A16, 64, None) == 4
+    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 128, 1, A16, 64, None) == 2
+    assert L.kq_gemv_swiglu(1, None, 64, 256, A16, 1, 256, 1, A16, 64, None) == 1
+
+
+def test_chain_rejects_bad_epilogue():
+    bad = _step()
+    bad.epilogue = 7
+    arr = (kq.ChainStep * 1)(bad)
+    h = ctypes.c_void_p()
+    assert kq.lib().kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 5
+    two = _step(n=2)
+    two.w[1], two.rows[1], two.y[1], two.ldy[1] = A16, 64, A16, 64
+    two.epilogue = 1                              # SwiGLU takes one matrix
+    arr = (kq.ChainStep * 1)(two)
+    assert kq.lib().kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 5

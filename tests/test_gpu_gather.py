@@ -21,7 +21,7 @@ def test_gather_matches_dequant(qtype):
     ids = np.array([0, rows - 1, 64, 63, 7, 7, rows - 11, 200, 0, 321, 65], dtype=np.int32)
     out = kq.gather_rows(qtype, w, rows, cols, torch.as_tensor(ids, device=DEV))
     torch.cuda.synchronize()
-    want = O.dequant_f32(qtype, rows, cols, g.numpy())[ids]
+    want = O.gather(qtype, rows, cols, g.numpy(), ids)
     got = out.cpu().numpy()
     bad = got != want
     assert not bad.any(), f"{int(bad.sum())} gathered weights differ from the oracle, first at {np.argwhere(bad)[0]}"

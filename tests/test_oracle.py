@@ -1,5 +1,7 @@
 """The CPU oracle against its pins, and the pins against planted mistakes."""
 import os
+
+import numpy as np
 import shutil
 import tempfile
 
@@ -62,3 +64,24 @@ def test_pins_catch_planted_mistake(name, orig, mut):
         assert caught, f"no pin caught mutant '{name}'"
     finally:
         shutil.rmtree(d, ignore_errors=True)
+
+
+def test_silu_closed_forms():
+    """silu pins that do not retype its formula: silu(0) = 0, the odd part silu(g) - silu(-g) = g,
+    sigmoid(ln 3) = 3/4 so silu(ln 3) = 0.75 ln 3, the limits g and 0, and swiglu(g, u) = silu(g) u."""
+    import math
+    assert O.silu(0.0) == 0.0
+    g = np.linspace(-30.0, 30.0, 601)
+    assert np.allclose(O.silu(g) - O.silu(-g), g, rtol=0, atol=1e-13)
+    assert abs(O.silu(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+    assert O.silu(800.0) == 800.0 and O.silu(-800.0) == 0.0
+    assert abs(O.silu(40.0) - 40.0) < 1e-14 and abs(O.silu(-40.0)) < 1e-15
+    assert np.array_equal(O.swiglu(g, 2.0 * np.ones_like(g)), 2.0 * O.silu(g))
+
+
+def test_gather_is_rows_of_dequant():
+    from quant_weight_streaming_amd import synth
+    g = synth.gen_weights("q4k", 70, 512, 5).numpy()
+    ids = [69, 0, 64, 5, 5]
+    full = O.dequant_f32("q4k", 70, 512, g)
+    assert np.array_equal(O.gather("q4k", 70, 512, g, ids), full[ids])
