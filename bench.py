@@ -513,7 +513,8 @@ def main():
         frac = min(1.0, args.cpu_seconds * rate * 1e9 / synth.sweep_bytes("q4k"))
         log(f"[bench] oracle probe {rate:.3f} GB/s -> sample fraction {frac:.3f}")
 
-    sw = Sweep(3, "q4k", (1, 8), 0.0, frac)
+    VERIFY = (2, 3, 4, 12, 16)     # speculative-verify block sizes for the cost staircase
+    sw = Sweep(3, "q4k", (1, 8) + VERIFY, 0.0, frac)
     res = {}
     for B in (1, 8):
         plain, graph = time_sweep(sw, B, args.steps, args.warmup)
@@ -522,6 +523,18 @@ def main():
         log(f"[bench] cfg3 B={B}: plain {plain:.3f} ms ({sw.weight_bytes / plain / 1e6:.0f} GB/s), "
             f"graph {graph:.3f} ms ({sw.weight_bytes / graph / 1e6:.0f} GB/s), "
             f"chain {chain:.3f} ms ({sw.weight_bytes / chain / 1e6:.0f} GB/s)")
+    # verify cost: the sweep at S rows per call (a speculative block verified in one forward)
+    for B in VERIFY:
+        plain, graph = time_sweep(sw, B, max(3, args.steps // 2), args.warmup)
+        chain = time_chain(sw, B, max(3, args.steps // 2), args.warmup)
+        res[B] = dict(plain_ms=plain, graph_ms=graph, chain_ms=chain)
+    stair = {}
+    t1 = min(res[1]["graph_ms"], res[1]["chain_ms"])
+    for B in sorted(res):
+        t = min(res[B]["graph_ms"], res[B]["chain_ms"])
+        stair[str(B)] = dict(ms=round(t, 4), vs_one_row=round(t / t1, 3), rows_per_s=round(tok_s(t, B), 1))
+    log("[bench] verify cost (sweep time at S rows / at 1 row): " +
+        ", ".join(f"S={k}: {v['vs_one_row']}x" for k, v in stair.items()))
     kt1 = kernel_times(sw, 1)
     kt8 = kernel_times(sw, 8)
     cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
@@ -622,6 +635,7 @@ def main():
         "batch1_all": {"chain_ms": round(res[1]["chain_ms"], 4), "graph_ms": round(res[1]["graph_ms"], 4),
                        "plain_ms": round(res[1]["plain_ms"], 4),
                        "graph_weight_gbs": round(weight_gbs(bytes3, res[1]["graph_ms"]), 1)},
+        "verify_cost_staircase": stair,
         "gate_up_swiglu_epilogue_us": swiglu_us,
         "kernels_b1": kt1,
         "kernels_b8": kt8,

@@ -4,7 +4,7 @@
  * The operation is the decode-step matrix-vector product over GGUF K-quant
  * weights,
  *
- *     y[b, r] = sum_k dequant(W)[r, k] * x[b, k]        for b < batch <= 8,
+ *     y[b, r] = sum_k dequant(W)[r, k] * x[b, k]        for b < batch <= 16,
  *
  * where every generated token streams the whole quantised decoder through it
  * once.  Sources for what is computed:
@@ -62,7 +62,13 @@ extern "C" {
 #define KQ_X_F32 0
 #define KQ_X_BF16 1
 
-#define KQ_MAX_BATCH 8
+/* batch rows per call: up to 16 with bf16 activations (one speculative-verify
+ * block: the drafter proposes blocks of 16 tokens and the runner accepts block
+ * lengths 2..16, "Muse Glimmer 30B - ExecuTorch PTE" card, paragraph "Faster
+ * Generation Through Speculative Decoding" and "Adjustments per variant"), up
+ * to 8 with fp32 */
+#define KQ_MAX_BATCH 16
+#define KQ_MAX_BATCH_F32 8
 #define KQ_MAX_PROJ 8
 
 /* epilogues */
@@ -74,7 +80,7 @@ extern "C" {
 #define KQ_ERR_NULL 1   /* a required pointer is NULL */
 #define KQ_ERR_SHAPE 2  /* rows < 1, cols not a positive multiple of 256, ldx < cols, ldy < rows, ... */
 #define KQ_ERR_ALIGN 3  /* w / x not 16-byte aligned, y not 4-byte aligned, or row stride of x not 16 B */
-#define KQ_ERR_BATCH 4  /* batch outside 1..KQ_MAX_BATCH, or n outside 1..KQ_MAX_PROJ */
+#define KQ_ERR_BATCH 4  /* batch outside 1..KQ_MAX_BATCH (KQ_MAX_BATCH_F32 for fp32 x), or n outside 1..KQ_MAX_PROJ */
 #define KQ_ERR_TYPE 5   /* unknown weight or activation format */
 #define KQ_ERR_HIP 6    /* a HIP runtime call or kernel launch failed */
 #define KQ_ERR_NOMEM 7  /* scratch allocation failed */
@@ -224,7 +230,7 @@ typedef struct kq_chain kq_chain;
  * Plan a chain of n_steps (1..65536) steps on the current device: validates
  * every step as kq_gemv_multi would, sizes the persistent grid from the
  * kernel's occupancy, and allocates the chain's device memory (partial sums,
- * 16.1 MB, plus about 2.4 KB per step for the step table and the step
+ * 64 MiB, plus about 2.4 KB per step for the step table and the step
  * barrier's words).  Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
  * Every x must also satisfy ((batch-1)*ldx + cols) * element size < 2^31.
  * On success *out owns the plan; release it with kq_chain_destroy.

@@ -138,7 +138,8 @@ static int validate(int type, int n, const void* const* w, const int64_t* rows, 
                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy) {
   if (type != KQ_Q4_K && type != KQ_Q5_K && type != KQ_Q6_K) return KQ_ERR_TYPE;
   if (xtype != KQ_X_F32 && xtype != KQ_X_BF16) return KQ_ERR_TYPE;
-  if (batch < 1 || batch > KQ_MAX_BATCH || n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
+  if (batch < 1 || batch > (xtype == KQ_X_F32 ? KQ_MAX_BATCH_F32 : KQ_MAX_BATCH) || n < 1 || n > KQ_MAX_PROJ)
+    return KQ_ERR_BATCH;
   if (!w || !rows || !y || !ldy || !x) return KQ_ERR_NULL;
   for (int i = 0; i < n; ++i)
     if (!w[i] || !y[i]) return KQ_ERR_NULL;
@@ -192,9 +193,14 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   // (and sub-block sums) of the columns its nw*upw units touch in LDS, within
   // `budget` bytes (64 KiB leaves room for two 4-wavefront workgroups per CU,
   // 112 KiB is for one 8-wavefront workgroup), plus its wavefronts' partial sums.
-  const int nw = force_nw ? force_nw : wg_waves(batch);
-  const bool mf = xtype == KQ_X_BF16 && batch >= matrix_cores_from();
-  const int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
+  // above batch 8 only the matrix cores with 8-wavefront workgroups are built
+  const int nw = batch > 8 ? 8 : force_nw ? force_nw : wg_waves(batch);
+  const bool mf = xtype == KQ_X_BF16 && (batch >= matrix_cores_from() || batch > 8);
+  // staging budget: what is left of the CU's LDS after the tile sums (two tiles
+  // per wavefront assumed here; the final size is checked below)
+  const int64_t tile_sums = (int64_t)nw * 2 * batch * 64 * sizeof(float);
+  int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
+  if (budget > (int64_t)kMaxLds - tile_sums - 2048) budget = (int64_t)kMaxLds - tile_sums - 2048;
   const int64_t target = (int64_t)cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
@@ -307,6 +313,15 @@ static hipError_t launch_chain(int xtype, int batch, const ChainArgs& c, int nw,
     KQ_CHAIN_CASE(1) KQ_CHAIN_CASE(2) KQ_CHAIN_CASE(3) KQ_CHAIN_CASE(4)
     KQ_CHAIN_CASE(5) KQ_CHAIN_CASE(6) KQ_CHAIN_CASE(7) KQ_CHAIN_CASE(8)
 #undef KQ_CHAIN_CASE
+    default: break;
+  }
+  if (f32 || !mf || nw != 8) return hipErrorInvalidValue;
+  switch (batch) {
+#define KQ_CHAIN_WIDE(B) \
+  case B: return launch_chain_wide<B>(c, grid, lds, s, occupancy);
+    KQ_CHAIN_WIDE(9) KQ_CHAIN_WIDE(10) KQ_CHAIN_WIDE(11) KQ_CHAIN_WIDE(12)
+    KQ_CHAIN_WIDE(13) KQ_CHAIN_WIDE(14) KQ_CHAIN_WIDE(15) KQ_CHAIN_WIDE(16)
+#undef KQ_CHAIN_WIDE
     default: return hipErrorInvalidValue;
   }
 }
@@ -452,7 +467,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   if (n_steps < 1 || n_steps > (1 << 16)) return KQ_ERR_BATCH;
   if (!steps) return KQ_ERR_NULL;
   if (xtype != KQ_X_F32 && xtype != KQ_X_BF16) return KQ_ERR_TYPE;
-  if (batch < 1 || batch > KQ_MAX_BATCH) return KQ_ERR_BATCH;
+  if (batch < 1 || batch > (xtype == KQ_X_F32 ? KQ_MAX_BATCH_F32 : KQ_MAX_BATCH)) return KQ_ERR_BATCH;
   const int64_t esize = xtype == KQ_X_F32 ? 4 : 2;
   for (int j = 0; j < n_steps; ++j) {
     const kq_chain_step& st = steps[j];
@@ -479,7 +494,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
                          max_grid, nw, st.epilogue, nullptr, nullptr, &plans[j]);
-      if (rc == KQ_ERR_RANGE && nw == 8) {   // every step then runs with 4-wavefront workgroups
+      if (rc == KQ_ERR_RANGE && nw == 8 && batch <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;
       }
@@ -488,14 +503,13 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     }
     return (int)KQ_OK;
   };
-  int64_t groups = (int64_t)cus * (8 / nw);   // one 8-wavefront or two 4-wavefront workgroups per CU
+  // Every step is planned as its single launch would be; the persistent grid
+  // (one 8-wavefront or two 4-wavefront workgroups per CU, fewer if the
+  // occupancy says so) walks each step's logical blocks grid-stride.
   size_t lds = 0;
-  const int nw0 = nw;
-  int rc = plan_all(groups, &lds);
-  if (rc == KQ_ERR_RANGE && nw != nw0) {
-    groups = (int64_t)cus * 2;
-    rc = plan_all(groups, &lds);
-  }
+  int rc = plan_all(kMaxGroups, &lds);
+  if (rc == KQ_ERR_RANGE && nw == 4 && batch <= 8) rc = plan_all(kMaxGroups, &lds);
+  int64_t groups = (int64_t)cus * (8 / nw);
   int occ = 0;
   if (rc == KQ_OK &&
       launch_chain(xtype, batch, ChainArgs{}, nw, plans[0].mf, 0, lds, nullptr, &occ) != hipSuccess)
@@ -504,7 +518,6 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   if (rc == KQ_OK && (int64_t)occ * cus < groups) {
     groups = (int64_t)occ * cus / 8 * 8;
     if (groups < 8) rc = KQ_ERR_RANGE;
-    else rc = plan_all(groups, &lds);
   }
   if (rc != KQ_OK) {
     delete c;

@@ -329,16 +329,17 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
   using F = Fmt<QT>;
   using L = MfmaLds<QT, B>;
   constexpr int NB = L::NB, SB = F::kSubBlocks, KB = F::kSubW / 8;
+  constexpr int H = NB <= 2 ? 2 : 1;                  // chains in flight (registers allow two up to NB 2)
   const int t_base = len * L::kXCol, z_base = t_base + len * L::kTCol;
   const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;
   const bf16x8 bconst = __builtin_bit_cast(bf16x8, u32x4{kc, kc, kc, kc});
   const int nt = len * SB, nch = (nt + 3) / 4;
-  for (int c0 = wid; c0 < nch; c0 += 2 * NW) {
-    int it[2];
-    const uint8_t* ap[2][NB];
-    f32x4 t[2][NB];
+  for (int c0 = wid; c0 < nch; c0 += H * NW) {
+    int it[H];
+    const uint8_t* ap[H][NB];
+    f32x4 t[H][NB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < H; ++h) {
       const int ch = min(c0 + h * NW, nch - 1);
       it[h] = min(4 * ch + (lane >> 4), nt - 1);
       const int ic = it[h] / SB, g = it[h] - ic * SB;
@@ -347,22 +348,27 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
         ap[h][gb] = lds + a_operand_offset<B>(lane, gb, ic, 0, z_base) + g * F::kSubW * 2;
       }
     }
-    bf16x8 av[2][NB][KB], bc[KB];
+    bf16x8 av[H][NB][KB], bc[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) bc[kb] = bconst;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < H; ++h)
 #pragma unroll
         for (int gb = 0; gb < NB; ++gb) av[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[h][gb] + kb * 16);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (NB == 1) mfma_chain<KB>(t[h][0], av[h][0], bc);
-      else mfma_chain2<KB>(t[h][0], t[h][NB - 1], av[h][0], av[h][NB - 1], bc);
+    for (int h = 0; h < H; ++h) {
+      if constexpr (NB == 1) {
+        mfma_chain<KB>(t[h][0], av[h][0], bc);
+      } else {
+#pragma unroll
+        for (int gb = 0; gb + 1 < NB; gb += 2) mfma_chain2<KB>(t[h][gb], t[h][gb + 1], av[h][gb], av[h][gb + 1], bc);
+        if constexpr (NB % 2 == 1) mfma_chain<KB>(t[h][NB - 1], av[h][NB - 1], bc);
+      }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < H; ++h)
       if (c0 + h * NW < nch && 4 * (c0 + h * NW) + (lane >> 4) < nt && (lane & 15) == 0)
 #pragma unroll
         for (int gb = 0; gb < NB; ++gb)
@@ -373,49 +379,144 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
 // One unit on the matrix cores: ap[gb] are this lane's A-operand pointers for
 // the unit's column, Tc the column's T block.  The operands and T of sub-block
 // g+1 are read from LDS while sub-block g is on the matrix core, so the read
-// latency is not paid per instruction.
-template <int QT, int B>
+// latency is not paid per instruction.  LEAN (chain kernels, which hold the code
+// of every weight type and would otherwise spill registers at batch 5..8): with
+// two operand sets, each sub-block's operands are read just before use.
+template <int QT, int B, bool LEAN>
 __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6, const uint8_t* const* ap,
                                                   const float* Tc, float* acc, uint32_t M, uint32_t K) {
   using F = Fmt<QT>;
   constexpr int SB = F::kSubBlocks, NP = F::kPairs, KB = F::kSubW / 8, NB = MfmaLds<QT, B>::NB;
   float ca[SB], cm[SB];
   sb_coeffs<QT>(buf, d6, 0.0078125f, ca, cm);
-  bf16x8 A[2][NB][KB];
-  f32x4 Tv[2][NB];
-  auto read_operands = [&](int g, int h) {
+  auto scale = [&](int g, int gb, const f32x4& S, const f32x4& t) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int gb = 0; gb < NB; ++gb)
-        A[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-#pragma unroll
-    for (int gb = 0; gb < NB; ++gb) Tv[h][gb] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+    for (int r = 0; r < 4; ++r) {
+      if (4 * gb + r < B) {
+        float& v = acc[4 * gb + r];
+        v = __builtin_fmaf(ca[g], S[r] - t[r], v);
+        if constexpr (QT != KQ_Q6_K) v = __builtin_fmaf(-cm[g], t[r], v);
+      }
+    }
   };
-  read_operands(0, 0);
   uint32_t pr[NP];
+  if constexpr (LEAN && NB == 2) {
 #pragma unroll
-  for (int g = 0; g < SB; ++g) {
-    const int h = g & 1;
-    if (g + 1 < SB) read_operands(g + 1, h ^ 1);
-    unpack_pairs<QT>(buf, g, M, K, pr);
-    bf16x8 bop[KB];
+    for (int g = 0; g < SB; ++g) {
+      bf16x8 A[NB][KB];
+      f32x4 Tv[NB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      bop[kb] = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
-    f32x4 S[NB];
-    if constexpr (NB == 1) mfma_chain<KB>(S[0], A[h][0], bop);
-    else mfma_chain2<KB>(S[0], S[NB - 1], A[h][0], A[h][NB - 1], bop);
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int gb = 0; gb < NB; ++gb) {
-      const f32x4 t = Tv[h][gb];
+        for (int gb = 0; gb < NB; ++gb)
+          A[gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (4 * gb + r < B) {
-          float& v = acc[4 * gb + r];
-          v = __builtin_fmaf(ca[g], S[gb][r] - t[r], v);
-          if constexpr (QT != KQ_Q6_K) v = __builtin_fmaf(-cm[g], t[r], v);
+      for (int gb = 0; gb < NB; ++gb) Tv[gb] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+      unpack_pairs<QT>(buf, g, M, K, pr);
+      bf16x8 bop[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        bop[kb] = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
+      f32x4 S[NB];
+      mfma_chain2<KB>(S[0], S[1], A[0], A[1], bop);
+#pragma unroll
+      for (int gb = 0; gb < NB; ++gb) scale(g, gb, S[gb], Tv[gb]);
+    }
+  } else if constexpr (NB <= 2) {
+    bf16x8 A[2][NB][KB];
+    f32x4 Tv[2][NB];
+    auto read_operands = [&](int g, int h) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int gb = 0; gb < NB; ++gb)
+          A[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
+#pragma unroll
+      for (int gb = 0; gb < NB; ++gb) Tv[h][gb] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+    };
+    read_operands(0, 0);
+#pragma unroll
+    for (int g = 0; g < SB; ++g) {
+      const int h = g & 1;
+      if (g + 1 < SB) read_operands(g + 1, h ^ 1);
+      unpack_pairs<QT>(buf, g, M, K, pr);
+      bf16x8 bop[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        bop[kb] = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
+      f32x4 S[NB];
+      if constexpr (NB == 1) mfma_chain<KB>(S[0], A[h][0], bop);
+      else mfma_chain2<KB>(S[0], S[NB - 1], A[h][0], A[h][NB - 1], bop);
+#pragma unroll
+      for (int gb = 0; gb < NB; ++gb) scale(g, gb, S[gb], Tv[h][gb]);
+    }
+  } else if constexpr (LEAN) {
+    // batch 9..16 in a chain kernel: operand sets two at a time, read just before use
+    constexpr int NPAIR = (NB + 1) / 2;
+#pragma unroll
+    for (int g = 0; g < SB; ++g) {
+      unpack_pairs<QT>(buf, g, M, K, pr);
+      bf16x8 bop[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        bop[kb] = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
+#pragma unroll
+      for (int q = 0; q < NPAIR; ++q) {
+        bf16x8 A[2][KB];
+        f32x4 Tv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int gb = 2 * q + i;
+          if (gb < NB) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              A[i][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
+            Tv[i] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+          }
         }
+        f32x4 S[2];
+        if (2 * q + 1 < NB) mfma_chain2<KB>(S[0], S[1], A[0], A[1], bop);
+        else mfma_chain<KB>(S[0], A[0], bop);
+        scale(g, 2 * q, S[0], Tv[0]);
+        if (2 * q + 1 < NB) scale(g, 2 * q + 1, S[1], Tv[1]);
+      }
+    }
+  } else {
+    // batch 9..16: three or four operand sets, taken two at a time; the next
+    // pair's operands are read from LDS while the current pair computes
+    constexpr int NPAIR = (NB + 1) / 2;
+    bf16x8 A[2][2][KB];
+    f32x4 Tv[2][2];
+    auto read_pair = [&](int g, int q, int h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int gb = 2 * q + i;
+        if (gb < NB) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            A[h][i][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
+          Tv[h][i] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+        }
+      }
+    };
+    read_pair(0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < SB; ++g) {
+      unpack_pairs<QT>(buf, g, M, K, pr);
+      bf16x8 bop[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        bop[kb] = __builtin_bit_cast(bf16x8, u32x4{pr[4 * kb], pr[4 * kb + 1], pr[4 * kb + 2], pr[4 * kb + 3]});
+#pragma unroll
+      for (int q = 0; q < NPAIR; ++q) {
+        const int h = (g * NPAIR + q) & 1;
+        if (q + 1 < NPAIR) read_pair(g, q + 1, h ^ 1);
+        else if (g + 1 < SB) read_pair(g + 1, 0, h ^ 1);
+        f32x4 S[2];
+        if (2 * q + 1 < NB) mfma_chain2<KB>(S[0], S[1], A[h][0], A[h][1], bop);
+        else mfma_chain<KB>(S[0], A[h][0], bop);
+        scale(g, 2 * q, S[0], Tv[h][0]);
+        if (2 * q + 1 < NB) scale(g, 2 * q + 1, S[1], Tv[h][1]);
       }
     }
   }
@@ -604,7 +705,8 @@ __device__ __forceinline__ void chain_wait(const ChainCtl& c, int step, uint32_t
 // before the wait for the previous step, and the activations are read, and y
 // written, through the device coherence point.
 template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH, bool CHAIN, class GA>
-__device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ctl, int step, uint32_t tag) {
+__device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ctl, int step, uint32_t tag,
+                                           bool wait = true) {
   using F = Fmt<QT>;
   constexpr int NCH = F::kChunks, SB = F::kSubBlocks;
   constexpr int XW = XF32 ? 256 : 128;
@@ -682,7 +784,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
 #pragma unroll
     for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
     if constexpr (!DYN) refill(DEPTH - 1);
-    chain_wait(*ctl, step, tag);
+    if (wait) chain_wait(*ctl, step, tag);
     xs.template load<true>(a, c0w, len, 0);
   } else {
     xs.template load<false>(a, c0w, len, 0);
@@ -772,7 +874,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         const uint8_t* ap[NB];
 #pragma unroll
         for (int gb = 0; gb < NB; ++gb) ap[gb] = base + a_operand_offset<B>(lane, gb, ic, 0, z_base);
-        process_unit_mfma<QT, B>(buf[k], d6[k], ap,
+        process_unit_mfma<QT, B, CHAIN>(buf[k], d6[k], ap,
                                  reinterpret_cast<const float*>(base + t_base + ic * MfmaLds<QT, B>::kTCol),
                                  acc, M, K);
       } else {
@@ -842,7 +944,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     else if (ts >= U0 && te <= U1) write_tile<B, CHAIN>(a, t, lane, s);   // every tile when tiles_per_wg > 0
     else hand_off<B, CHAIN>(a, t, lblock, NW * upw, lane, s);
   }
-  return true;
+  return wait;
 }
 
 // ---------------------------------------------------------------- chains
@@ -874,11 +976,18 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
     ConstChainStep& st = steps[j];
     const int g = st.grid;
     bool waited = false;
-    if ((int)blockIdx.x < g) {
-      const int lblock = (blockIdx.x & 7) * (g >> 3) + (blockIdx.x >> 3);
-      if (st.type == KQ_Q4_K) waited = gemv_block<KQ_Q4_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag);
-      else if (st.type == KQ_Q5_K) waited = gemv_block<KQ_Q5_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag);
-      else waited = gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag);
+    // the step's logical blocks, as a single launch numbers them, grid-stride
+    // over the resident workgroups (the launch is a multiple of 8 workgroups, so
+    // every logical block keeps the XCD it would have had); the first block
+    // with work waits at the step barrier
+    for (int vb = blockIdx.x; vb < g; vb += gridDim.x) {
+      const int lblock = (vb & 7) * (g >> 3) + (vb >> 3);
+      if (st.type == KQ_Q4_K)
+        waited |= gemv_block<KQ_Q4_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
+      else if (st.type == KQ_Q5_K)
+        waited |= gemv_block<KQ_Q5_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
+      else
+        waited |= gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
     }
     if (blockIdx.x == 0 && j > 0 && !waited) chain_collect(c.ctl, j - 1, tag);   // the collector never skips a step
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's y / partial stores are done
@@ -908,6 +1017,12 @@ static hipError_t launch_nw(const GemvArgs& a, int nw, int grid, size_t lds, hip
   return hipGetLastError();
 }
 
+template <int QT, int B>
+static hipError_t launch_wide(const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_kernel<QT, B, false, true, 8, KQ_DEPTH>), dim3(grid), dim3(512), lds, s, a);
+  return hipGetLastError();
+}
+
 // The matrix-core variant exists for bf16 activations and batch >= 2.
 template <int QT, int B, bool XF32>
 static hipError_t launch_one(const GemvArgs& a, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
@@ -929,8 +1044,24 @@ static hipError_t launch_b(const GemvArgs& a, int batch, int nw, bool mf, int gr
     case 6: return launch_one<QT, 6, XF32>(a, nw, mf, grid, lds, s);
     case 7: return launch_one<QT, 7, XF32>(a, nw, mf, grid, lds, s);
     case 8: return launch_one<QT, 8, XF32>(a, nw, mf, grid, lds, s);
-    default: return hipErrorInvalidValue;
+    default: break;
   }
+  // batch 9..16: bf16 activations on the matrix cores, 8-wavefront workgroups
+  if constexpr (!XF32) {
+    if (!mf || nw != 8) return hipErrorInvalidValue;
+    switch (batch) {
+      case 9: return launch_wide<QT, 9>(a, grid, lds, s);
+      case 10: return launch_wide<QT, 10>(a, grid, lds, s);
+      case 11: return launch_wide<QT, 11>(a, grid, lds, s);
+      case 12: return launch_wide<QT, 12>(a, grid, lds, s);
+      case 13: return launch_wide<QT, 13>(a, grid, lds, s);
+      case 14: return launch_wide<QT, 14>(a, grid, lds, s);
+      case 15: return launch_wide<QT, 15>(a, grid, lds, s);
+      case 16: return launch_wide<QT, 16>(a, grid, lds, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int B, bool XF32, bool MF>
@@ -952,6 +1083,15 @@ hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t 
   }
   if (mf) return hipErrorInvalidValue;
   return launch_chain_nw<B, XF32, false>(c, nw, grid, lds, s, occupancy);
+}
+
+// Chain launch for batch 9..16 (bf16 activations, matrix cores, 8-wavefront workgroups).
+template <int B>
+hipError_t launch_chain_wide(const ChainArgs& c, int grid, size_t lds, hipStream_t s, int* occupancy) {
+  const void* k = reinterpret_cast<const void*>(&chain_kernel<B, false, true, 8>);
+  if (occupancy) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, k, 512, lds);
+  hipLaunchKernelGGL((chain_kernel<B, false, true, 8>), dim3(grid), dim3(512), lds, s, c);
+  return hipGetLastError();
 }
 
 // Host entry for one weight type; each type is instantiated in its own

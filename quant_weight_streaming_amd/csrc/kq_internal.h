@@ -63,6 +63,8 @@ struct ChainArgs {
 
 template <int B, bool XF32>
 hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t lds, hipStream_t s, int* occupancy);
+template <int B>
+hipError_t launch_chain_wide(const ChainArgs& c, int grid, size_t lds, hipStream_t s, int* occupancy);
 
 template <int QT>
 hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkq.so")
 
 KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 1, 2, 3
 KQ_X_F32, KQ_X_BF16 = 0, 1
-KQ_MAX_BATCH, KQ_MAX_PROJ = 8, 8
+KQ_MAX_BATCH, KQ_MAX_BATCH_F32, KQ_MAX_PROJ = 16, 8, 8
 KQ_EPI_NONE, KQ_EPI_SWIGLU = 0, 1
 TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}

@@ -53,7 +53,8 @@ A16 = 0x10000  # a fake, 16-byte aligned "device" address: validation fails befo
     ((A16, 64, 256, A16 + 2, 1, 256, 1, A16, 64), 3),   # x misaligned
     ((A16, 64, 256, A16, 1, 260, 1, A16, 64), 3),       # bf16 row stride not 16 B
     ((A16, 64, 256, A16, 1, 256, 0, A16, 64), 4),       # batch 0
-    ((A16, 64, 256, A16, 1, 256, 9, A16, 64), 4),       # batch 9
+    ((A16, 64, 256, A16, 1, 256, 17, A16, 64), 4),      # batch 17 (bf16 x allows 16)
+    ((A16, 64, 256, A16, 0, 256, 9, A16, 64), 4),       # batch 9 with fp32 x (fp32 allows 8)
     ((A16, 64, 256, A16, 7, 256, 1, A16, 64), 5),       # xtype
 ])
 def test_gemv_rejects(args, code):
@@ -112,7 +113,8 @@ def _step(**kw):
     (dict(type=9), 1, 1, 5),                 # weight type
     (dict(), 7, 1, 5),                       # activation type
     (dict(), 1, 0, 4),                       # batch
-    (dict(), 1, 9, 4),
+    (dict(), 1, 17, 4),
+    (dict(), 0, 9, 4),                       # fp32 x: at most 8
     (dict(n=0), 1, 1, 4),                    # segments
     (dict(cols=300, ldx=300), 1, 1, 2),      # cols % 256
     (dict(ldx=128), 1, 1, 2),                # ldx < cols
@@ -164,7 +166,7 @@ def test_swiglu_rejects():
     assert L.kq_repack_swiglu(1, 0, 256, A16, A16, A16, None) == 2
     assert L.kq_repack_swiglu(1, 64, 300, A16, A16, A16, None) == 2
     assert L.kq_repack_swiglu(1, 64, 256, A16, A16, A16 + 4, None) == 3
-    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 256, 9, A16, 64, None) == 4
+    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 256, 17, A16, 64, None) == 4
     assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 128, 1, A16, 64, None) == 2
     assert L.kq_gemv_swiglu(1, None, 64, 256, A16, 1, 256, 1, A16, 64, None) == 1
 

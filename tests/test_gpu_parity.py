@@ -257,3 +257,13 @@ def test_vector_path_bf16(qtype, batch, cols, monkeypatch):
     monkeypatch.setenv("KQ_MATRIX_CORES_FROM", "9")
     run_case(qtype, 5 * 64 + 9, cols, batch, "bf16", 600 + batch, check_w=False)
 
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("batch", [9, 12, 13, 16])
+@pytest.mark.parametrize("shape", [(3 * 64 + 17, 5 * 256), (5 * 64 + 9, 122 * 256)], ids=["ragged", "windows"])
+def test_verify_block_batches(qtype, batch, shape):
+    """A speculative-verify block of up to 16 rows (bf16 x, matrix cores with three or four operand
+    sets): a ragged tile, and long rows split into column windows."""
+    rows, cols = shape
+    run_case(qtype, rows, cols, batch, "bf16", 800 + batch, check_w=False)

@@ -73,3 +73,9 @@ def test_config4_sweep_gemvs(spec):
 def test_p4_sweep_gemvs(spec):
     """The 6656-hidden decoder's projections (K = 26, 16 and 78 super-blocks, a four-way fused qkvg)."""
     run_gemv(spec, [1, 3, 8], 5)
+
+
+@pytest.mark.parametrize("spec", [synth.QKV, synth.GATE_UP, synth.DOWN, synth.HEAD], ids=lambda s: s.name)
+def test_verify_block_full_size(spec):
+    """The sweep's projections verifying a 16-token speculative block (and 12), sampled rows."""
+    run_gemv(spec, [12, 16], 6)
