@@ -71,9 +71,11 @@ extern "C" {
 #define KQ_MAX_BATCH_F32 8
 #define KQ_MAX_PROJ 8
 
-/* epilogues */
+/* epilogues (what a launch does with a finished output before storing it) */
 #define KQ_EPI_NONE 0
-#define KQ_EPI_SWIGLU 1
+#define KQ_EPI_SWIGLU 1    /* silu(gate) * up, see kq_gemv_swiglu */
+#define KQ_EPI_SIGMOID 2   /* y = 1 / (1 + exp(-(W x))): the attention output gate */
+#define KQ_EPI_RESIDUAL 3  /* y = y + W x: y holds the residual stream on entry */
 
 /* status codes */
 #define KQ_OK 0
@@ -157,6 +159,22 @@ int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, in
 int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
 
 /*
+ * kq_gemv_multi with an epilogue per segment (epi: host array of n codes,
+ * KQ_EPI_NONE, KQ_EPI_SIGMOID or KQ_EPI_RESIDUAL).  Both fold the work either
+ * side of a projection into its launch ("Muse-Glimmer-30B (text decoder) -
+ * Apple Core AI", section "The architecture, and what the port had to do about
+ * it"): the sigmoid output gate read from the same hidden state as Q/K/V is the
+ * fourth segment of the fused qkvg launch, and the residual add closes the
+ * attention and feed-forward blocks around the O and down projections.
+ * RESIDUAL reads y[i][b*ldy + r] before writing it (a segment's y must not
+ * overlap another segment's).  Otherwise as kq_gemv_multi; KQ_ERR_TYPE for an
+ * unknown code.
+ */
+int kq_gemv_multi_epi(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x,
+                      int xtype, int64_t ldx, int batch, float *const *y, const int64_t *ldy, const int32_t *epi,
+                      void *stream);
+
+/*
  * SwiGLU epilogue: the gate and up projections of the feed-forward block in one
  * launch whose output is already the block's hidden activation,
  *     y[b*ldy + r] = silu(g) * u,  g = sum_k Wg[r, k] x[b, k],  u = sum_k Wu[r, k] x[b, k],
@@ -220,7 +238,8 @@ typedef struct kq_chain_step {
   int64_t ldy[KQ_MAX_PROJ];       /* output row strides (elements), >= rows */
   const void *x;                  /* device activations, batch rows of stride ldx */
   int64_t ldx;                    /* activation row stride (elements), >= cols */
-  int32_t epilogue;               /* KQ_EPI_NONE, or KQ_EPI_SWIGLU: n = 1, w from kq_repack_swiglu, rows[0] = inter */
+  int32_t epilogue;               /* segment i's KQ_EPI_* code in bits 4i..4i+3 (KQ_EPI_SWIGLU: n = 1,
+                                     w from kq_repack_swiglu, rows[0] = inter) */
   int32_t reserved;               /* set to 0 */
 } kq_chain_step;
 

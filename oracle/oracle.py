@@ -11,6 +11,7 @@ Functions:
   dequant_f32(...)                      the same rounded once to fp32 (RNE)
   gemv(qtype, rows, cols, gguf, x)      y = W x^T and a = sum |w x| in fp64, [batch, rows]
   silu(g), swiglu(g, u)                 the SwiGLU feed-forward's activation in fp64
+  sigmoid(v)                            the attention output gate, fp64
   gather(qtype, rows, cols, gguf, ids)  rows ids of dequant_f32 (the embedding lookup)
 """
 from __future__ import annotations
@@ -141,6 +142,14 @@ def silu(g):
     g = np.asarray(g, dtype=np.float64)
     with np.errstate(over="ignore"):
         return g / (1.0 + np.exp(-g))
+
+
+def sigmoid(v):
+    """sigmoid(v) = 1 / (1 + exp(-v)) in fp64: the attention output gate of the same card and section
+    (a sigmoid gate read from the hidden state that Q/K/V read)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-v))
 
 
 def swiglu(g, u):

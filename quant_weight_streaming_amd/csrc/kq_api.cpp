@@ -164,11 +164,13 @@ struct Plan {
 
 // Launch geometry of a validated call on a device with `cus` CUs, using at most
 // `max_grid` workgroups (a multiple of 8).
-// epi == KQ_EPI_SWIGLU: one matrix (n == 1) from kq_repack_swiglu, rows[0] =
-// the intermediate size, 32 outputs per 64-row tile.
+// epi: segment i's epilogue code in bits 4i..4i+3.  KQ_EPI_SWIGLU: one matrix
+// (n == 1) from kq_repack_swiglu, rows[0] = the intermediate size, 32 outputs
+// per 64-row tile.
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
-                     int64_t max_grid, int force_nw, int epi, float* partial, uint32_t* counters, Plan* out) {
+                     int64_t max_grid, int force_nw, uint32_t epi, float* partial, uint32_t* counters,
+                     Plan* out) {
   const int64_t n_cols = cols / 256;
   GemvArgs a{};
   a.epi = epi;
@@ -180,7 +182,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     a.ldy[i] = ldy[i];
     a.rows[i] = (int32_t)rows[i];
     a.tile_begin[i] = (int32_t)tiles;
-    tiles += epi == KQ_EPI_SWIGLU ? (rows[i] + 31) / 32 : (rows[i] + 63) / 64;
+    tiles += epi == (uint32_t)KQ_EPI_SWIGLU ? (rows[i] + 31) / 32 : (rows[i] + 63) / 64;
     if (tiles > INT32_MAX) return KQ_ERR_RANGE;
   }
   for (int i = n; i <= KQ_MAX_PROJ; ++i) a.tile_begin[i] = (int32_t)tiles;
@@ -278,11 +280,23 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   return KQ_OK;
 }
 
+// Packed per-segment epilogue codes are valid: SwiGLU alone on a single matrix,
+// else sigmoid / residual / none on each of the n segments.
+static bool valid_epilogue(int n, uint32_t epi) {
+  if (epi == (uint32_t)KQ_EPI_SWIGLU) return n == 1;
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = (epi >> (4 * i)) & 15u;
+    if (i >= n ? c != 0 : (c != KQ_EPI_NONE && c != KQ_EPI_SIGMOID && c != KQ_EPI_RESIDUAL)) return false;
+  }
+  return true;
+}
+
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream,
-                     int epi = KQ_EPI_NONE) {
+                     uint32_t epi = KQ_EPI_NONE) {
   int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
   if (rc != KQ_OK) return rc;
+  if (!valid_epilogue(n, epi)) return KQ_ERR_TYPE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
   DeviceState* st = nullptr;
@@ -408,6 +422,19 @@ int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void* gate, co
   return KQ_OK;
 }
 
+int kq_gemv_multi_epi(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, const int32_t* epi,
+                      void* stream) {
+  if (!epi) return KQ_ERR_NULL;
+  if (n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
+  uint32_t packed = 0;
+  for (int i = 0; i < n; ++i) {
+    if (epi[i] != KQ_EPI_NONE && epi[i] != KQ_EPI_SIGMOID && epi[i] != KQ_EPI_RESIDUAL) return KQ_ERR_TYPE;
+    packed |= (uint32_t)epi[i] << (4 * i);
+  }
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed);
+}
+
 int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,
                    int batch, float* y, int64_t ldy, void* stream) {
   if (inter > (int64_t)INT32_MAX / 2 - 64) return KQ_ERR_RANGE;
@@ -473,7 +500,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     const kq_chain_step& st = steps[j];
     const int rc = validate(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy);
     if (rc != KQ_OK) return rc;
-    if (st.epilogue != KQ_EPI_NONE && (st.epilogue != KQ_EPI_SWIGLU || st.n != 1)) return KQ_ERR_TYPE;
+    if (!valid_epilogue(st.n, (uint32_t)st.epilogue)) return KQ_ERR_TYPE;
     if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
   int dev = 0;
@@ -493,7 +520,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     for (int j = 0; j < n_steps; ++j) {
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
-                         max_grid, nw, st.epilogue, nullptr, nullptr, &plans[j]);
+                         max_grid, nw, (uint32_t)st.epilogue, nullptr, nullptr, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && batch <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;

@@ -550,13 +550,21 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
   for (int i = 1; i < KQ_MAX_PROJ; ++i)
     if (i < a.nproj && t >= a.tile_begin[i]) p = i;
   const int row = (t - a.tile_begin[p]) * kTileRows + lane;
+  const uint32_t code = (a.epi >> (4 * p)) & 15u;
   if (row < a.rows[p]) {
     float* y = a.y[p];
     const int64_t ldy = a.ldy[p];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      if constexpr (COH) __hip_atomic_store(y + b * ldy + row, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else y[b * ldy + row] = v[b];
+      float o = v[b];
+      if (code == KQ_EPI_SIGMOID) {
+        o = 1.0f / (1.0f + expf(-o));            // the attention output gate
+      } else if (code == KQ_EPI_RESIDUAL) {      // y holds the residual stream on entry
+        float* yp = y + b * ldy + row;
+        o += COH ? __hip_atomic_load(yp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *yp;
+      }
+      if constexpr (COH) __hip_atomic_store(y + b * ldy + row, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else y[b * ldy + row] = o;
     }
   }
 }

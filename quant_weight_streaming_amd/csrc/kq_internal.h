@@ -24,7 +24,8 @@ struct GemvArgs {
   int32_t upw;                         // units per wavefront
   int32_t tsb;                         // LDS capacity in staged columns per workgroup
   int32_t tpw;                         // tiles a wavefront's run of units can touch (its LDS tile sums)
-  int32_t epi;                         // KQ_EPI_NONE, or KQ_EPI_SWIGLU: tile t holds 32 gate and 32 up rows
+  uint32_t epi;                        // epilogue code of segment i in bits 4i..4i+3 (KQ_EPI_*); KQ_EPI_SWIGLU:
+                                       // one segment whose tile t holds 32 gate and 32 up rows
   // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
   // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkq.so")
 KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 1, 2, 3
 KQ_X_F32, KQ_X_BF16 = 0, 1
 KQ_MAX_BATCH, KQ_MAX_BATCH_F32, KQ_MAX_PROJ = 16, 8, 8
-KQ_EPI_NONE, KQ_EPI_SWIGLU = 0, 1
+KQ_EPI_NONE, KQ_EPI_SWIGLU, KQ_EPI_SIGMOID, KQ_EPI_RESIDUAL = 0, 1, 2, 3
 TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
@@ -26,7 +26,8 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4:
           10: "KQ_ERR_DEVICE"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
-           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_dequant", "kq_gather_rows", "kq_repack_swiglu",
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_multi_epi", "kq_dequant", "kq_gather_rows",
+           "kq_repack_swiglu",
            "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
            "kq_chain_status", "kq_chain_destroy")
 
@@ -73,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_multi.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), vp]
         L.kq_gemv_multi.restype = ci
+        L.kq_gemv_multi_epi.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
+                                        ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32), vp]
+        L.kq_gemv_multi_epi.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
         L.kq_gather_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, vp]
@@ -163,6 +167,19 @@ def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) 
     LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
     _check("kq_gemv_multi", lib().kq_gemv_multi(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
                                                 x.shape[0], Y, LD, _stream(stream)))
+
+
+def kq_gemv_multi_epi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis, stream=None) -> None:
+    n = len(ws)
+    if len(rows) != n or len(ys) != n or len(epis) != n:
+        raise ValueError("ws, rows, ys and epis must have the same length")
+    W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in ws])
+    R = (ctypes.c_int64 * n)(*rows)
+    Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
+    E = (ctypes.c_int32 * n)(*epis)
+    _check("kq_gemv_multi_epi", lib().kq_gemv_multi_epi(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x),
+                                                        x.stride(0), x.shape[0], Y, LD, E, _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:

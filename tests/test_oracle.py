@@ -85,3 +85,15 @@ def test_gather_is_rows_of_dequant():
     ids = [69, 0, 64, 5, 5]
     full = O.dequant_f32("q4k", 70, 512, g)
     assert np.array_equal(O.gather("q4k", 70, 512, g, ids), full[ids])
+
+
+def test_sigmoid_closed_forms():
+    """sigmoid(0) = 1/2, sigmoid(v) + sigmoid(-v) = 1, sigmoid(ln 3) = 3/4, the limits, and
+    silu(v) = v sigmoid(v)."""
+    import math
+    assert O.sigmoid(0.0) == 0.5
+    v = np.linspace(-40.0, 40.0, 801)
+    assert np.allclose(O.sigmoid(v) + O.sigmoid(-v), 1.0, rtol=0, atol=1e-15)
+    assert abs(O.sigmoid(math.log(3.0)) - 0.75) < 1e-15
+    assert O.sigmoid(800.0) == 1.0 and O.sigmoid(-800.0) == 0.0
+    assert np.allclose(O.silu(v), v * O.sigmoid(v), rtol=1e-15, atol=0)
