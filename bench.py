@@ -211,6 +211,48 @@ def time_swiglu(inter: int, cols: int, batches, copies: int = 6, reps: int = 4) 
     return out
 
 
+def time_fused(parts, cols: int, batches, variants, copies: int = 6, reps: int = 4) -> dict:
+    """Mean launch time of one fused multi-projection launch (Q4_K, row segments `parts`) per variant
+    (name -> (epilogue codes or None, rms_eps)), over `copies` distinct weight sets."""
+    import torch
+    from quant_weight_streaming_amd import kq, synth
+    rows = sum(parts)
+    sets = []
+    for i in range(copies):
+        g = synth.gen_weights("q4k", rows, cols, synth.seed_of("bench-fused", i), device="cuda:0")
+        ws, r0 = [], 0
+        for r in parts:
+            ws.append(kq.repack("q4k", g[r0:r0 + r].contiguous(), r, cols))
+            r0 += r
+        sets.append(ws)
+        del g
+    out = {}
+    for name, (epis, eps) in variants.items():
+        out[name] = {}
+        for B in batches:
+            x = synth.gen_x(B, cols, synth.seed_of("bench-fused-x", B), device="cuda:0")
+            ys = [torch.zeros((B, r), device="cuda:0") for r in parts]
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                kq.kq_gemv_fused("q4k", sets[0], list(parts), cols, x, ys, epis, eps, s)
+                with torch.cuda.graph(graph, stream=s):
+                    for ws in sets:
+                        kq.kq_gemv_fused("q4k", ws, list(parts), cols, x, ys, epis, eps, s)
+            torch.cuda.current_stream().wait_stream(s)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out[name][f"b{B}"] = round(e0.elapsed_time(e1) * 1e3 / (reps * copies), 2)
+    return out
+
+
 def run_calls(calls):
     for fn, args, name in calls:
         rc = fn(*args)
@@ -539,6 +581,11 @@ def main():
     kt8 = kernel_times(sw, 8)
     cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
     swiglu_us = time_swiglu(synth.INTER, synth.HIDDEN, (1, 8))
+    qkvg = synth.QKVG_P4
+    fused_us = time_fused(qkvg.parts, qkvg.cols, (1, 8), {
+        "plain": (None, 0.0),
+        "rmsnorm_and_sigmoid_gate": ([kq.KQ_EPI_NONE] * 3 + [kq.KQ_EPI_SIGMOID], 1e-5)})
+    log(f"[bench] fused QKVG 8704x6656: {fused_us} us")
     log(f"[bench] gate+up with SwiGLU epilogue (Q4_K 2 x {synth.INTER}x{synth.HIDDEN}): {swiglu_us} us "
         f"(plain gate+up: {kt1['gate_up']['avg_us']} / {kt8['gate_up']['avg_us']} us)")
     if cpu:
@@ -637,6 +684,7 @@ def main():
                        "graph_weight_gbs": round(weight_gbs(bytes3, res[1]["graph_ms"]), 1)},
         "verify_cost_staircase": stair,
         "gate_up_swiglu_epilogue_us": swiglu_us,
+        "qkvg_6656_fused_us": fused_us,
         "kernels_b1": kt1,
         "kernels_b8": kt8,
         "c4_q5k_merged": c4,

@@ -159,20 +159,33 @@ int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, in
 int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
 
 /*
- * kq_gemv_multi with an epilogue per segment (epi: host array of n codes,
- * KQ_EPI_NONE, KQ_EPI_SIGMOID or KQ_EPI_RESIDUAL).  Both fold the work either
- * side of a projection into its launch ("Muse-Glimmer-30B (text decoder) -
- * Apple Core AI", section "The architecture, and what the port had to do about
- * it"): the sigmoid output gate read from the same hidden state as Q/K/V is the
- * fourth segment of the fused qkvg launch, and the residual add closes the
- * attention and feed-forward blocks around the O and down projections.
- * RESIDUAL reads y[i][b*ldy + r] before writing it (a segment's y must not
- * overlap another segment's).  Otherwise as kq_gemv_multi; KQ_ERR_TYPE for an
- * unknown code.
+ * kq_gemv_multi with the work either side of the projections folded into the
+ * launch ("Muse-Glimmer-30B (text decoder) - Apple Core AI", section "The
+ * architecture, and what the port had to do about it"):
+ *
+ * Before: rms_eps > 0 normalises every activation row first with a weight-less
+ * RMSNorm (the card puts one on the embedding output and on Q/K),
+ *     y[i][b*ldy + r] = sum_k dequant(W_i)[r, k] * x[b, k] / sqrt(mean_k x[b, k]^2 + rms_eps).
+ * The launch computes sum_k x[b, k]^2 alongside the staging of x and scales the
+ * finished dot products, which is the same quantity.  rms_eps == 0: no
+ * normalisation; negative, infinite or NaN: KQ_ERR_SHAPE.
+ *
+ * After: epi (host array of n codes, or NULL for all KQ_EPI_NONE) gives each
+ * segment's epilogue:
+ *   KQ_EPI_SIGMOID  y = 1 / (1 + exp(-y)): the sigmoid output gate read from the
+ *                   same hidden state as Q/K/V, the fourth segment of the fused
+ *                   qkvg launch;
+ *   KQ_EPI_RESIDUAL y = r + y, r read from y[i][b*ldy + r] before it is written:
+ *                   the residual add that closes the attention and feed-forward
+ *                   blocks around the O and down projections (a segment's y must
+ *                   not overlap another segment's);
+ *   KQ_EPI_SWIGLU   n = 1 only, w from kq_repack_swiglu and rows[0] = inter:
+ *                   as kq_gemv_swiglu.
+ * Otherwise as kq_gemv_multi; KQ_ERR_TYPE for an unknown code.
  */
-int kq_gemv_multi_epi(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x,
-                      int xtype, int64_t ldx, int batch, float *const *y, const int64_t *ldy, const int32_t *epi,
-                      void *stream);
+int kq_gemv_fused(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
+                  int64_t ldx, int batch, float *const *y, const int64_t *ldy, const int32_t *epi, float rms_eps,
+                  void *stream);
 
 /*
  * SwiGLU epilogue: the gate and up projections of the feed-forward block in one
@@ -240,7 +253,7 @@ typedef struct kq_chain_step {
   int64_t ldx;                    /* activation row stride (elements), >= cols */
   int32_t epilogue;               /* segment i's KQ_EPI_* code in bits 4i..4i+3 (KQ_EPI_SWIGLU: n = 1,
                                      w from kq_repack_swiglu, rows[0] = inter) */
-  int32_t reserved;               /* set to 0 */
+  float rms_eps;                  /* > 0: weight-less RMSNorm of x first, as kq_gemv_fused; 0: none */
 } kq_chain_step;
 
 typedef struct kq_chain kq_chain;

@@ -12,6 +12,8 @@ Functions:
   gemv(qtype, rows, cols, gguf, x)      y = W x^T and a = sum |w x| in fp64, [batch, rows]
   silu(g), swiglu(g, u)                 the SwiGLU feed-forward's activation in fp64
   sigmoid(v)                            the attention output gate, fp64
+  rmsnorm(x, eps)                       the weight-less RMSNorm, fp64
+  gemv_rmsnorm(...)                     W (rmsnorm(x)) from the fp64 dequantised W, fp64
   gather(qtype, rows, cols, gguf, ids)  rows ids of dequant_f32 (the embedding lookup)
 """
 from __future__ import annotations
@@ -150,6 +152,25 @@ def sigmoid(v):
     v = np.asarray(v, dtype=np.float64)
     with np.errstate(over="ignore"):
         return 1.0 / (1.0 + np.exp(-v))
+
+
+def rmsnorm(x, eps):
+    """The weight-less RMSNorm of each row of x in fp64: x / sqrt(mean(x^2) + eps), no gain ("Muse-Glimmer-30B
+    (text decoder) - Apple Core AI", section "The architecture, and what the port had to do about it": applied to
+    the embedding output and to Q/K).  x: float rows [batch, K]."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gemv_rmsnorm(qtype, rows, cols, gguf, x, eps):
+    """(y, a) = (W xn, |W| |xn|) per batch row, xn = rmsnorm(x, eps), W the fp64 dequantised matrix.
+    x: float32 [batch, cols] or uint16 bf16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    # a bf16 value is the upper half of the fp32 with the same bits
+    xd = ((x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x).astype(np.float64)
+    xn = rmsnorm(xd, eps)
+    W = dequant(qtype, rows, cols, gguf)
+    return xn @ W.T, np.abs(xn) @ np.abs(W).T
 
 
 def swiglu(g, u):

@@ -3,6 +3,7 @@
 // kernels of kq_gemv.h (instantiated per weight type in kq_gemv_q*.hip) and
 // kq_repack.hip.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -30,7 +31,7 @@ int64_t sb_bytes(int type) {
 // calls (the last arrival of a tile resets its counter), so they are cleared
 // once, at allocation.
 constexpr int kMaxGroups = 8192;
-constexpr size_t kPartialBytes = (size_t)kMaxGroups * 2 * KQ_MAX_BATCH * 64 * sizeof(float);
+constexpr size_t kPartialBytes = (size_t)kMaxGroups * 2 * kPartialStride * sizeof(float);
 constexpr size_t kCounterBytes = (size_t)kMaxGroups * sizeof(uint32_t);
 constexpr int kMaxDevices = 64;
 
@@ -169,11 +170,13 @@ struct Plan {
 // per 64-row tile.
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
-                     int64_t max_grid, int force_nw, uint32_t epi, float* partial, uint32_t* counters,
-                     Plan* out) {
+                     int64_t max_grid, int force_nw, uint32_t epi, float rms_eps, float* partial,
+                     uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
+  const bool norm = rms_eps > 0.0f;
   GemvArgs a{};
   a.epi = epi;
+  a.rms_eps = rms_eps;
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) {
     if (rows[i] > (int64_t)INT32_MAX - 64) return KQ_ERR_RANGE;
@@ -207,7 +210,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
   const int64_t per_col =
-      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1, 0, 0) - gemv_lds_bytes(type, xtype, batch, nw, mf, 0, 0, 0));
+      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1, 0, 0, norm) -
+                gemv_lds_bytes(type, xtype, batch, nw, mf, 0, 0, 0, norm));
   const int64_t max_cols = budget / per_col;
   if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
   int64_t n_groups = (n_units + nw * upw - 1) / (nw * upw);
@@ -275,7 +279,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     a.tpw = (int32_t)((upw - 1 + n_cols - 1) / n_cols + 1);
   }
   out->a.tpw = a.tpw;
-  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols, (int)run_units, a.tpw);
+  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols, (int)run_units, a.tpw, norm);
   if (out->lds > kMaxLds) return KQ_ERR_RANGE;
   return KQ_OK;
 }
@@ -291,22 +295,26 @@ static bool valid_epilogue(int n, uint32_t epi) {
   return true;
 }
 
+// The weight-less RMSNorm's epsilon: 0 (no normalisation) or finite and > 0.
+static bool valid_rms_eps(float e) { return e == 0.0f || (e > 0.0f && e <= FLT_MAX); }
+
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream,
-                     uint32_t epi = KQ_EPI_NONE) {
+                     uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f) {
   int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
   if (rc != KQ_OK) return rc;
   if (!valid_epilogue(n, epi)) return KQ_ERR_TYPE;
+  if (!valid_rms_eps(rms_eps)) return KQ_ERR_SHAPE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
   DeviceState* st = nullptr;
   rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
   Plan p{};
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, st->partial,
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, rms_eps, st->partial,
                  st->counters, &p);
   if (rc == KQ_ERR_RANGE && wg_waves(batch) == 8)   // too many units per workgroup for per-unit slots: 4-wavefront runs
-    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, st->partial,
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, rms_eps, st->partial,
                    st->counters, &p);
   if (rc != KQ_OK) return rc;
   if (launch_gemv(type, xtype, batch, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
@@ -422,17 +430,23 @@ int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void* gate, co
   return KQ_OK;
 }
 
-int kq_gemv_multi_epi(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
-                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, const int32_t* epi,
-                      void* stream) {
-  if (!epi) return KQ_ERR_NULL;
+int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x, int xtype,
+                  int64_t ldx, int batch, float* const* y, const int64_t* ldy, const int32_t* epi, float rms_eps,
+                  void* stream) {
   if (n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
   uint32_t packed = 0;
-  for (int i = 0; i < n; ++i) {
-    if (epi[i] != KQ_EPI_NONE && epi[i] != KQ_EPI_SIGMOID && epi[i] != KQ_EPI_RESIDUAL) return KQ_ERR_TYPE;
-    packed |= (uint32_t)epi[i] << (4 * i);
+  if (epi) {
+    if (n == 1 && epi[0] == KQ_EPI_SWIGLU) {
+      packed = KQ_EPI_SWIGLU;
+      if (rows && rows[0] > (int64_t)INT32_MAX / 2 - 64) return KQ_ERR_RANGE;
+    } else {
+      for (int i = 0; i < n; ++i) {
+        if (epi[i] != KQ_EPI_NONE && epi[i] != KQ_EPI_SIGMOID && epi[i] != KQ_EPI_RESIDUAL) return KQ_ERR_TYPE;
+        packed |= (uint32_t)epi[i] << (4 * i);
+      }
+    }
   }
-  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed);
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed, rms_eps);
 }
 
 int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,
@@ -501,6 +515,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     const int rc = validate(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy);
     if (rc != KQ_OK) return rc;
     if (!valid_epilogue(st.n, (uint32_t)st.epilogue)) return KQ_ERR_TYPE;
+    if (!valid_rms_eps(st.rms_eps)) return KQ_ERR_SHAPE;
     if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
   int dev = 0;
@@ -520,7 +535,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     for (int j = 0; j < n_steps; ++j) {
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
-                         max_grid, nw, (uint32_t)st.epilogue, nullptr, nullptr, &plans[j]);
+                         max_grid, nw, (uint32_t)st.epilogue, st.rms_eps, nullptr, nullptr, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && batch <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;

@@ -40,7 +40,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kTileRows = 64;
 constexpr int kChunk = 16;                      // bytes per lane per chunk
 constexpr int kChunkStride = kTileRows * kChunk;  // 1024 bytes between chunks of one tile
-constexpr int kPartialStride = KQ_MAX_BATCH * kTileRows;  // floats per partial-sum slot
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx950: 32-bit data
 // format, bounds checked against num_records.
 constexpr int kBufferFlags = 0x00020000;

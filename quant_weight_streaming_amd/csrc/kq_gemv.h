@@ -121,12 +121,40 @@ struct XStage {
     }
   }
 
+  // Q2 (not null: the launch normalises x): Q2[ic * B + b] = sum of x^2 over
+  // staged column ic of batch row b.  The SB items of one (column, row) sit in SB
+  // consecutive lanes (n and every round's start are multiples of SB), so their
+  // squares are added by a fixed butterfly and every workgroup that stages a
+  // column gets the same bits for it.
   template <bool WITH_T>
-  __device__ __forceinline__ void store(uint8_t* X, float* T, int len, int r) const {
+  __device__ __forceinline__ void store(uint8_t* X, float* T, float* Q2, int len, int r) const {
     const int n = len * B * SB;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int i = (r * IPT + j) * NT + threadIdx.x;
+      if (Q2) {
+        float q = 0.0f;
+        if (i < n) {
+#pragma unroll
+          for (int e = 0; e < VPI; ++e) {
+            const u32x4 xv = v[j][e];
+            if constexpr (XF32) {
+              q = fmaf(__uint_as_float(xv.x), __uint_as_float(xv.x), q);
+              q = fmaf(__uint_as_float(xv.y), __uint_as_float(xv.y), q);
+              q = fmaf(__uint_as_float(xv.z), __uint_as_float(xv.z), q);
+              q = fmaf(__uint_as_float(xv.w), __uint_as_float(xv.w), q);
+            } else {
+              q = dot2_bf16(xv.x, xv.x, q);
+              q = dot2_bf16(xv.y, xv.y, q);
+              q = dot2_bf16(xv.z, xv.z, q);
+              q = dot2_bf16(xv.w, xv.w, q);
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < SB; m <<= 1) q += __shfl_xor(q, m);
+        if (i < n && i % SB == 0) Q2[i / SB] = q;   // i / SB = ic * B + b
+      }
       if (i < n) {
         const int g = i % SB, q = i / SB, b = q % B, ic = q / B;
         u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * ES);
@@ -569,6 +597,26 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
   }
 }
 
+// Weight-less RMSNorm folded into the GEMV: W (x / rms(x)) = (W x) / rms(x),
+// rms(x) = sqrt(sum_k x_k^2 / K + eps) per batch row.  ss[b] is the sum of x^2
+// over all K columns of row b (the same for every lane); v[b] *= 1 / rms.
+template <int B, class GA>
+__device__ __forceinline__ void rms_scale(const GA& a, float* v, const float* ss) {
+  const float k = (float)a.n_cols * 256.0f;
+#pragma unroll
+  for (int b = 0; b < B; ++b) v[b] *= 1.0f / sqrtf(ss[b] / k + a.rms_eps);
+}
+
+// A piece's sums of x^2 go to the slot's words kPartialQ + b, lane b < B.
+template <int B>
+__device__ __forceinline__ void publish_q(float* slot, int lane, const float* q) {
+  float mine = 0.0f;
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+    if (lane == b) mine = q[b];
+  if (lane < B) __hip_atomic_store(slot + kPartialQ + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup L holds its sum for tile t, whose columns other workgroups share.
 // Hand it over; the last workgroup to arrive adds all of them in workgroup
 // order and writes y.  No L2 writeback is needed: the partials are written with
@@ -577,13 +625,15 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
 // counter, and the last arrival reads them with agent-scope atomic loads, which
 // bypass the per-XCD caches.  The counter is reset for the next call.
 template <int B, bool COH, class GA>
-__device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane, const float* v) {
+__device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane, const float* v, const float* q) {
   const int n_cols = a.n_cols;
+  const bool norm = a.rms_eps > 0.0f;
   const int slot = (t == (L * wgu) / n_cols) ? 0 : 1;
   float* mine = a.partial + (int64_t)(L * 2 + slot) * kPartialStride;
 #pragma unroll
   for (int b = 0; b < B; ++b)
     __hip_atomic_store(mine + b * kTileRows + lane, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (norm) publish_q<B>(mine, lane, q);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const int la = (t * n_cols) / wgu, lb = ((t + 1) * n_cols - 1) / wgu;
   uint32_t old = 0;
@@ -594,11 +644,12 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
+  float qs = 0.0f;   // lane b < B: the pieces' sums of x^2 for batch row b
   // read the pieces PR workgroups at a time (one round trip per PR), then add
   // them in workgroup order
   constexpr int PR = B <= 2 ? 8 : 4;
   for (int l0 = la; l0 <= lb; l0 += PR) {
-    float v[PR][B];
+    float v[PR][B], qv[PR];
 #pragma unroll
     for (int j = 0; j < PR; ++j) {
       const int l = l0 + j;
@@ -608,12 +659,23 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
       for (int b = 0; b < B; ++b)
         v[j][b] = l <= lb ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                           : 0.0f;
+      qv[j] = norm && l <= lb && lane < B
+                  ? __hip_atomic_load(pp + kPartialQ + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < PR; ++j)
+    for (int j = 0; j < PR; ++j) {
 #pragma unroll
       for (int b = 0; b < B; ++b)
         if (l0 + j <= lb) s[b] += v[j][b];
+      if (l0 + j <= lb) qs += qv[j];
+    }
+  }
+  if (norm) {
+    float qa[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) qa[b] = __shfl(qs, b);
+    rms_scale<B>(a, s, qa);
   }
   write_tile<B, COH>(a, t, lane, s);
   if (lane == 0) __hip_atomic_store(&a.counters[la], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -623,11 +685,13 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
 // window's columns.  Every window contributes one piece per tile; the last to
 // arrive adds them in window order.  Same publication protocol as hand_off.
 template <int B, bool COH, class GA>
-__device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, const float* v) {
+__device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, const float* v, const float* q) {
+  const bool norm = a.rms_eps > 0.0f;
   float* mine = a.partial + (int64_t)(w * a.n_tiles + t) * kPartialStride;
 #pragma unroll
   for (int b = 0; b < B; ++b)
     __hip_atomic_store(mine + b * kTileRows + lane, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (norm) publish_q<B>(mine, lane, q);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   uint32_t old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(&a.counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -637,23 +701,35 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
   float s[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) s[b] = 0.0f;
+  float qs = 0.0f;
   constexpr int PR = B <= 2 ? 8 : 4;
   for (int w0 = 0; w0 < a.n_win; w0 += PR) {
-    float q[PR][B];
+    float pv[PR][B], qv[PR];
 #pragma unroll
     for (int j = 0; j < PR; ++j) {
       const float* pp = a.partial + (int64_t)((w0 + j) * a.n_tiles + t) * kPartialStride;
 #pragma unroll
       for (int b = 0; b < B; ++b)
-        q[j][b] = w0 + j < a.n_win
-                      ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : 0.0f;
+        pv[j][b] = w0 + j < a.n_win
+                       ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.0f;
+      qv[j] = norm && w0 + j < a.n_win && lane < B
+                  ? __hip_atomic_load(pp + kPartialQ + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < PR; ++j)
+    for (int j = 0; j < PR; ++j) {
 #pragma unroll
       for (int b = 0; b < B; ++b)
-        if (w0 + j < a.n_win) s[b] += q[j][b];
+        if (w0 + j < a.n_win) s[b] += pv[j][b];
+      if (w0 + j < a.n_win) qs += qv[j];
+    }
+  }
+  if (norm) {
+    float qa[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) qa[b] = __shfl(qs, b);
+    rms_scale<B>(a, s, qa);
   }
   write_tile<B, COH>(a, t, lane, s);
   if (lane == 0) __hip_atomic_store(&a.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -748,10 +824,14 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   const int len = min(cw, U1 - U0);
   uint32_t* X = lds_words;
   float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);
-  // per-wavefront tile sums [NW][tpw][B][64] follow the staged columns
-  float* P = MF ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds_words) +
-                                           a.tsb * MfmaLds<QT, B>::kPerCol + 512)
-                : T + a.tsb * SB * B;
+  // the staged columns' sums of squares (normalised launches only), then the
+  // per-wavefront tile sums [NW][tpw][B][64]
+  const bool norm = a.rms_eps > 0.0f;
+  float* Q2 = MF ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds_words) +
+                                            a.tsb * MfmaLds<QT, B>::kPerCol + 512)
+                 : T + a.tsb * SB * B;
+  float* P = norm ? Q2 + ((a.tsb * B + 3) & ~3) : Q2;
+  if (!norm) Q2 = nullptr;
   // DYN (batch 1, one 8-wavefront workgroup per CU): instead of fixed runs the
   // wavefronts take the workgroup's units one at a time from an LDS counter, so
   // a wavefront that gets fewer issue slots than its neighbours simply computes
@@ -804,11 +884,11 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   }
   {
     uint8_t* Xb = reinterpret_cast<uint8_t*>(lds_words);
-    xs.template store<!MF>(Xb, T, len, 0);
+    xs.template store<!MF>(Xb, T, Q2, len, 0);
     const int nr = XStage<QT, B, XF32, NW, kRS>::rounds(len);
     for (int r = 1; r < nr; ++r) {
       xs.template load<CHAIN>(a, c0w, len, r);
-      xs.template store<!MF>(Xb, T, len, r);
+      xs.template store<!MF>(Xb, T, Q2, len, r);
     }
     if constexpr (MF) {
       const int z_base = len * MfmaLds<QT, B>::kPerCol;
@@ -948,9 +1028,33 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
       }
     }
-    if (a.n_win > 1) hand_off_windows<B, CHAIN>(a, t, w, lane, s);
-    else if (ts >= U0 && te <= U1) write_tile<B, CHAIN>(a, t, lane, s);   // every tile when tiles_per_wg > 0
-    else hand_off<B, CHAIN>(a, t, lblock, NW * upw, lane, s);
+    // normalised launches: the sum of x^2 over the workgroup's columns of tile t.
+    // Lanes take the columns, then a xor butterfly adds across the wavefront; at
+    // every level both partners add the same two values, so all lanes end with
+    // the same bits.
+    float q[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) q[b] = 0.0f;
+    if (norm) {
+      for (int U = max(U0, ts) + lane; U < min(U1, te); U += 64) {
+        int ic = cs + U % cw - c0w;
+        if (ic < 0) ic += cw;
+#pragma unroll
+        for (int b = 0; b < B; ++b) q[b] += Q2[ic * B + b];
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+        for (int b = 0; b < B; ++b) q[b] += __shfl_xor(q[b], m);
+    }
+    if (a.n_win > 1) {
+      hand_off_windows<B, CHAIN>(a, t, w, lane, s, q);
+    } else if (ts >= U0 && te <= U1) {   // every tile when tiles_per_wg > 0
+      if (norm) rms_scale<B>(a, s, q);
+      write_tile<B, CHAIN>(a, t, lane, s);
+    } else {
+      hand_off<B, CHAIN>(a, t, lblock, NW * upw, lane, s, q);
+    }
   }
   return wait;
 }

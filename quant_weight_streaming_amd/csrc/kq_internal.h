@@ -10,6 +10,11 @@ namespace kq {
 
 
 // Kernel arguments of one GEMV launch (one or several projections sharing x).
+// floats per partial-sum slot: [KQ_MAX_BATCH][64] row sums, then (normalised
+// launches) the piece's sums of x^2 per batch row at kPartialQ
+constexpr int kPartialQ = KQ_MAX_BATCH * 64;
+constexpr int kPartialStride = kPartialQ + 64;
+
 struct GemvArgs {
   const uint8_t* w[KQ_MAX_PROJ];       // repacked weights of each projection
   float* y[KQ_MAX_PROJ];               // outputs
@@ -26,6 +31,7 @@ struct GemvArgs {
   int32_t tpw;                         // tiles a wavefront's run of units can touch (its LDS tile sums)
   uint32_t epi;                        // epilogue code of segment i in bits 4i..4i+3 (KQ_EPI_*); KQ_EPI_SWIGLU:
                                        // one segment whose tile t holds 32 gate and 32 up rows
+  float rms_eps;                       // > 0: x is normalised first, x / sqrt(mean(x^2) + rms_eps) per batch row
   // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
   // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even
@@ -83,10 +89,12 @@ inline bool dyn_units(int batch, int nw, bool mf) { return batch == 1 && nw == 8
 
 // `run_units`: units of one workgroup (the per-unit slots of dynamic workgroups);
 // `tpw`: tiles one wavefront's run can touch (its tile sums otherwise).
+// norm: the launch normalises x (sums of x^2 per staged column and batch row).
 inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols, int run_units,
-                             int tpw) {
-  const size_t partials = dyn_units(batch, nw, mf) ? 16 + (size_t)run_units * batch * 64 * sizeof(float)
-                                                   : (size_t)nw * tpw * batch * 64 * sizeof(float);
+                             int tpw, bool norm = false) {
+  const size_t partials = (dyn_units(batch, nw, mf) ? 16 + (size_t)run_units * batch * 64 * sizeof(float)
+                                                    : (size_t)nw * tpw * batch * 64 * sizeof(float)) +
+                          (norm ? (size_t)((staged_cols * batch + 3) & ~3) * sizeof(float) : 0);
   const int sb = type == KQ_Q6_K ? 16 : 8;
   if (mf) {
     const int nb = (batch + 3) / 4;

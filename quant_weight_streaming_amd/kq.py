@@ -26,7 +26,7 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4:
           10: "KQ_ERR_DEVICE"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
-           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_multi_epi", "kq_dequant", "kq_gather_rows",
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_fused", "kq_dequant", "kq_gather_rows",
            "kq_repack_swiglu",
            "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
            "kq_chain_status", "kq_chain_destroy")
@@ -38,7 +38,7 @@ class ChainStep(ctypes.Structure):
                 ("w", ctypes.c_void_p * KQ_MAX_PROJ), ("rows", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("epilogue", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float)]
 
 
 class KQError(RuntimeError):
@@ -74,9 +74,10 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_multi.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), vp]
         L.kq_gemv_multi.restype = ci
-        L.kq_gemv_multi_epi.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
-                                        ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32), vp]
-        L.kq_gemv_multi_epi.restype = ci
+        L.kq_gemv_fused.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
+                                    ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.c_float, vp]
+        L.kq_gemv_fused.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
         L.kq_gather_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, vp]
@@ -169,17 +170,20 @@ def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) 
                                                 x.shape[0], Y, LD, _stream(stream)))
 
 
-def kq_gemv_multi_epi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis, stream=None) -> None:
+def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rms_eps: float = 0.0,
+                  stream=None) -> None:
+    """kq_gemv_multi with a weight-less RMSNorm of x first (rms_eps > 0) and an epilogue code per segment
+    (epis: None for none)."""
     n = len(ws)
-    if len(rows) != n or len(ys) != n or len(epis) != n:
+    if len(rows) != n or len(ys) != n or (epis is not None and len(epis) != n):
         raise ValueError("ws, rows, ys and epis must have the same length")
     W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in ws])
     R = (ctypes.c_int64 * n)(*rows)
     Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
-    E = (ctypes.c_int32 * n)(*epis)
-    _check("kq_gemv_multi_epi", lib().kq_gemv_multi_epi(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x),
-                                                        x.stride(0), x.shape[0], Y, LD, E, _stream(stream)))
+    E = (ctypes.c_int32 * n)(*epis) if epis is not None else None
+    _check("kq_gemv_fused", lib().kq_gemv_fused(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
+                                                x.shape[0], Y, LD, E, rms_eps, _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:
@@ -209,11 +213,13 @@ def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tens
 
 
 def kq_chain_create(steps, xtype: int, batch: int) -> int:
-    """steps: sequence of (qtype, ws, rows, cols, x, ys) as kq_gemv_multi takes them; returns the handle."""
+    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps]]) as kq_gemv_multi takes them, the
+    epilogue packed four bits per segment; returns the handle."""
     arr = (ChainStep * len(steps))()
     for st, step in zip(arr, steps):
         qtype, ws, rows, cols, x, ys = step[:6]
         st.epilogue = step[6] if len(step) > 6 else KQ_EPI_NONE
+        st.rms_eps = step[7] if len(step) > 7 else 0.0
         n = len(ws)
         if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ:
             raise ValueError("ws, rows and ys must have the same length, at most KQ_MAX_PROJ")

@@ -184,20 +184,26 @@ def test_chain_rejects_bad_epilogue():
     assert kq.lib().kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 5
 
 
-def test_multi_epi_rejects():
+def test_fused_rejects():
     L = kq.lib()
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     W = (vp * 2)(A16, A16)
     R = (i64 * 2)(64, 64)
     Y = (vp * 2)(A16, A16)
     LD = (i64 * 2)(64, 64)
-    assert L.kq_gemv_multi_epi(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None) == 1
     E = (ctypes.c_int32 * 2)(2, 9)
-    assert L.kq_gemv_multi_epi(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, None) == 5      # unknown code
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, None) == 5      # unknown code
     E = (ctypes.c_int32 * 2)(1, 0)
-    assert L.kq_gemv_multi_epi(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, None) == 5      # SwiGLU has its own call
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, None) == 5      # SwiGLU needs n = 1
+    for eps in (-1e-5, float("inf"), float("nan")):
+        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, eps, None) == 2
+    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, 0.0, None) == 4
     st = _step()
     st.epilogue = 3 | (2 << 4)                    # a code for a segment the step does not have
     arr = (kq.ChainStep * 1)(st)
     h = ctypes.c_void_p()
     assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 5
+    st = _step()
+    st.rms_eps = -1.0
+    arr = (kq.ChainStep * 1)(st)
+    assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 2

@@ -1,4 +1,4 @@
-"""Sigmoid-gate and residual epilogues (kq_gemv_multi_epi) against the oracle.
+"""Sigmoid-gate and residual epilogues (kq_gemv_fused) against the oracle.
 
 sigmoid: |sigmoid'| <= 1/4, so |dy| <= 0.25e-4 a + 2^-21 sigmoid(y) (the GEMV tolerance carried
 through, plus the fp32 exp, add and divide).  residual: |dy| <= 1e-4 a + 2^-24 |r + y| (one fp32 add).
@@ -29,7 +29,7 @@ def test_qkvg_with_sigmoid_gate_and_residual(qtype, batch):
     res = torch.randn(batch, parts[2], generator=torch.Generator().manual_seed(5)) * 10
     ys = [torch.full((batch, r + 2), 7.0, device=DEV) for r in parts]
     ys[2][:, :parts[2]] = res.to(DEV)
-    kq.kq_gemv_multi_epi(qtype, ws, parts, cols, x.to(DEV), ys, epis)
+    kq.kq_gemv_fused(qtype, ws, parts, cols, x.to(DEV), ys, epis)
     torch.cuda.synchronize()
     for i, (g, r, y, e) in enumerate(zip(gs, parts, ys, epis)):
         yh = y.cpu().numpy()
@@ -65,7 +65,7 @@ def test_residual_in_a_chain():
     assert ch.status() == 0
     h1 = kq.gemv("q4k", w0, hidden, 256, x0)
     r1 = h1.clone()
-    kq.kq_gemv_multi_epi("q4k", [w1], [hidden], hidden, h1, [r1], [kq.KQ_EPI_RESIDUAL])
+    kq.kq_gemv_fused("q4k", [w1], [hidden], hidden, h1, [r1], [kq.KQ_EPI_RESIDUAL])
     torch.cuda.synchronize()
     assert torch.equal(h, h1) and torch.equal(r, r1), "the chain differs from the launches"
     ch.close()

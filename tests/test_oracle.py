@@ -97,3 +97,39 @@ def test_sigmoid_closed_forms():
     assert abs(O.sigmoid(math.log(3.0)) - 0.75) < 1e-15
     assert O.sigmoid(800.0) == 1.0 and O.sigmoid(-800.0) == 0.0
     assert np.allclose(O.silu(v), v * O.sigmoid(v), rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_pins():
+    """Hand-computed values, the unit mean square at eps = 0, scale invariance and the eps term."""
+    import math
+    x = np.array([[3.0, 4.0]])
+    assert np.allclose(O.rmsnorm(x, 0.0), [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=1e-15, atol=0)
+    assert (O.rmsnorm(np.ones((1, 4)), 3.0) == 0.5).all()             # 1 / sqrt(1 + 3)
+    assert (O.rmsnorm(np.full((2, 8), -2.0), 0.0) == -1.0).all()
+    r = np.random.default_rng(1).standard_normal((3, 1000))
+    n = O.rmsnorm(r, 0.0)
+    assert np.allclose(np.mean(n * n, axis=1), 1.0, rtol=1e-13)
+    assert np.allclose(O.rmsnorm(7.5 * r, 0.0), n, rtol=1e-13, atol=0)
+    m = np.mean(r * r, axis=1)
+    assert np.allclose(np.mean(O.rmsnorm(r, 0.25) ** 2, axis=1), m / (m + 0.25), rtol=1e-13)
+    assert (O.rmsnorm(np.zeros((1, 16)), 1e-5) == 0.0).all()
+
+
+def test_gemv_rmsnorm_is_the_scaled_gemv():
+    """W rmsnorm(x) equals the oracle GEMV of x divided by rms(x) (the C oracle's own dot products), for bf16
+    bits and fp32 x; and a zero x row gives y = a = 0."""
+    import torch
+    from quant_weight_streaming_amd import synth
+    rows, cols = 70, 512
+    g = synth.gen_weights("q6k", rows, cols, synth.seed_of("onorm"))
+    xb = synth.gen_x(2, cols, synth.seed_of("onorm-x"), "bf16").view(torch.int16).numpy().view(np.uint16)
+    y0, a0 = O.gemv("q6k", rows, cols, g.numpy(), xb)
+    xd = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rms = np.sqrt(np.mean(xd * xd, axis=1, keepdims=True) + 1e-5)
+    y, a = O.gemv_rmsnorm("q6k", rows, cols, g.numpy(), xb, 1e-5)
+    assert np.allclose(y, y0 / rms, rtol=0, atol=1e-12 * (a0 / rms).max())
+    assert np.allclose(a, a0 / rms, rtol=1e-12)
+    xf = synth.gen_x(1, cols, synth.seed_of("onorm-xf"), "f32").numpy()
+    xf[0, :] = 0.0
+    y, a = O.gemv_rmsnorm("q6k", rows, cols, g.numpy(), xf, 1e-8)
+    assert (y == 0).all() and (a == 0).all()
