@@ -235,8 +235,13 @@ int kq_gather_rows(int type, const void *w, int64_t rows, int64_t cols, const in
  * step j+1 issues its first weight loads while step j drains, and reads its
  * activations only after every output of step j has been written.  So x of step
  * j+1 may be y of step j (or of any earlier step): fp32 activations, with ldx
- * = ldy.  The results are those of the same kq_gemv_multi calls made in order
- * (bitwise: each step runs the same arithmetic in the same order).
+ * = ldy.  A chain runs 8-wavefront workgroups, one per CU (KQ_WG_WAVES = 4 or 8
+ * sets the shape of chains and single launches alike).  Single launches use the
+ * same shape above batch 1; at batch 1 they default to two 4-wavefront
+ * workgroups per CU.  With the same shape the results are those of the same
+ * kq_gemv_multi calls made in order (bitwise: each step runs the same
+ * arithmetic in the same order); otherwise each step is within the GEMV's
+ * tolerance of them.
  *
  * kq_chain_step describes one step exactly as kq_gemv_multi takes it (n = 1 for
  * a single matrix).  All steps share xtype and batch.

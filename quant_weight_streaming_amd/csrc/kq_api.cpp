@@ -125,11 +125,26 @@ static int matrix_cores_from() {
   return (x >= 2 && x <= 9) ? x : 3;
 }
 
+// Wavefronts per workgroup of a single launch (KQ_WG_WAVES = 4 or 8
+// overrides): two 4-wavefront workgroups per CU at batch 1, whose larger number
+// of waves in flight shortens the launch's start; one 8-wavefront workgroup
+// per CU above.
 static int wg_waves(int batch) {
   const char* e = getenv("KQ_WG_WAVES");
   const int x = e ? atoi(e) : 0;
   if (x == 4 || x == 8) return x;
   return batch == 1 ? 4 : 8;
+}
+
+// Wavefronts per workgroup of a chain (KQ_WG_WAVES overrides): 8 at every
+// batch.  With two 4-wavefront workgroups on a CU the older one's waves win the
+// issue arbitration, so the pair ends a step several microseconds apart and the
+// CU runs half-empty until the step barrier; at batch 1 the eight wavefronts
+// of one workgroup instead take its units one at a time.
+static int chain_wg_waves() {
+  const char* e = getenv("KQ_WG_WAVES");
+  const int x = e ? atoi(e) : 0;
+  return (x == 4 || x == 8) ? x : 8;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS of one CU
@@ -256,6 +271,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     }
   }
   if (!even_ok) return KQ_ERR_RANGE;
+  const int64_t wgu = (int64_t)nw * upw;
+  a.wgu = (int32_t)wgu;
   a.nproj = n;
   a.n_cols = (int32_t)n_cols;
   a.x = x;
@@ -269,7 +286,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   out->nw = nw;
   out->mf = mf;
   out->grid = grid;
-  const int64_t run_units = a.tiles_per_wg > 0 ? (int64_t)a.tiles_per_wg * tcols : nw * upw;
+  const int64_t run_units = a.tiles_per_wg > 0 ? (int64_t)a.tiles_per_wg * tcols : wgu;
   // a run of u units starting anywhere in a tile of c columns touches at most
   // ceil((u - 1) / c) + 1 tiles
   if (a.tiles_per_wg > 0) {
@@ -529,7 +546,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   kq_chain* c = new (std::nothrow) kq_chain;
   if (!c) return KQ_ERR_NOMEM;
   std::vector<Plan> plans(n_steps);
-  int nw = wg_waves(batch);
+  int nw = chain_wg_waves();
   auto plan_all = [&](int64_t max_grid, size_t* lds) {
     *lds = 0;
     for (int j = 0; j < n_steps; ++j) {

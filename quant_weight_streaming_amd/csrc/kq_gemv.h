@@ -816,9 +816,9 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     upw = (a.tiles_per_wg * cw + NW - 1) / NW;
   } else {
     upw = a.upw;
-    U0 = lblock * NW * upw;
+    U0 = lblock * a.wgu;
     if (U0 >= a.n_units) return false;               // whole workgroup idle
-    U1 = min(U0 + NW * upw, a.n_units);
+    U1 = min(U0 + a.wgu, a.n_units);
   }
   const int c0w = cs + U0 % cw;                    // staged columns c0w, c0w+1, ... (mod n_cols)
   const int len = min(cw, U1 - U0);
@@ -1053,7 +1053,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
       if (norm) rms_scale<B>(a, s, q);
       write_tile<B, CHAIN>(a, t, lane, s);
     } else {
-      hand_off<B, CHAIN>(a, t, lblock, NW * upw, lane, s, q);
+      hand_off<B, CHAIN>(a, t, lblock, a.wgu, lane, s, q);
     }
   }
   return wait;

@@ -27,6 +27,8 @@ struct GemvArgs {
   int64_t ldx;                         // activation row stride (elements)
   int32_t n_units;                     // total tiles * n_cols
   int32_t upw;                         // units per wavefront
+  int32_t wgu;                         // units per workgroup: nw * upw, or (units taken dynamically by
+                                       // the wavefronts) an even share of the units per CU
   int32_t tsb;                         // LDS capacity in staged columns per workgroup
   int32_t tpw;                         // tiles a wavefront's run of units can touch (its LDS tile sums)
   uint32_t epi;                        // epilogue code of segment i in bits 4i..4i+3 (KQ_EPI_*); KQ_EPI_SWIGLU:

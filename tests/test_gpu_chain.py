@@ -18,6 +18,13 @@ from tests.gpu_cases import check_y, say, x_host
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _chain_shape(monkeypatch):
+    """Single launches with the chain's workgroup shape (8 wavefronts; at batch 1 single launches default to 4),
+    so a chain step and its single launch run the same arithmetic in the same order."""
+    monkeypatch.setenv("KQ_WG_WAVES", "8")
 SENTINEL = 1.0e30
 
 
