@@ -200,10 +200,11 @@ def test_chain_graph_replay():
 def test_chain_wait_that_gives_up_is_reported(monkeypatch):
     """With no polls allowed (KQ_CHAIN_SPIN=0) a wait that finds the previous step unfinished gives up:
     the run ends and kq_chain_status says so (the results are then invalid); a chain made with the
-    default limit afterwards runs clean."""
+    default limit afterwards runs clean.  Step 1 gives every workgroup work, so every workgroup waits
+    for step 0, and the first to finish step 0 finds it unfinished."""
     batch = 1
     say("case chain spin 0")
-    specs = [("q6k", (64 * 64,), 122 * 256), ("q4k", (256,), 1024), ("q4k", (256,), 1024)]
+    specs = [("q6k", (64 * 64,), 122 * 256), ("q4k", (16384,), 4096), ("q4k", (256,), 1024)]
     steps, hosts = _independent_steps(specs, batch, "bf16", "spin")
     monkeypatch.setenv("KQ_CHAIN_SPIN", "0")
     ch = kq.Chain(steps, batch)
