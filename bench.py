@@ -213,7 +213,7 @@ def time_swiglu(inter: int, cols: int, batches, copies: int = 6, reps: int = 4) 
 
 def time_fused(parts, cols: int, batches, variants, copies: int = 6, reps: int = 4) -> dict:
     """Mean launch time of one fused multi-projection launch (Q4_K, row segments `parts`) per variant
-    (name -> (epilogue codes or None, rms_eps)), over `copies` distinct weight sets."""
+    (name -> (epilogue codes or None, rms_eps[, head_eps])), over `copies` distinct weight sets."""
     import torch
     from quant_weight_streaming_amd import kq, synth
     rows = sum(parts)
@@ -227,7 +227,9 @@ def time_fused(parts, cols: int, batches, variants, copies: int = 6, reps: int =
         sets.append(ws)
         del g
     out = {}
-    for name, (epis, eps) in variants.items():
+    for name, var in variants.items():
+        epis, eps = var[0], var[1]
+        heps = var[2] if len(var) > 2 else 0.0
         out[name] = {}
         for B in batches:
             x = synth.gen_x(B, cols, synth.seed_of("bench-fused-x", B), device="cuda:0")
@@ -236,10 +238,10 @@ def time_fused(parts, cols: int, batches, variants, copies: int = 6, reps: int =
             s.wait_stream(torch.cuda.current_stream())
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.stream(s):
-                kq.kq_gemv_fused("q4k", sets[0], list(parts), cols, x, ys, epis, eps, s)
+                kq.kq_gemv_fused("q4k", sets[0], list(parts), cols, x, ys, epis, eps, s, heps)
                 with torch.cuda.graph(graph, stream=s):
                     for ws in sets:
-                        kq.kq_gemv_fused("q4k", ws, list(parts), cols, x, ys, epis, eps, s)
+                        kq.kq_gemv_fused("q4k", ws, list(parts), cols, x, ys, epis, eps, s, heps)
             torch.cuda.current_stream().wait_stream(s)
             graph.replay()
             torch.cuda.synchronize()
@@ -584,7 +586,9 @@ def main():
     qkvg = synth.QKVG_P4
     fused_us = time_fused(qkvg.parts, qkvg.cols, (1, 8), {
         "plain": (None, 0.0),
-        "rmsnorm_and_sigmoid_gate": ([kq.KQ_EPI_NONE] * 3 + [kq.KQ_EPI_SIGMOID], 1e-5)})
+        "rmsnorm_and_sigmoid_gate": ([kq.KQ_EPI_NONE] * 3 + [kq.KQ_EPI_SIGMOID], 1e-5),
+        "rmsnorm_qk_head_norm_sigmoid_gate": ([kq.KQ_EPI_HEADNORM] * 2 + [kq.KQ_EPI_NONE, kq.KQ_EPI_SIGMOID],
+                                              1e-5, 1e-6)})
     log(f"[bench] fused QKVG 8704x6656: {fused_us} us")
     log(f"[bench] gate+up with SwiGLU epilogue (Q4_K 2 x {synth.INTER}x{synth.HIDDEN}): {swiglu_us} us "
         f"(plain gate+up: {kt1['gate_up']['avg_us']} / {kt8['gate_up']['avg_us']} us)")

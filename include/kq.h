@@ -76,6 +76,8 @@ extern "C" {
 #define KQ_EPI_SWIGLU 1    /* silu(gate) * up, see kq_gemv_swiglu */
 #define KQ_EPI_SIGMOID 2   /* y = 1 / (1 + exp(-(W x))): the attention output gate */
 #define KQ_EPI_RESIDUAL 3  /* y = y + W x: y holds the residual stream on entry */
+#define KQ_EPI_HEADNORM 4  /* weight-less RMSNorm of each KQ_HEAD_ROWS outputs (the Q and K heads) */
+#define KQ_HEAD_ROWS 128   /* outputs per head of a KQ_EPI_HEADNORM segment (head_dim) */
 
 /* status codes */
 #define KQ_OK 0
@@ -179,13 +181,20 @@ int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, 
  *                   the residual add that closes the attention and feed-forward
  *                   blocks around the O and down projections (a segment's y must
  *                   not overlap another segment's);
+ *   KQ_EPI_HEADNORM the card's weight-less RMSNorm on Q/K: every KQ_HEAD_ROWS
+ *                   consecutive outputs of the segment form a head, and
+ *                   y = v / sqrt(mean over the head of v^2 + head_eps) per batch
+ *                   row.  rows[i] must be a multiple of KQ_HEAD_ROWS and
+ *                   head_eps finite and > 0 (else KQ_ERR_SHAPE); a launch with
+ *                   such a segment has at most 8192 tiles of 64 rows in total
+ *                   (else KQ_ERR_RANGE).  head_eps is ignored without one;
  *   KQ_EPI_SWIGLU   n = 1 only, w from kq_repack_swiglu and rows[0] = inter:
  *                   as kq_gemv_swiglu.
  * Otherwise as kq_gemv_multi; KQ_ERR_TYPE for an unknown code.
  */
 int kq_gemv_fused(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
                   int64_t ldx, int batch, float *const *y, const int64_t *ldy, const int32_t *epi, float rms_eps,
-                  void *stream);
+                  float head_eps, void *stream);
 
 /*
  * SwiGLU epilogue: the gate and up projections of the feed-forward block in one
@@ -259,6 +268,8 @@ typedef struct kq_chain_step {
   int32_t epilogue;               /* segment i's KQ_EPI_* code in bits 4i..4i+3 (KQ_EPI_SWIGLU: n = 1,
                                      w from kq_repack_swiglu, rows[0] = inter) */
   float rms_eps;                  /* > 0: weight-less RMSNorm of x first, as kq_gemv_fused; 0: none */
+  float head_eps;                 /* epsilon of KQ_EPI_HEADNORM segments, as kq_gemv_fused */
+  int32_t reserved;               /* set to 0 */
 } kq_chain_step;
 
 typedef struct kq_chain kq_chain;

@@ -13,6 +13,7 @@ Functions:
   silu(g), swiglu(g, u)                 the SwiGLU feed-forward's activation in fp64
   sigmoid(v)                            the attention output gate, fp64
   rmsnorm(x, eps)                       the weight-less RMSNorm, fp64
+  head_rmsnorm(v, eps, head_rows)       the same per head of consecutive outputs (Q/K norm), fp64
   gemv_rmsnorm(...)                     W (rmsnorm(x)) from the fp64 dequantised W, fp64
   gather(qtype, rows, cols, gguf, ids)  rows ids of dequant_f32 (the embedding lookup)
 """
@@ -160,6 +161,17 @@ def rmsnorm(x, eps):
     the embedding output and to Q/K).  x: float rows [batch, K]."""
     x = np.asarray(x, dtype=np.float64)
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def head_rmsnorm(v, eps, head_rows=128):
+    """The weight-less RMSNorm of each head of `head_rows` consecutive outputs, per batch row, in fp64: the card's
+    norm on Q/K, whose heads are 128 wide (head_dim).  v: [batch, rows] with rows a multiple of head_rows."""
+    v = np.asarray(v, dtype=np.float64)
+    b, r = v.shape
+    if r % head_rows:
+        raise ValueError("rows must be a multiple of head_rows")
+    h = v.reshape(b, r // head_rows, head_rows)
+    return (h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)).reshape(b, r)
 
 
 def gemv_rmsnorm(qtype, rows, cols, gguf, x, eps):

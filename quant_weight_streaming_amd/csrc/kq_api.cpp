@@ -31,8 +31,13 @@ int64_t sb_bytes(int type) {
 // calls (the last arrival of a tile resets its counter), so they are cleared
 // once, at allocation.
 constexpr int kMaxGroups = 8192;
-constexpr size_t kPartialBytes = (size_t)kMaxGroups * 2 * kPartialStride * sizeof(float);
-constexpr size_t kCounterBytes = (size_t)kMaxGroups * sizeof(uint32_t);
+// then the per-head sums of squares of KQ_EPI_HEADNORM launches ([tile][2][KQ_MAX_BATCH]),
+// and after the tile counters one counter per head
+constexpr size_t kPartialFloats = (size_t)kMaxGroups * 2 * kPartialStride;
+constexpr size_t kHeadSsFloats = (size_t)kMaxGroups * 2 * KQ_MAX_BATCH;
+constexpr size_t kPartialBytes = (kPartialFloats + kHeadSsFloats) * sizeof(float);
+constexpr size_t kCounterBytes = (size_t)2 * kMaxGroups * sizeof(uint32_t);
+static_assert(kHeadRows == 2 * 64, "a head is two row tiles");
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
@@ -185,13 +190,14 @@ struct Plan {
 // per 64-row tile.
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
-                     int64_t max_grid, int force_nw, uint32_t epi, float rms_eps, float* partial,
+                     int64_t max_grid, int force_nw, uint32_t epi, float rms_eps, float head_eps, float* partial,
                      uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
   const bool norm = rms_eps > 0.0f;
   GemvArgs a{};
   a.epi = epi;
   a.rms_eps = rms_eps;
+  a.head_eps = head_eps;
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) {
     if (rows[i] > (int64_t)INT32_MAX - 64) return KQ_ERR_RANGE;
@@ -204,6 +210,9 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     if (tiles > INT32_MAX) return KQ_ERR_RANGE;
   }
   for (int i = n; i <= KQ_MAX_PROJ; ++i) a.tile_begin[i] = (int32_t)tiles;
+  bool heads = false;
+  for (int i = 0; i < n; ++i) heads |= ((epi >> (4 * i)) & 15u) == (uint32_t)KQ_EPI_HEADNORM;
+  if (heads && tiles > kMaxGroups) return KQ_ERR_RANGE;   // the head scratch is indexed by tile
   const int64_t n_units = tiles * n_cols;
   if (n_units + 2 * n_cols + 8 * (int64_t)kMaxGroups >= INT32_MAX) return KQ_ERR_RANGE;
   const int64_t max_groups = max_grid < kMaxGroups ? max_grid : kMaxGroups;
@@ -282,6 +291,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   a.tsb = (int32_t)tcols;
   a.partial = partial;
   a.counters = counters;
+  a.head_ss = partial ? partial + kPartialFloats : nullptr;
+  a.head_ctr = counters ? counters + kMaxGroups : nullptr;
   out->a = a;
   out->nw = nw;
   out->mf = mf;
@@ -301,15 +312,32 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   return KQ_OK;
 }
 
+static bool segment_code(int32_t c) {
+  return c == KQ_EPI_NONE || c == KQ_EPI_SIGMOID || c == KQ_EPI_RESIDUAL || c == KQ_EPI_HEADNORM;
+}
+
 // Packed per-segment epilogue codes are valid: SwiGLU alone on a single matrix,
-// else sigmoid / residual / none on each of the n segments.
+// else none / sigmoid / residual / head norm on each of the n segments.
 static bool valid_epilogue(int n, uint32_t epi) {
   if (epi == (uint32_t)KQ_EPI_SWIGLU) return n == 1;
   for (int i = 0; i < 8; ++i) {
     const uint32_t c = (epi >> (4 * i)) & 15u;
-    if (i >= n ? c != 0 : (c != KQ_EPI_NONE && c != KQ_EPI_SIGMOID && c != KQ_EPI_RESIDUAL)) return false;
+    if (i >= n ? c != 0 : !segment_code((int32_t)c)) return false;
   }
   return true;
+}
+
+// Head-norm segments hold whole heads, and their epsilon is finite and > 0.
+static int check_heads(int n, const int64_t* rows, uint32_t epi, float head_eps) {
+  if (epi == (uint32_t)KQ_EPI_SWIGLU) return KQ_OK;
+  bool heads = false;
+  for (int i = 0; i < n; ++i) {
+    if (((epi >> (4 * i)) & 15u) != (uint32_t)KQ_EPI_HEADNORM) continue;
+    heads = true;
+    if (rows[i] % kHeadRows != 0) return KQ_ERR_SHAPE;
+  }
+  if (heads && !(head_eps > 0.0f && head_eps <= FLT_MAX)) return KQ_ERR_SHAPE;
+  return KQ_OK;
 }
 
 // The weight-less RMSNorm's epsilon: 0 (no normalisation) or finite and > 0.
@@ -317,21 +345,25 @@ static bool valid_rms_eps(float e) { return e == 0.0f || (e > 0.0f && e <= FLT_M
 
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream,
-                     uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f) {
+                     uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f, float head_eps = 0.0f) {
   int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
   if (rc != KQ_OK) return rc;
   if (!valid_epilogue(n, epi)) return KQ_ERR_TYPE;
   if (!valid_rms_eps(rms_eps)) return KQ_ERR_SHAPE;
+  rc = check_heads(n, rows, epi, head_eps);
+  if (rc != KQ_OK) return rc;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
   DeviceState* st = nullptr;
   rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
   Plan p{};
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, rms_eps, st->partial,
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, rms_eps, head_eps,
+                 st->partial,
                  st->counters, &p);
   if (rc == KQ_ERR_RANGE && wg_waves(batch) == 8)   // too many units per workgroup for per-unit slots: 4-wavefront runs
-    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, rms_eps, st->partial,
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, rms_eps, head_eps,
+                   st->partial,
                    st->counters, &p);
   if (rc != KQ_OK) return rc;
   if (launch_gemv(type, xtype, batch, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
@@ -449,7 +481,7 @@ int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void* gate, co
 
 int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x, int xtype,
                   int64_t ldx, int batch, float* const* y, const int64_t* ldy, const int32_t* epi, float rms_eps,
-                  void* stream) {
+                  float head_eps, void* stream) {
   if (n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
   uint32_t packed = 0;
   if (epi) {
@@ -458,12 +490,12 @@ int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, in
       if (rows && rows[0] > (int64_t)INT32_MAX / 2 - 64) return KQ_ERR_RANGE;
     } else {
       for (int i = 0; i < n; ++i) {
-        if (epi[i] != KQ_EPI_NONE && epi[i] != KQ_EPI_SIGMOID && epi[i] != KQ_EPI_RESIDUAL) return KQ_ERR_TYPE;
+        if (!segment_code(epi[i])) return KQ_ERR_TYPE;
         packed |= (uint32_t)epi[i] << (4 * i);
       }
     }
   }
-  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed, rms_eps);
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed, rms_eps, head_eps);
 }
 
 int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,
@@ -533,6 +565,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     if (rc != KQ_OK) return rc;
     if (!valid_epilogue(st.n, (uint32_t)st.epilogue)) return KQ_ERR_TYPE;
     if (!valid_rms_eps(st.rms_eps)) return KQ_ERR_SHAPE;
+    const int hrc = check_heads(st.n, st.rows, (uint32_t)st.epilogue, st.head_eps);
+    if (hrc != KQ_OK) return hrc;
     if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
   int dev = 0;
@@ -552,7 +586,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     for (int j = 0; j < n_steps; ++j) {
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
-                         max_grid, nw, (uint32_t)st.epilogue, st.rms_eps, nullptr, nullptr, &plans[j]);
+                         max_grid, nw, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, nullptr, nullptr, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && batch <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;
@@ -601,6 +635,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     h[j].a = plans[j].a;
     h[j].a.partial = d_partial;
     h[j].a.counters = d_counters;
+    h[j].a.head_ss = d_partial + kPartialFloats;
+    h[j].a.head_ctr = d_counters + kMaxGroups;
     h[j].type = steps[j].type;
     h[j].grid = (int32_t)plans[j].grid;
   }

@@ -550,6 +550,61 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
   }
 }
 
+// Weight-less RMSNorm of each head of kHeadRows outputs of a segment (the Q
+// and K heads): y = v / sqrt(mean over the head of v^2 + head_eps) per batch
+// row.  A head is two tiles, whose writers may be different workgroups: each
+// stores its raw values and its sum of squares (a xor butterfly, the same bits
+// in every lane) through the coherence point, waits for them, and bumps the
+// head's counter; the second to arrive adds the two sums in tile order, scales
+// its own values and re-reads, scales and rewrites the other tile's.  The
+// counter is reset for the next call.
+template <int B, class GA>
+__device__ __forceinline__ void head_norm_tile(GA& a, int t, int p, int lane, const float* v) {
+  const int tl = t - a.tile_begin[p], par = tl & 1, h0 = t - par;
+  float* y = a.y[p];
+  const int64_t ldy = a.ldy[p];
+  const int row = tl * kTileRows + lane;
+  float q[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) q[b] = v[b] * v[b];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+    for (int b = 0; b < B; ++b) q[b] += __shfl_xor(q[b], m);
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+    __hip_atomic_store(y + b * ldy + row, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* hs = a.head_ss + ((int64_t)h0 * 2 + par) * KQ_MAX_BATCH;
+  float mine = 0.0f;
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+    if (lane == b) mine = q[b];
+  if (lane < B) __hip_atomic_store(hs + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(a.head_ctr + h0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old == 0) return;                      // the head's other tile finishes it
+  asm volatile("" ::: "memory");
+  const float* ho = a.head_ss + ((int64_t)h0 * 2 + (par ^ 1)) * KQ_MAX_BATCH;
+  const float qo = lane < B ? __hip_atomic_load(ho + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+  float sc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const float other = __shfl(qo, b);
+    const float tot = par ? other + q[b] : q[b] + other;   // tile 0's sum first
+    sc[b] = 1.0f / sqrtf(tot / (float)kHeadRows + a.head_eps);
+  }
+  const int row_o = (tl ^ 1) * kTileRows + lane;
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    __hip_atomic_store(y + b * ldy + row, v[b] * sc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float vo = __hip_atomic_load(y + b * ldy + row_o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(y + b * ldy + row_o, vo * sc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (lane == 0) __hip_atomic_store(a.head_ctr + h0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Write finished row sums of tile t (all of its columns) to y; COH: write
 // through to the device coherence point (read later in the same launch).
 template <int B, bool COH, class GA>
@@ -579,6 +634,10 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
     if (i < a.nproj && t >= a.tile_begin[i]) p = i;
   const int row = (t - a.tile_begin[p]) * kTileRows + lane;
   const uint32_t code = (a.epi >> (4 * p)) & 15u;
+  if (code == KQ_EPI_HEADNORM) {
+    head_norm_tile<B>(a, t, p, lane, v);
+    return;
+  }
   if (row < a.rows[p]) {
     float* y = a.y[p];
     const int64_t ldy = a.ldy[p];

@@ -12,6 +12,7 @@ namespace kq {
 // Kernel arguments of one GEMV launch (one or several projections sharing x).
 // floats per partial-sum slot: [KQ_MAX_BATCH][64] row sums, then (normalised
 // launches) the piece's sums of x^2 per batch row at kPartialQ
+constexpr int kHeadRows = 128;        // outputs per head of a KQ_EPI_HEADNORM segment (head_dim)
 constexpr int kPartialQ = KQ_MAX_BATCH * 64;
 constexpr int kPartialStride = kPartialQ + 64;
 
@@ -34,6 +35,9 @@ struct GemvArgs {
   uint32_t epi;                        // epilogue code of segment i in bits 4i..4i+3 (KQ_EPI_*); KQ_EPI_SWIGLU:
                                        // one segment whose tile t holds 32 gate and 32 up rows
   float rms_eps;                       // > 0: x is normalised first, x / sqrt(mean(x^2) + rms_eps) per batch row
+  float head_eps;                      // KQ_EPI_HEADNORM segments: the per-head norm's epsilon
+  float* head_ss;                      // scratch: [tile][2][KQ_MAX_BATCH] sums of squares of the heads' tiles
+  uint32_t* head_ctr;                  // scratch: arrival counters per head (by its first tile), zero between calls
   // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
   // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even

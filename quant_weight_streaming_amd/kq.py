@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libkq.so")
 KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 1, 2, 3
 KQ_X_F32, KQ_X_BF16 = 0, 1
 KQ_MAX_BATCH, KQ_MAX_BATCH_F32, KQ_MAX_PROJ = 16, 8, 8
-KQ_EPI_NONE, KQ_EPI_SWIGLU, KQ_EPI_SIGMOID, KQ_EPI_RESIDUAL = 0, 1, 2, 3
+KQ_EPI_NONE, KQ_EPI_SWIGLU, KQ_EPI_SIGMOID, KQ_EPI_RESIDUAL, KQ_EPI_HEADNORM = 0, 1, 2, 3, 4
+KQ_HEAD_ROWS = 128
 TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
@@ -38,7 +39,7 @@ class ChainStep(ctypes.Structure):
                 ("w", ctypes.c_void_p * KQ_MAX_PROJ), ("rows", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("epilogue", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("head_eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
 class KQError(RuntimeError):
@@ -76,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_multi.restype = ci
         L.kq_gemv_fused.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32),
-                                    ctypes.c_float, vp]
+                                    ctypes.c_float, ctypes.c_float, vp]
         L.kq_gemv_fused.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
@@ -171,9 +172,9 @@ def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) 
 
 
 def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rms_eps: float = 0.0,
-                  stream=None) -> None:
+                  stream=None, head_eps: float = 0.0) -> None:
     """kq_gemv_multi with a weight-less RMSNorm of x first (rms_eps > 0) and an epilogue code per segment
-    (epis: None for none)."""
+    (epis: None for none; KQ_EPI_HEADNORM segments use head_eps)."""
     n = len(ws)
     if len(rows) != n or len(ys) != n or (epis is not None and len(epis) != n):
         raise ValueError("ws, rows, ys and epis must have the same length")
@@ -183,7 +184,7 @@ def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rm
     LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
     E = (ctypes.c_int32 * n)(*epis) if epis is not None else None
     _check("kq_gemv_fused", lib().kq_gemv_fused(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
-                                                x.shape[0], Y, LD, E, rms_eps, _stream(stream)))
+                                                x.shape[0], Y, LD, E, rms_eps, head_eps, _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:
@@ -213,13 +214,14 @@ def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tens
 
 
 def kq_chain_create(steps, xtype: int, batch: int) -> int:
-    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps]]) as kq_gemv_multi takes them, the
-    epilogue packed four bits per segment; returns the handle."""
+    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps[, head_eps]]]) as kq_gemv_multi takes
+    them, the epilogue packed four bits per segment; returns the handle."""
     arr = (ChainStep * len(steps))()
     for st, step in zip(arr, steps):
         qtype, ws, rows, cols, x, ys = step[:6]
         st.epilogue = step[6] if len(step) > 6 else KQ_EPI_NONE
         st.rms_eps = step[7] if len(step) > 7 else 0.0
+        st.head_eps = step[8] if len(step) > 8 else 0.0
         n = len(ws)
         if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ:
             raise ValueError("ws, rows and ys must have the same length, at most KQ_MAX_PROJ")

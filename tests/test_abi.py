@@ -192,12 +192,19 @@ def test_fused_rejects():
     Y = (vp * 2)(A16, A16)
     LD = (i64 * 2)(64, 64)
     E = (ctypes.c_int32 * 2)(2, 9)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, None) == 5      # unknown code
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, 0.0, None) == 5      # unknown code
     E = (ctypes.c_int32 * 2)(1, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, None) == 5      # SwiGLU needs n = 1
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, 0.0, None) == 5      # SwiGLU needs n = 1
     for eps in (-1e-5, float("inf"), float("nan")):
-        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, eps, None) == 2
-    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, 0.0, None) == 4
+        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, eps, 0.0, None) == 2
+    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, 0.0, 0.0, None) == 4
+    # head norm: rows a multiple of KQ_HEAD_ROWS, head_eps finite and > 0
+    E = (ctypes.c_int32 * 2)(4, 0)
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, 1e-6, None) == 2    # 64 rows
+    R2 = (i64 * 2)(128, 64)
+    LD2 = (i64 * 2)(128, 64)
+    for eps in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.kq_gemv_fused(1, 2, W, R2, 256, A16, 1, 256, 1, Y, LD2, E, 0.0, eps, None) == 2
     st = _step()
     st.epilogue = 3 | (2 << 4)                    # a code for a segment the step does not have
     arr = (kq.ChainStep * 1)(st)
@@ -205,5 +212,8 @@ def test_fused_rejects():
     assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 5
     st = _step()
     st.rms_eps = -1.0
+    arr = (kq.ChainStep * 1)(st)
+    assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 2
+    st = _step(epilogue=4, head_eps=1e-6)           # a head-norm segment of 64 rows
     arr = (kq.ChainStep * 1)(st)
     assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 2

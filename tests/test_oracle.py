@@ -133,3 +133,24 @@ def test_gemv_rmsnorm_is_the_scaled_gemv():
     xf[0, :] = 0.0
     y, a = O.gemv_rmsnorm("q6k", rows, cols, g.numpy(), xf, 1e-8)
     assert (y == 0).all() and (a == 0).all()
+
+
+def test_head_rmsnorm_pins():
+    """Per-head closed forms: a constant head c maps to c / sqrt(c^2 + eps); heads are independent; every head of
+    the output has mean square m / (m + eps) of its input's mean square m."""
+    import math
+    v = np.concatenate([np.full((1, 128), 3.0), np.full((1, 128), -0.5)], axis=1)
+    out = O.head_rmsnorm(v, 0.25)
+    assert np.allclose(out[0, :128], 3.0 / math.sqrt(9.25), rtol=1e-15)
+    assert np.allclose(out[0, 128:], -0.5 / math.sqrt(0.5), rtol=1e-15)
+    r = np.random.default_rng(2).standard_normal((2, 512))
+    a = O.head_rmsnorm(r, 1e-3)
+    r2 = r.copy()
+    r2[:, 128:256] *= 100.0                        # only head 1 changes
+    b = O.head_rmsnorm(r2, 1e-3)
+    assert (a[:, :128] == b[:, :128]).all() and (a[:, 256:] == b[:, 256:]).all()
+    m = np.mean(r.reshape(2, 4, 128) ** 2, axis=-1)
+    got = np.mean(a.reshape(2, 4, 128) ** 2, axis=-1)
+    assert np.allclose(got, m / (m + 1e-3), rtol=1e-13)
+    with pytest.raises(ValueError):
+        O.head_rmsnorm(np.ones((1, 100)), 1e-6)
