@@ -595,13 +595,17 @@ __device__ __forceinline__ void head_norm_tile(GA& a, int t, int p, int lane, co
     const float tot = par ? other + q[b] : q[b] + other;   // tile 0's sum first
     sc[b] = 1.0f / sqrtf(tot / (float)kHeadRows + a.head_eps);
   }
+  // every read of the other tile goes out before the first store (one round trip, not B)
   const int row_o = (tl ^ 1) * kTileRows + lane;
+  float vo[B];
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < B; ++b) vo[b] = __hip_atomic_load(y + b * ldy + row_o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int b = 0; b < B; ++b)
     __hip_atomic_store(y + b * ldy + row, v[b] * sc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float vo = __hip_atomic_load(y + b * ldy + row_o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(y + b * ldy + row_o, vo * sc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+    __hip_atomic_store(y + b * ldy + row_o, vo[b] * sc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (lane == 0) __hip_atomic_store(a.head_ctr + h0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -641,17 +645,26 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
   if (row < a.rows[p]) {
     float* y = a.y[p];
     const int64_t ldy = a.ldy[p];
+    float o[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) o[b] = v[b];
+    if (code == KQ_EPI_SIGMOID) {                // the attention output gate
+#pragma unroll
+      for (int b = 0; b < B; ++b) o[b] = 1.0f / (1.0f + expf(-o[b]));
+    } else if (code == KQ_EPI_RESIDUAL) {        // y holds the residual stream on entry
+      float r[B];                                // every read goes out before the first store
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float* yp = y + b * ldy + row;
+        r[b] = COH ? __hip_atomic_load(yp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *yp;
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) o[b] += r[b];
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      float o = v[b];
-      if (code == KQ_EPI_SIGMOID) {
-        o = 1.0f / (1.0f + expf(-o));            // the attention output gate
-      } else if (code == KQ_EPI_RESIDUAL) {      // y holds the residual stream on entry
-        float* yp = y + b * ldy + row;
-        o += COH ? __hip_atomic_load(yp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *yp;
-      }
-      if constexpr (COH) __hip_atomic_store(y + b * ldy + row, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else y[b * ldy + row] = o;
+      if constexpr (COH) __hip_atomic_store(y + b * ldy + row, o[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else y[b * ldy + row] = o[b];
     }
   }
 }
