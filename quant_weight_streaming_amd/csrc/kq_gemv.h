@@ -1087,8 +1087,23 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
 #pragma unroll
     for (int b = 0; b < B; ++b) s[b] = 0.0f;
     if constexpr (DYN) {
+      // the tile's unit slots in unit order; four slots are read before they
+      // are added, so the reads overlap (the order of the additions is kept)
       const float* S = P + 4;
-      for (int U = max(U0, ts); U < min(U1, te); ++U)
+      int U = max(U0, ts);
+      const int Ue = min(U1, te);
+      for (; U + 4 <= Ue; U += 4) {
+        float r[4][B];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < B; ++b) r[j][b] = S[((U + j - U0) * B + b) * kTileRows + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < B; ++b) s[b] += r[j][b];
+      }
+      for (; U < Ue; ++U)
 #pragma unroll
         for (int b = 0; b < B; ++b) s[b] += S[((U - U0) * B + b) * kTileRows + lane];
     } else {
