@@ -58,7 +58,12 @@ extern "C" {
 #define KQ_Q5_K 2
 #define KQ_Q6_K 3
 
-/* activation formats: fp32, or bf16 (bit patterns, 2 bytes per element) */
+/* activation formats: fp32, or bf16 (bit patterns, 2 bytes per element).
+ * fp32 activations are carried as two bf16 terms, hi = bf16(x) and
+ * lo = bf16(x - hi), which give x to within 2^-18 |x|; the products of both run
+ * as a bf16 batch of twice the size.  The GEMV bound (1e-4 * sum |w x|) holds for
+ * rows whose largest |x| is at least 2^-100 (below, lo falls among bf16's
+ * subnormals and loses bits) and at most 2^100. */
 #define KQ_X_F32 0
 #define KQ_X_BF16 1
 

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkq.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["kq_gemv_q4k.hip", "kq_gemv_q5k.hip", "kq_gemv_q6k.hip", "kq_chain_bf16_lo.hip", "kq_chain_bf16_hi.hip",
-           "kq_chain_f32.hip", "kq_chain_bf16_wide.hip", "kq_repack.hip", "kq_api.cpp"]
+           "kq_chain_f32.hip", "kq_chain_f32_wide.hip", "kq_chain_bf16_wide.hip", "kq_repack.hip", "kq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-command-line-argument",

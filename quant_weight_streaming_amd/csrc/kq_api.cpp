@@ -181,6 +181,7 @@ struct Plan {
   bool mf;       // matrix-core path
   int64_t grid;  // workgroups, a multiple of 8
   size_t lds;    // dynamic LDS per workgroup
+  int rows;      // staged activation rows: the batch, or twice it for fp32 activations
 };
 
 // Launch geometry of a validated call on a device with `cus` CUs, using at most
@@ -222,20 +223,23 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   // (and sub-block sums) of the columns its nw*upw units touch in LDS, within
   // `budget` bytes (64 KiB leaves room for two 4-wavefront workgroups per CU,
   // 112 KiB is for one 8-wavefront workgroup), plus its wavefronts' partial sums.
-  // above batch 8 only the matrix cores with 8-wavefront workgroups are built
-  const int nw = batch > 8 ? 8 : force_nw ? force_nw : wg_waves(batch);
-  const bool mf = xtype == KQ_X_BF16 && (batch >= matrix_cores_from() || batch > 8);
+  // The activations are staged as bf16 rows: the batch, or (fp32 activations)
+  // two rows per batch row, hi = bf16(x) and lo = bf16(x - hi).  Every launch
+  // decision below is taken on the staged rows.
+  const int srows = xtype == KQ_X_F32 ? 2 * batch : batch;
+  // above 8 staged rows only the matrix cores with 8-wavefront workgroups are built
+  const int nw = srows > 8 ? 8 : force_nw ? force_nw : wg_waves(srows);
+  const bool mf = srows >= matrix_cores_from() || srows > 8;
   // staging budget: what is left of the CU's LDS after the tile sums (two tiles
   // per wavefront assumed here; the final size is checked below)
-  const int64_t tile_sums = (int64_t)nw * 2 * batch * 64 * sizeof(float);
+  const int64_t tile_sums = (int64_t)nw * 2 * srows * 64 * sizeof(float);
   int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
   if (budget > (int64_t)kMaxLds - tile_sums - 2048) budget = (int64_t)kMaxLds - tile_sums - 2048;
   const int64_t target = (int64_t)cus * waves_per_cu();
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
   const int64_t per_col =
-      (int64_t)(gemv_lds_bytes(type, xtype, batch, nw, mf, 1, 0, 0, norm) -
-                gemv_lds_bytes(type, xtype, batch, nw, mf, 0, 0, 0, norm));
+      (int64_t)(gemv_lds_bytes(type, srows, nw, mf, 1, 0, 0, norm) - gemv_lds_bytes(type, srows, nw, mf, 0, 0, 0, norm));
   const int64_t max_cols = budget / per_col;
   if (n_cols > max_cols && nw * upw > max_cols) upw = max_cols / nw > 0 ? max_cols / nw : 1;
   int64_t n_groups = (n_units + nw * upw - 1) / (nw * upw);
@@ -257,7 +261,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   a.tiles_per_wg = 0;
   const int64_t n_win = (n_cols + max_cols - 1) / max_cols;
   const int forced_r = aligned_tiles();
-  if (((batch >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
+  if (((srows >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
       n_win * tiles <= 2 * (int64_t)kMaxGroups) {
     int64_t g_target = (int64_t)cus * waves_per_cu() / nw;
     if (g_target > max_groups) g_target = max_groups;
@@ -307,7 +311,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     a.tpw = (int32_t)((upw - 1 + n_cols - 1) / n_cols + 1);
   }
   out->a.tpw = a.tpw;
-  out->lds = gemv_lds_bytes(type, xtype, batch, nw, mf, (int)tcols, (int)run_units, a.tpw, norm);
+  out->lds = gemv_lds_bytes(type, srows, nw, mf, (int)tcols, (int)run_units, a.tpw, norm);
+  out->rows = srows;
   if (out->lds > kMaxLds) return KQ_ERR_RANGE;
   return KQ_OK;
 }
@@ -361,12 +366,13 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, rms_eps, head_eps,
                  st->partial,
                  st->counters, &p);
-  if (rc == KQ_ERR_RANGE && wg_waves(batch) == 8)   // too many units per workgroup for per-unit slots: 4-wavefront runs
+  if (rc == KQ_ERR_RANGE && wg_waves(xtype == KQ_X_F32 ? 2 * batch : batch) == 8)   // too many units per
+                                                                                        // workgroup: 4-wave runs
     rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, rms_eps, head_eps,
                    st->partial,
                    st->counters, &p);
   if (rc != KQ_OK) return rc;
-  if (launch_gemv(type, xtype, batch, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
+  if (launch_gemv(type, xtype, p.rows, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;
@@ -374,22 +380,38 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
 
 // ---------------------------------------------------------------- chains
 
-static hipError_t launch_chain(int xtype, int batch, const ChainArgs& c, int nw, bool mf, int grid, size_t lds,
+// `rows`: staged activation rows (the batch, or twice it for fp32 activations).
+static hipError_t launch_chain(int xtype, int rows, const ChainArgs& c, int nw, bool mf, int grid, size_t lds,
                                hipStream_t s, int* occupancy) {
-  const bool f32 = xtype == KQ_X_F32;
-  switch (batch) {
+  if (xtype == KQ_X_F32) {
+    switch (rows) {
+      case 2: return launch_chain_b<2, true>(c, nw, mf, grid, lds, s, occupancy);
+      case 4: return launch_chain_b<4, true>(c, nw, mf, grid, lds, s, occupancy);
+      case 6: return launch_chain_b<6, true>(c, nw, mf, grid, lds, s, occupancy);
+      case 8: return launch_chain_b<8, true>(c, nw, mf, grid, lds, s, occupancy);
+      default: break;
+    }
+    if (!mf || nw != 8) return hipErrorInvalidValue;
+    switch (rows) {
+      case 10: return launch_chain_wide<10, true>(c, grid, lds, s, occupancy);
+      case 12: return launch_chain_wide<12, true>(c, grid, lds, s, occupancy);
+      case 14: return launch_chain_wide<14, true>(c, grid, lds, s, occupancy);
+      case 16: return launch_chain_wide<16, true>(c, grid, lds, s, occupancy);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (rows) {
 #define KQ_CHAIN_CASE(B) \
-  case B: return f32 ? launch_chain_b<B, true>(c, nw, mf, grid, lds, s, occupancy) \
-                     : launch_chain_b<B, false>(c, nw, mf, grid, lds, s, occupancy);
+  case B: return launch_chain_b<B, false>(c, nw, mf, grid, lds, s, occupancy);
     KQ_CHAIN_CASE(1) KQ_CHAIN_CASE(2) KQ_CHAIN_CASE(3) KQ_CHAIN_CASE(4)
     KQ_CHAIN_CASE(5) KQ_CHAIN_CASE(6) KQ_CHAIN_CASE(7) KQ_CHAIN_CASE(8)
 #undef KQ_CHAIN_CASE
     default: break;
   }
-  if (f32 || !mf || nw != 8) return hipErrorInvalidValue;
-  switch (batch) {
+  if (!mf || nw != 8) return hipErrorInvalidValue;
+  switch (rows) {
 #define KQ_CHAIN_WIDE(B) \
-  case B: return launch_chain_wide<B>(c, grid, lds, s, occupancy);
+  case B: return launch_chain_wide<B, false>(c, grid, lds, s, occupancy);
     KQ_CHAIN_WIDE(9) KQ_CHAIN_WIDE(10) KQ_CHAIN_WIDE(11) KQ_CHAIN_WIDE(12)
     KQ_CHAIN_WIDE(13) KQ_CHAIN_WIDE(14) KQ_CHAIN_WIDE(15) KQ_CHAIN_WIDE(16)
 #undef KQ_CHAIN_WIDE
@@ -412,7 +434,7 @@ static uint32_t chain_spin() {
 
 struct kq_chain {
   int dev = 0;
-  int xtype = 0, batch = 0, nw = 4;
+  int xtype = 0, rows = 0, nw = 4;   // rows: staged activation rows (2 x batch for fp32 activations)
   bool mf = false;
   int grid = 0;
   size_t lds = 0;
@@ -580,6 +602,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   kq_chain* c = new (std::nothrow) kq_chain;
   if (!c) return KQ_ERR_NOMEM;
   std::vector<Plan> plans(n_steps);
+  const int srows = xtype == KQ_X_F32 ? 2 * batch : batch;
   int nw = chain_wg_waves();
   auto plan_all = [&](int64_t max_grid, size_t* lds) {
     *lds = 0;
@@ -587,7 +610,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
                          max_grid, nw, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, nullptr, nullptr, &plans[j]);
-      if (rc == KQ_ERR_RANGE && nw == 8 && batch <= 8) {   // every step then runs with 4-wavefront workgroups
+      if (rc == KQ_ERR_RANGE && nw == 8 && srows <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;
       }
@@ -601,11 +624,11 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   // occupancy says so) walks each step's logical blocks grid-stride.
   size_t lds = 0;
   int rc = plan_all(kMaxGroups, &lds);
-  if (rc == KQ_ERR_RANGE && nw == 4 && batch <= 8) rc = plan_all(kMaxGroups, &lds);
+  if (rc == KQ_ERR_RANGE && nw == 4 && srows <= 8) rc = plan_all(kMaxGroups, &lds);
   int64_t groups = (int64_t)cus * (8 / nw);
   int occ = 0;
   if (rc == KQ_OK &&
-      launch_chain(xtype, batch, ChainArgs{}, nw, plans[0].mf, 0, lds, nullptr, &occ) != hipSuccess)
+      launch_chain(xtype, srows, ChainArgs{}, nw, plans[0].mf, 0, lds, nullptr, &occ) != hipSuccess)
     rc = KQ_ERR_HIP;
   if (rc == KQ_OK && occ < 1) rc = KQ_ERR_RANGE;
   if (rc == KQ_OK && (int64_t)occ * cus < groups) {
@@ -652,7 +675,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   }
   c->dev = dev;
   c->xtype = xtype;
-  c->batch = batch;
+  c->rows = srows;
   c->nw = nw;
   c->mf = plans[0].mf;
   c->grid = (int)groups;
@@ -670,7 +693,7 @@ int kq_chain_run(kq_chain* c, void* stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
   if (dev != c->dev) return KQ_ERR_DEVICE;
-  if (launch_chain(c->xtype, c->batch, c->args, c->nw, c->mf, c->grid, c->lds, static_cast<hipStream_t>(stream),
+  if (launch_chain(c->xtype, c->rows, c->args, c->nw, c->mf, c->grid, c->lds, static_cast<hipStream_t>(stream),
                    nullptr) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;

@@ -3,12 +3,12 @@
 #include "kq_gemv.h"
 
 namespace kq {
-template hipError_t launch_chain_wide<9>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<10>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<11>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<12>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<13>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<14>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<15>(const ChainArgs&, int, size_t, hipStream_t, int*);
-template hipError_t launch_chain_wide<16>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<9, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<10, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<11, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<12, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<13, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<14, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<15, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
+template hipError_t launch_chain_wide<16, false>(const ChainArgs&, int, size_t, hipStream_t, int*);
 }  // namespace kq

@@ -81,28 +81,41 @@ __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, int lane, u3
 // for it does not wait for the weights.  On the dot2 path the store also forms
 // T, the item's activation sum in the dot product's own order (bf16: the same
 // dot2 chain over (128,128), Q6_K (160,160); fp32: sum x), at T[ic * SB + g][b].
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Staging of the activations into LDS as bf16 rows of 512 bytes (RS apart).
+// B is the number of staged rows.  XF32: the activations are fp32 and each of
+// the B / 2 rows read is staged as two bf16 rows, hi = bf16(x) as row b and
+// lo = bf16(x - hi) as row b + B / 2, so that hi + lo is x to within 2^-18 |x|
+// and the bf16 products run on both.
 template <int QT, int B, bool XF32, int NW, int RS>
 struct XStage {
   using F = Fmt<QT>;
   static constexpr int SB = F::kSubBlocks;
-  static constexpr int ES = XF32 ? 4 : 2;                   // bytes per element
+  static constexpr int BU = XF32 ? B / 2 : B;               // activation rows read
+  static constexpr int ES = XF32 ? 4 : 2;                   // bytes per element read
   static constexpr int VPI = F::kSubW * ES / 16;            // 16-byte vectors per item
   static constexpr int IPT = VPI >= 8 ? 1 : 8 / VPI;        // items per thread and round
   static constexpr int NT = 64 * NW;
+  static_assert(!XF32 || B % 2 == 0, "fp32 activations stage two rows each");
   u32x4 v[IPT][VPI];
 
-  __device__ __forceinline__ static int rounds(int len) { return (len * B * SB + IPT * NT - 1) / (IPT * NT); }
+  __device__ __forceinline__ static int rounds(int len) { return (len * BU * SB + IPT * NT - 1) / (IPT * NT); }
 
   // COH: read through the device coherence point (the activations may have been
   // written by another XCD earlier in the same launch).
   template <bool COH, class GA>
   __device__ __forceinline__ void load(GA& a, int c0, int len, int r) {
-    const int n = len * B * SB;
+    const int n = len * BU * SB;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int i = (r * IPT + j) * NT + threadIdx.x;
       if (i < n) {
-        const int g = i % SB, q = i / SB, b = q % B, ic = q / B;
+        const int g = i % SB, q = i / SB, b = q % BU, ic = q / BU;
         int c = c0 + ic;
         if (c >= a.n_cols) c -= a.n_cols;
         const int64_t off = ((int64_t)b * a.ldx + (int64_t)c * 256 + g * F::kSubW) * ES;
@@ -121,14 +134,14 @@ struct XStage {
     }
   }
 
-  // Q2 (not null: the launch normalises x): Q2[ic * B + b] = sum of x^2 over
-  // staged column ic of batch row b.  The SB items of one (column, row) sit in SB
-  // consecutive lanes (n and every round's start are multiples of SB), so their
-  // squares are added by a fixed butterfly and every workgroup that stages a
-  // column gets the same bits for it.
+  // Q2 (not null: the launch normalises x): Q2[ic * BU + b] = sum of x^2 over
+  // staged column ic of activation row b (from the values read, fp32 or bf16).
+  // The SB items of one (column, row) sit in SB consecutive lanes (n and every
+  // round's start are multiples of SB), so their squares are added by a fixed
+  // butterfly and every workgroup that stages a column gets the same bits for it.
   template <bool WITH_T>
   __device__ __forceinline__ void store(uint8_t* X, float* T, float* Q2, int len, int r) const {
-    const int n = len * B * SB;
+    const int n = len * BU * SB;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int i = (r * IPT + j) * NT + threadIdx.x;
@@ -153,50 +166,82 @@ struct XStage {
         }
 #pragma unroll
         for (int m = 1; m < SB; m <<= 1) q += __shfl_xor(q, m);
-        if (i < n && i % SB == 0) Q2[i / SB] = q;   // i / SB = ic * B + b
+        if (i < n && i % SB == 0) Q2[i / SB] = q;   // i / SB = ic * BU + b
       }
       if (i < n) {
-        const int g = i % SB, q = i / SB, b = q % B, ic = q / B;
-        u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * ES);
-        float t = 0.0f;
+        const int g = i % SB, q = i / SB, b = q % BU, ic = q / BU;
         const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;  // bf16 (160,160) / (128,128)
+        // T: the sub-block's products with every weight at the offset, per staged row
+        auto tsum = [&](const u32x4& w, float t) {
+          t = dot2_bf16(kc, w.x, t);
+          t = dot2_bf16(kc, w.y, t);
+          t = dot2_bf16(kc, w.z, t);
+          return dot2_bf16(kc, w.w, t);
+        };
+        if constexpr (XF32) {
+          u32x4* xh = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * 2);
+          u32x4* xo = reinterpret_cast<u32x4*>(X + (ic * B + b + BU) * RS + g * F::kSubW * 2);
+          float th = 0.0f, tl = 0.0f;
 #pragma unroll
-        for (int e = 0; e < VPI; ++e) {
-          const u32x4 xv = v[j][e];
-          xl[e] = xv;
-          if constexpr (WITH_T && !XF32) {
-            t = dot2_bf16(kc, xv.x, t);
-            t = dot2_bf16(kc, xv.y, t);
-            t = dot2_bf16(kc, xv.z, t);
-            t = dot2_bf16(kc, xv.w, t);
-          } else if constexpr (WITH_T) {
-            t += __uint_as_float(xv.x);
-            t += __uint_as_float(xv.y);
-            t += __uint_as_float(xv.z);
-            t += __uint_as_float(xv.w);
+          for (int e = 0; e < VPI; e += 2) {
+            u32x4 hw, lw;
+            uint32_t* hp = reinterpret_cast<uint32_t*>(&hw);
+            uint32_t* lp = reinterpret_cast<uint32_t*>(&lw);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const u32x4 xv = v[j][e + k / 4];
+              const float f = __uint_as_float(k % 4 == 0 ? xv.x : k % 4 == 1 ? xv.y : k % 4 == 2 ? xv.z : xv.w);
+              const uint32_t h = bf16_bits(f);
+              const uint32_t l = bf16_bits(f - __uint_as_float(h << 16));   // the difference is exact
+              if (k % 2 == 0) {
+                hp[k / 2] = h;
+                lp[k / 2] = l;
+              } else {
+                hp[k / 2] |= h << 16;
+                lp[k / 2] |= l << 16;
+              }
+            }
+            xh[e / 2] = hw;
+            xo[e / 2] = lw;
+            if constexpr (WITH_T) {
+              th = tsum(hw, th);
+              tl = tsum(lw, tl);
+            }
           }
+          if constexpr (WITH_T) {
+            T[(ic * SB + g) * B + b] = th;
+            T[(ic * SB + g) * B + b + BU] = tl;
+          }
+        } else {
+          u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * 2);
+          float t = 0.0f;
+#pragma unroll
+          for (int e = 0; e < VPI; ++e) {
+            xl[e] = v[j][e];
+            if constexpr (WITH_T) t = tsum(v[j][e], t);
+          }
+          if constexpr (WITH_T) T[(ic * SB + g) * B + b] = t;
         }
-        if constexpr (WITH_T) T[(ic * SB + g) * B + b] = t;
       }
     }
   }
 };
 
-// Accumulate one unit into acc[B].  Xc / Tc: the staged activations and sums of
-// the unit's column.  The (sub-block, batch row) steps are software-pipelined:
-// each step reads the next step's activations from LDS before its own dot
-// products, and a scheduling barrier keeps the compiler from hoisting reads any
-// further (which would cost registers and occupancy).
-template <int QT, int B, bool XF32>
+// Accumulate one unit into acc[B].  Xc / Tc: the staged (bf16) activations and
+// sums of the unit's column.  The (sub-block, batch row) steps are
+// software-pipelined: each step reads the next step's activations from LDS
+// before its own dot products, and a scheduling barrier keeps the compiler from
+// hoisting reads any further (which would cost registers and occupancy).
+template <int QT, int B>
 __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, const uint32_t* Xc, const float* Tc,
                                              float* acc, uint32_t M, uint32_t K) {
   using F = Fmt<QT>;
   constexpr int SB = F::kSubBlocks, NP = F::kPairs;
-  constexpr int XW = XF32 ? 256 : 128;
-  constexpr int NV = XF32 ? NP / 2 : NP / 4;        // 16-byte LDS reads per sub-block and batch row
-  constexpr int SWD = XF32 ? F::kSubW : F::kSubW / 2;
+  constexpr int XW = 128;                           // 32-bit words per staged row
+  constexpr int NV = NP / 4;                        // 16-byte LDS reads per sub-block and batch row
+  constexpr int SWD = F::kSubW / 2;
   float ca[SB], cm[SB];
-  sb_coeffs<QT>(buf, d6, XF32 ? 1.0f : 0.0078125f, ca, cm);
+  sb_coeffs<QT>(buf, d6, 0.0078125f, ca, cm);
   u32x4 xc[NV], xn[NV];
   float tc, tn = 0.0f;
   {
@@ -219,28 +264,15 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         tn = Tc[gn * B + bn];
       }
       float s = 0.0f;
-      if constexpr (!XF32) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          s = dot2_bf16(pr[4 * v + 0], xc[v].x, s);
-          s = dot2_bf16(pr[4 * v + 1], xc[v].y, s);
-          s = dot2_bf16(pr[4 * v + 2], xc[v].z, s);
-          s = dot2_bf16(pr[4 * v + 3], xc[v].w, s);
-        }
-        acc[b] = __builtin_fmaf(ca[g], s - tc, acc[b]);
-        if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
-      } else {
-        const float off = (QT == KQ_Q6_K) ? 160.0f : 128.0f;  // (128 + q) - off = q, or q - 32
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          s = __builtin_fmaf(bf16_lo(pr[2 * v]) - off, __uint_as_float(xc[v].x), s);
-          s = __builtin_fmaf(bf16_hi(pr[2 * v]) - off, __uint_as_float(xc[v].y), s);
-          s = __builtin_fmaf(bf16_lo(pr[2 * v + 1]) - off, __uint_as_float(xc[v].z), s);
-          s = __builtin_fmaf(bf16_hi(pr[2 * v + 1]) - off, __uint_as_float(xc[v].w), s);
-        }
-        acc[b] = __builtin_fmaf(ca[g], s, acc[b]);
-        if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
+      for (int v = 0; v < NV; ++v) {
+        s = dot2_bf16(pr[4 * v + 0], xc[v].x, s);
+        s = dot2_bf16(pr[4 * v + 1], xc[v].y, s);
+        s = dot2_bf16(pr[4 * v + 2], xc[v].z, s);
+        s = dot2_bf16(pr[4 * v + 3], xc[v].w, s);
       }
+      acc[b] = __builtin_fmaf(ca[g], s - tc, acc[b]);
+      if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
 #pragma unroll
       for (int v = 0; v < NV; ++v) xc[v] = xn[v];
       tc = tn;
@@ -564,6 +596,10 @@ __device__ __forceinline__ void head_norm_tile(GA& a, int t, int p, int lane, co
   float* y = a.y[p];
   const int64_t ldy = a.ldy[p];
   const int row = tl * kTileRows + lane;
+  // the tile's sum of squares, then lane 0's value in every lane: the compiler
+  // may fuse a square into the butterfly's first addition differently in each
+  // lane, and the head's two halves must add the same published values
+  // whichever finishes second
   float q[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) q[b] = v[b] * v[b];
@@ -571,6 +607,8 @@ __device__ __forceinline__ void head_norm_tile(GA& a, int t, int p, int lane, co
   for (int m = 32; m >= 1; m >>= 1)
 #pragma unroll
     for (int b = 0; b < B; ++b) q[b] += __shfl_xor(q[b], m);
+#pragma unroll
+  for (int b = 0; b < B; ++b) q[b] = __shfl(q[b], 0);
 #pragma unroll
   for (int b = 0; b < B; ++b)
     __hip_atomic_store(y + b * ldy + row, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -865,7 +903,10 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
                                            bool wait = true) {
   using F = Fmt<QT>;
   constexpr int NCH = F::kChunks, SB = F::kSubBlocks;
-  constexpr int XW = XF32 ? 256 : 128;
+  constexpr int XW = 128;                          // 32-bit words per staged (bf16) row
+  // B staged rows; fp32 activations give two per output row (XStage), which
+  // are added back together before the tile's epilogue
+  constexpr int BU = XF32 ? B / 2 : B;
   extern __shared__ uint32_t lds_words[];
   // readfirstlane: the wavefront index is uniform across the wavefront; saying so
   // keeps all unit/column bookkeeping in SGPRs.
@@ -936,7 +977,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     __builtin_amdgcn_sched_barrier(0);
   };
   // first round of activation loads, then the weight prologue, then the stores
-  constexpr int kRS = MF ? MfmaLds<QT, B>::kXRow : 256 * (XF32 ? 4 : 2);
+  constexpr int kRS = MF ? MfmaLds<QT, B>::kXRow : 512;
   XStage<QT, B, XF32, NW, kRS> xs;
   if constexpr (CHAIN) {
     // before the step barrier every buffer is filled (DYN: the first unit), so
@@ -1012,7 +1053,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         float acc[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-        process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+        process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
 #pragma unroll
         for (int b = 0; b < B; ++b) S[(kb[k] * B + b) * kTileRows + lane] = acc[b];
       }
@@ -1038,7 +1079,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
                                  reinterpret_cast<const float*>(base + t_base + ic * MfmaLds<QT, B>::kTCol),
                                  acc, M, K);
       } else {
-        process_unit<QT, B, XF32>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+        process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
       }
       if (c == cs + cw - 1 || u + 1 == u1) {
         float* pw = P + ((wid * a.tpw + (t - t0)) * B) * kTileRows;
@@ -1115,32 +1156,36 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         for (int b = 0; b < B; ++b) s[b] += pw[b * kTileRows + lane];
       }
     }
+    // fp32 activations: each output row's hi and lo sums
+    float su[BU];
+#pragma unroll
+    for (int b = 0; b < BU; ++b) su[b] = XF32 ? s[b] + s[b + BU] : s[b];
     // normalised launches: the sum of x^2 over the workgroup's columns of tile t.
     // Lanes take the columns, then a xor butterfly adds across the wavefront; at
     // every level both partners add the same two values, so all lanes end with
     // the same bits.
-    float q[B];
+    float q[BU];
 #pragma unroll
-    for (int b = 0; b < B; ++b) q[b] = 0.0f;
+    for (int b = 0; b < BU; ++b) q[b] = 0.0f;
     if (norm) {
       for (int U = max(U0, ts) + lane; U < min(U1, te); U += 64) {
         int ic = cs + U % cw - c0w;
         if (ic < 0) ic += cw;
 #pragma unroll
-        for (int b = 0; b < B; ++b) q[b] += Q2[ic * B + b];
+        for (int b = 0; b < BU; ++b) q[b] += Q2[ic * BU + b];
       }
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1)
 #pragma unroll
-        for (int b = 0; b < B; ++b) q[b] += __shfl_xor(q[b], m);
+        for (int b = 0; b < BU; ++b) q[b] += __shfl_xor(q[b], m);
     }
     if (a.n_win > 1) {
-      hand_off_windows<B, CHAIN>(a, t, w, lane, s, q);
+      hand_off_windows<BU, CHAIN>(a, t, w, lane, su, q);
     } else if (ts >= U0 && te <= U1) {   // every tile when tiles_per_wg > 0
-      if (norm) rms_scale<B>(a, s, q);
-      write_tile<B, CHAIN>(a, t, lane, s);
+      if (norm) rms_scale<BU>(a, su, q);
+      write_tile<BU, CHAIN>(a, t, lane, su);
     } else {
-      hand_off<B, CHAIN>(a, t, lblock, a.wgu, lane, s, q);
+      hand_off<BU, CHAIN>(a, t, lblock, a.wgu, lane, su, q);
     }
   }
   return wait;
@@ -1216,51 +1261,69 @@ static hipError_t launch_nw(const GemvArgs& a, int nw, int grid, size_t lds, hip
   return hipGetLastError();
 }
 
-template <int QT, int B>
+template <int QT, int B, bool XF32>
 static hipError_t launch_wide(const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_kernel<QT, B, false, true, 8, KQ_DEPTH>), dim3(grid), dim3(512), lds, s, a);
+  hipLaunchKernelGGL((gemv_kernel<QT, B, XF32, true, 8, KQ_DEPTH>), dim3(grid), dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
-// The matrix-core variant exists for bf16 activations and batch >= 2.
+// The matrix-core variant exists from 2 staged rows.
 template <int QT, int B, bool XF32>
 static hipError_t launch_one(const GemvArgs& a, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
-  if constexpr (!XF32 && B >= 2) {
+  if constexpr (B >= 2) {
     if (mf) return launch_nw<QT, B, XF32, true>(a, nw, grid, lds, s);
   }
   if (mf) return hipErrorInvalidValue;
   return launch_nw<QT, B, XF32, false>(a, nw, grid, lds, s);
 }
 
+// `rows`: staged rows, the batch (bf16 activations) or twice the batch (fp32).
 template <int QT, bool XF32>
-static hipError_t launch_b(const GemvArgs& a, int batch, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
-  switch (batch) {
-    case 1: return launch_one<QT, 1, XF32>(a, nw, mf, grid, lds, s);
-    case 2: return launch_one<QT, 2, XF32>(a, nw, mf, grid, lds, s);
-    case 3: return launch_one<QT, 3, XF32>(a, nw, mf, grid, lds, s);
-    case 4: return launch_one<QT, 4, XF32>(a, nw, mf, grid, lds, s);
-    case 5: return launch_one<QT, 5, XF32>(a, nw, mf, grid, lds, s);
-    case 6: return launch_one<QT, 6, XF32>(a, nw, mf, grid, lds, s);
-    case 7: return launch_one<QT, 7, XF32>(a, nw, mf, grid, lds, s);
-    case 8: return launch_one<QT, 8, XF32>(a, nw, mf, grid, lds, s);
-    default: break;
+static hipError_t launch_b(const GemvArgs& a, int rows, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
+  if constexpr (XF32) {
+    switch (rows) {
+      case 2: return launch_one<QT, 2, true>(a, nw, mf, grid, lds, s);
+      case 4: return launch_one<QT, 4, true>(a, nw, mf, grid, lds, s);
+      case 6: return launch_one<QT, 6, true>(a, nw, mf, grid, lds, s);
+      case 8: return launch_one<QT, 8, true>(a, nw, mf, grid, lds, s);
+      default: break;
+    }
+  } else {
+    switch (rows) {
+      case 1: return launch_one<QT, 1, false>(a, nw, mf, grid, lds, s);
+      case 2: return launch_one<QT, 2, false>(a, nw, mf, grid, lds, s);
+      case 3: return launch_one<QT, 3, false>(a, nw, mf, grid, lds, s);
+      case 4: return launch_one<QT, 4, false>(a, nw, mf, grid, lds, s);
+      case 5: return launch_one<QT, 5, false>(a, nw, mf, grid, lds, s);
+      case 6: return launch_one<QT, 6, false>(a, nw, mf, grid, lds, s);
+      case 7: return launch_one<QT, 7, false>(a, nw, mf, grid, lds, s);
+      case 8: return launch_one<QT, 8, false>(a, nw, mf, grid, lds, s);
+      default: break;
+    }
   }
-  // batch 9..16: bf16 activations on the matrix cores, 8-wavefront workgroups
-  if constexpr (!XF32) {
-    if (!mf || nw != 8) return hipErrorInvalidValue;
-    switch (batch) {
-      case 9: return launch_wide<QT, 9>(a, grid, lds, s);
-      case 10: return launch_wide<QT, 10>(a, grid, lds, s);
-      case 11: return launch_wide<QT, 11>(a, grid, lds, s);
-      case 12: return launch_wide<QT, 12>(a, grid, lds, s);
-      case 13: return launch_wide<QT, 13>(a, grid, lds, s);
-      case 14: return launch_wide<QT, 14>(a, grid, lds, s);
-      case 15: return launch_wide<QT, 15>(a, grid, lds, s);
-      case 16: return launch_wide<QT, 16>(a, grid, lds, s);
+  // 9..16 staged rows: matrix cores, 8-wavefront workgroups
+  if (!mf || nw != 8) return hipErrorInvalidValue;
+  if constexpr (XF32) {
+    switch (rows) {
+      case 10: return launch_wide<QT, 10, true>(a, grid, lds, s);
+      case 12: return launch_wide<QT, 12, true>(a, grid, lds, s);
+      case 14: return launch_wide<QT, 14, true>(a, grid, lds, s);
+      case 16: return launch_wide<QT, 16, true>(a, grid, lds, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (rows) {
+      case 9: return launch_wide<QT, 9, false>(a, grid, lds, s);
+      case 10: return launch_wide<QT, 10, false>(a, grid, lds, s);
+      case 11: return launch_wide<QT, 11, false>(a, grid, lds, s);
+      case 12: return launch_wide<QT, 12, false>(a, grid, lds, s);
+      case 13: return launch_wide<QT, 13, false>(a, grid, lds, s);
+      case 14: return launch_wide<QT, 14, false>(a, grid, lds, s);
+      case 15: return launch_wide<QT, 15, false>(a, grid, lds, s);
+      case 16: return launch_wide<QT, 16, false>(a, grid, lds, s);
       default: return hipErrorInvalidValue;
     }
   }
-  return hipErrorInvalidValue;
 }
 
 template <int B, bool XF32, bool MF>
@@ -1274,32 +1337,33 @@ static hipError_t launch_chain_nw(const ChainArgs& c, int nw, int grid, size_t l
 }
 
 // Chain launch (or, with `occupancy`, the number of its workgroups one CU
-// holds) for one batch size and activation type.
+// holds) for B staged rows (the batch, or twice the batch for fp32
+// activations) and one activation type.
 template <int B, bool XF32>
 hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t lds, hipStream_t s, int* occupancy) {
-  if constexpr (!XF32 && B >= 2) {
+  if constexpr (B >= 2) {
     if (mf) return launch_chain_nw<B, XF32, true>(c, nw, grid, lds, s, occupancy);
   }
   if (mf) return hipErrorInvalidValue;
   return launch_chain_nw<B, XF32, false>(c, nw, grid, lds, s, occupancy);
 }
 
-// Chain launch for batch 9..16 (bf16 activations, matrix cores, 8-wavefront workgroups).
-template <int B>
+// Chain launch for 9..16 staged rows (matrix cores, 8-wavefront workgroups).
+template <int B, bool XF32>
 hipError_t launch_chain_wide(const ChainArgs& c, int grid, size_t lds, hipStream_t s, int* occupancy) {
-  const void* k = reinterpret_cast<const void*>(&chain_kernel<B, false, true, 8>);
+  const void* k = reinterpret_cast<const void*>(&chain_kernel<B, XF32, true, 8>);
   if (occupancy) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, k, 512, lds);
-  hipLaunchKernelGGL((chain_kernel<B, false, true, 8>), dim3(grid), dim3(512), lds, s, c);
+  hipLaunchKernelGGL((chain_kernel<B, XF32, true, 8>), dim3(grid), dim3(512), lds, s, c);
   return hipGetLastError();
 }
 
 // Host entry for one weight type; each type is instantiated in its own
 // translation unit (kq_gemv_q4k.hip, ...), which keeps the build parallel.
 template <int QT>
-hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
+hipError_t launch_gemv_type(int xtype, int rows, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
                             hipStream_t s) {
-  return xtype == KQ_X_F32 ? launch_b<QT, true>(a, batch, nw, mf, grid, lds, s)
-                           : launch_b<QT, false>(a, batch, nw, mf, grid, lds, s);
+  return xtype == KQ_X_F32 ? launch_b<QT, true>(a, rows, nw, mf, grid, lds, s)
+                           : launch_b<QT, false>(a, rows, nw, mf, grid, lds, s);
 }
 
 }  // namespace kq

@@ -76,11 +76,11 @@ struct ChainArgs {
 
 template <int B, bool XF32>
 hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t lds, hipStream_t s, int* occupancy);
-template <int B>
+template <int B, bool XF32>
 hipError_t launch_chain_wide(const ChainArgs& c, int grid, size_t lds, hipStream_t s, int* occupancy);
 
 template <int QT>
-hipError_t launch_gemv_type(int xtype, int batch, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
+hipError_t launch_gemv_type(int xtype, int rows, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
                             hipStream_t s);
 
 // The dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols` columns
@@ -95,19 +95,19 @@ inline bool dyn_units(int batch, int nw, bool mf) { return batch == 1 && nw == 8
 
 // `run_units`: units of one workgroup (the per-unit slots of dynamic workgroups);
 // `tpw`: tiles one wavefront's run can touch (its tile sums otherwise).
-// norm: the launch normalises x (sums of x^2 per staged column and batch row).
-inline size_t gemv_lds_bytes(int type, int xtype, int batch, int nw, bool mf, int staged_cols, int run_units,
-                             int tpw, bool norm = false) {
-  const size_t partials = (dyn_units(batch, nw, mf) ? 16 + (size_t)run_units * batch * 64 * sizeof(float)
-                                                    : (size_t)nw * tpw * batch * 64 * sizeof(float)) +
-                          (norm ? (size_t)((staged_cols * batch + 3) & ~3) * sizeof(float) : 0);
+// `rows`: staged bf16 rows (the batch, or twice the batch for fp32 activations);
+// norm: the launch normalises x (sums of x^2 per staged column and row).
+inline size_t gemv_lds_bytes(int type, int rows, int nw, bool mf, int staged_cols, int run_units, int tpw,
+                             bool norm = false) {
+  const size_t partials = (dyn_units(rows, nw, mf) ? 16 + (size_t)run_units * rows * 64 * sizeof(float)
+                                                   : (size_t)nw * tpw * rows * 64 * sizeof(float)) +
+                          (norm ? (size_t)((staged_cols * rows + 3) & ~3) * sizeof(float) : 0);
   const int sb = type == KQ_Q6_K ? 16 : 8;
   if (mf) {
-    const int nb = (batch + 3) / 4;
-    return (size_t)staged_cols * (batch * 528 + sb * nb * 16) + 512 + partials;
+    const int nb = (rows + 3) / 4;
+    return (size_t)staged_cols * (rows * 528 + sb * nb * 16) + 512 + partials;
   }
-  const int xwords = xtype == KQ_X_F32 ? 256 : 128;
-  return (size_t)staged_cols * batch * 4 * (xwords + sb) + partials;
+  return (size_t)staged_cols * rows * 4 * (128 + sb) + partials;
 }
 hipError_t launch_repack(int type, int64_t rows, int64_t cols, const void* gguf, const void* gguf2, void* out,
                          hipStream_t s);

@@ -137,3 +137,24 @@ def test_head_norm_in_a_chain(monkeypatch):
     torch.cuda.synchronize()
     for a_, b_ in zip(ys, ref):
         assert torch.equal(a_, b_), "the chain differs from the launch"
+
+
+@pytest.mark.parametrize("batch,xdt", [(1, "f32"), (4, "f32"), (8, "bf16")])
+def test_head_norm_repeats_bitwise(batch, xdt):
+    """The same launch gives the same bits every time, whichever tile of a head finishes second (the head's
+    sum of squares is taken from one lane, so both halves add the same published values)."""
+    parts, cols = [512, 256, 256], 1024
+    say(f"case head norm repeats B={batch} {xdt}")
+    gs = [synth.gen_weights("q4k", r, cols, synth.seed_of("hn-rep", i), device=DEV) for i, r in enumerate(parts)]
+    ws = [kq.repack("q4k", g, r, cols) for g, r in zip(gs, parts)]
+    x = synth.gen_x(batch, cols, synth.seed_of("hn-rep-x", batch), xdt, device=DEV)
+    first = None
+    for _ in range(8):
+        ys = [torch.empty(batch, r, device=DEV) for r in parts]
+        kq.kq_gemv_fused("q4k", ws, parts, cols, x, ys, [kq.KQ_EPI_HEADNORM, kq.KQ_EPI_HEADNORM, kq.KQ_EPI_NONE],
+                         head_eps=1e-6)
+        torch.cuda.synchronize()
+        out = torch.cat(ys, 1)
+        if first is None:
+            first = out
+        assert torch.equal(out, first), "a repeated launch gave different bits"

@@ -267,3 +267,21 @@ def test_verify_block_batches(qtype, batch, shape):
     sets): a ragged tile, and long rows split into column windows."""
     rows, cols = shape
     run_case(qtype, rows, cols, batch, "bf16", 800 + batch, check_w=False)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+@pytest.mark.parametrize("scale", [2.0 ** -100, 1.0, 2.0 ** 100])
+def test_fp32_activation_range(batch, scale):
+    """fp32 activations run as two bf16 rows (hi = bf16(x), lo = bf16(x - hi)): within the GEMV bound over the
+    documented range of row scales, also when one row mixes magnitudes from 2^-20 to 2^20."""
+    rows, cols = 192, 1536
+    say(f"case fp32 range 2^{int(np.log2(scale))} B={batch}")
+    g = synth.gen_weights("q4k", rows, cols, synth.seed_of("f32range"))
+    w = kq.repack("q4k", g.to(DEV), rows, cols)
+    gen = torch.Generator().manual_seed(batch)
+    x = torch.randn(batch, cols, generator=gen) * scale
+    x[0] *= torch.exp2(torch.randint(-20, 21, (cols,), generator=gen).float())
+    y = kq.gemv("q4k", w, rows, cols, x.float().to(DEV))
+    torch.cuda.synchronize()
+    yo, ao = O.gemv("q4k", rows, cols, g.numpy(), x.float().numpy())
+    check_y(y.cpu().numpy(), yo, ao, f"fp32 x at scale 2^{int(np.log2(scale))}")
