@@ -255,6 +255,66 @@ def time_fused(parts, cols: int, batches, variants, copies: int = 6, reps: int =
     return out
 
 
+def time_decode_chain(batches, steps: int, warmup: int) -> dict:
+    """A whole decode step as one chain in which every step reads what an earlier step wrote (fp32 activations),
+    with the operations either side of each product fused into it: per layer, QKV reads the residual stream
+    through the weight-less input RMSNorm and normalises the Q and K heads, O reads q (a stand-in for the attention
+    output) and adds into the residual stream, gate+up reads the residual stream through the input norm and writes
+    silu(gate) * up (one interleaved 62,464-row matrix), down adds into the residual stream; then the head through
+    the input norm.  The first workload's shapes and types (52 layers, hidden 5,120, 18.03 GB of weights)."""
+    import torch
+    from quant_weight_streaming_amd import kq, synth
+    H, Q, KV, I, V, L = synth.HIDDEN, 4096, 256, synth.INTER, synth.VOCAB, synth.N_LAYERS
+    dev, hn = "cuda:0", kq.KQ_EPI_HEADNORM
+    layers, nbytes = [], 0
+    for li in range(L):
+        g = synth.gen_weights("q4k", Q + 2 * KV, H, synth.seed_of("dec", li, "qkv"), device=dev)
+        qkv = [kq.repack("q4k", g[a:b].contiguous(), b - a, H) for a, b in ((0, Q), (Q, Q + KV), (Q + KV, Q + 2 * KV))]
+        o = kq.repack("q4k", synth.gen_weights("q4k", H, Q, synth.seed_of("dec", li, "o"), device=dev), H, Q)
+        gate = synth.gen_weights("q4k", I, H, synth.seed_of("dec", li, "gate"), device=dev)
+        up = synth.gen_weights("q4k", I, H, synth.seed_of("dec", li, "up"), device=dev)
+        gu = kq.repack_swiglu("q4k", gate, up, I, H)
+        del g, gate, up
+        down = kq.repack("q6k", synth.gen_weights("q6k", H, I, synth.seed_of("dec", li, "down"), device=dev), H, I)
+        layers.append((qkv, o, gu, down))
+    head = kq.repack("q6k", synth.gen_weights("q6k", V, H, synth.seed_of("dec", "head"), device=dev), V, H)
+    for spec in (synth.QKV, synth.O_PROJ, synth.GATE_UP, synth.DOWN):
+        nbytes += L * spec.rows * spec.cols // 256 * synth.SB_BYTES[spec.qtype]
+    nbytes += V * H // 256 * synth.SB_BYTES["q6k"]
+    out = {"workload": "52 x {QKV + input RMSNorm + Q/K head norm, O + residual, gate+up + input RMSNorm + SwiGLU, "
+                       "down + residual} + head + input RMSNorm, fp32 activations, one chain",
+           "weight_bytes": nbytes}
+    for B in batches:
+        r = torch.randn(B, H, device=dev)
+        q, k, v = (torch.zeros(B, n, device=dev) for n in (Q, KV, KV))
+        h, logits = torch.zeros(B, I, device=dev), torch.zeros(B, V, device=dev)
+        st = []
+        for qkv, o, gu, down in layers:
+            st += [("q4k", qkv, [Q, KV, KV], H, r, [q, k, v], hn | (hn << 4), 1e-5, 1e-6),
+                   ("q4k", [o], [H], Q, q, [r], kq.KQ_EPI_RESIDUAL),
+                   ("q4k", [gu], [I], H, r, [h], kq.KQ_EPI_SWIGLU, 1e-5),
+                   ("q6k", [down], [H], I, h, [r], kq.KQ_EPI_RESIDUAL)]
+        st.append(("q6k", [head], [V], H, r, [logits], kq.KQ_EPI_NONE, 1e-5))
+        ch = kq.Chain(st, B)
+        for _ in range(warmup):
+            ch.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            ch.run()
+        e1.record()
+        torch.cuda.synchronize()
+        if ch.status() != 0:
+            raise RuntimeError("a chain step's wait gave up: the decode-chain timing is invalid")
+        ch.close()
+        ms = e0.elapsed_time(e1) / steps
+        out[f"b{B}"] = dict(ms=round(ms, 4), weight_gbs=round(nbytes / ms / 1e6, 1), tok_s=round(B * 1e3 / ms, 1))
+    del layers, head
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_calls(calls):
     for fn, args, name in calls:
         rc = fn(*args)
@@ -583,6 +643,10 @@ def main():
     kt8 = kernel_times(sw, 8)
     cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
     swiglu_us = time_swiglu(synth.INTER, synth.HIDDEN, (1, 8))
+    decode = time_decode_chain((1, 8), max(3, args.steps // 2), args.warmup)
+    log(f"[bench] fused decode chain (fp32 activations, norms, SwiGLU, residuals): "
+        + ", ".join(f"B={b[1:]} {v['ms']:.3f} ms ({v['weight_gbs']:.0f} GB/s)" for b, v in decode.items()
+                    if b.startswith("b")))
     qkvg = synth.QKVG_P4
     fused_us = time_fused(qkvg.parts, qkvg.cols, (1, 8), {
         "plain": (None, 0.0),
@@ -689,6 +753,7 @@ def main():
         "verify_cost_staircase": stair,
         "gate_up_swiglu_epilogue_us": swiglu_us,
         "qkvg_6656_fused_us": fused_us,
+        "decode_chain_fused": decode,
         "kernels_b1": kt1,
         "kernels_b8": kt8,
         "c4_q5k_merged": c4,
