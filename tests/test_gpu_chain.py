@@ -72,7 +72,8 @@ MIXED = [("q4k", (100, 64, 37), 1024), ("q6k", (300,), 512), ("q5k", (129,), 204
 
 
 @pytest.mark.parametrize("batch,xdtype", [(1, "bf16"), (2, "bf16"), (3, "bf16"), (5, "bf16"), (8, "bf16"),
-                                          (12, "bf16"), (16, "bf16"), (1, "f32"), (4, "f32")])
+                                          (12, "bf16"), (16, "bf16"), (1, "f32"), (4, "f32"),
+                                          (6, "f32"), (8, "f32")])
 def test_chain_matches_single_launches(batch, xdtype):
     say(f"case chain mixed B={batch} x={xdtype}")
     steps, hosts = _independent_steps(MIXED, batch, xdtype, f"mixed{batch}{xdtype}")

@@ -40,7 +40,7 @@ def test_config0_exact():
 
 @pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("xdtype", ["bf16", "f32"])
-@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_small_ragged(qtype, xdtype, batch):
     # 4 row tiles (the last one 17 rows), 5 super-block columns
     run_case(qtype, 3 * 64 + 17, 5 * 256, batch, xdtype, 100 + batch, check_w=(batch == 1))
