@@ -282,19 +282,31 @@ def time_decode_chain(batches, steps: int, warmup: int) -> dict:
         nbytes += L * spec.rows * spec.cols // 256 * synth.SB_BYTES[spec.qtype]
     nbytes += V * H // 256 * synth.SB_BYTES["q6k"]
     out = {"workload": "52 x {QKV + input RMSNorm + Q/K head norm, O + residual, gate+up + input RMSNorm + SwiGLU, "
-                       "down + residual} + head + input RMSNorm, fp32 activations, one chain",
+                       "down + residual} + head + input RMSNorm, one chain; activations fp32 (the outputs) or bf16 "
+                       "(the outputs' bf16 copies, the residual stream staying fp32)",
            "weight_bytes": nbytes}
-    for B in batches:
+    for act, B in [(a, b) for a in ("bf16", "f32") for b in batches]:
         r = torch.randn(B, H, device=dev)
         q, k, v = (torch.zeros(B, n, device=dev) for n in (Q, KV, KV))
         h, logits = torch.zeros(B, I, device=dev), torch.zeros(B, V, device=dev)
         st = []
-        for qkv, o, gu, down in layers:
-            st += [("q4k", qkv, [Q, KV, KV], H, r, [q, k, v], hn | (hn << 4), 1e-5, 1e-6),
-                   ("q4k", [o], [H], Q, q, [r], kq.KQ_EPI_RESIDUAL),
-                   ("q4k", [gu], [I], H, r, [h], kq.KQ_EPI_SWIGLU, 1e-5),
-                   ("q6k", [down], [H], I, h, [r], kq.KQ_EPI_RESIDUAL)]
-        st.append(("q6k", [head], [V], H, r, [logits], kq.KQ_EPI_NONE, 1e-5))
+        if act == "f32":
+            for qkv, o, gu, down in layers:
+                st += [("q4k", qkv, [Q, KV, KV], H, r, [q, k, v], hn | (hn << 4), 1e-5, 1e-6),
+                       ("q4k", [o], [H], Q, q, [r], kq.KQ_EPI_RESIDUAL),
+                       ("q4k", [gu], [I], H, r, [h], kq.KQ_EPI_SWIGLU, 1e-5),
+                       ("q6k", [down], [H], I, h, [r], kq.KQ_EPI_RESIDUAL)]
+            st.append(("q6k", [head], [V], H, r, [logits], kq.KQ_EPI_NONE, 1e-5))
+        else:
+            r16 = r.to(torch.bfloat16)
+            q16 = torch.zeros(B, Q, dtype=torch.bfloat16, device=dev)
+            h16 = torch.zeros(B, I, dtype=torch.bfloat16, device=dev)
+            for qkv, o, gu, down in layers:
+                st += [("q4k", qkv, [Q, KV, KV], H, r16, [q, k, v], hn | (hn << 4), 1e-5, 1e-6, [q16, None, None]),
+                       ("q4k", [o], [H], Q, q16, [r], kq.KQ_EPI_RESIDUAL, 0.0, 0.0, [r16]),
+                       ("q4k", [gu], [I], H, r16, [h], kq.KQ_EPI_SWIGLU, 1e-5, 0.0, [h16]),
+                       ("q6k", [down], [H], I, h16, [r], kq.KQ_EPI_RESIDUAL, 0.0, 0.0, [r16])]
+            st.append(("q6k", [head], [V], H, r16, [logits], kq.KQ_EPI_NONE, 1e-5))
         ch = kq.Chain(st, B)
         for _ in range(warmup):
             ch.run()
@@ -309,7 +321,8 @@ def time_decode_chain(batches, steps: int, warmup: int) -> dict:
             raise RuntimeError("a chain step's wait gave up: the decode-chain timing is invalid")
         ch.close()
         ms = e0.elapsed_time(e1) / steps
-        out[f"b{B}"] = dict(ms=round(ms, 4), weight_gbs=round(nbytes / ms / 1e6, 1), tok_s=round(B * 1e3 / ms, 1))
+        out[f"{act}_b{B}"] = dict(ms=round(ms, 4), weight_gbs=round(nbytes / ms / 1e6, 1),
+                                  tok_s=round(B * 1e3 / ms, 1))
     del layers, head
     torch.cuda.empty_cache()
     return out
@@ -644,9 +657,9 @@ def main():
     cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
     swiglu_us = time_swiglu(synth.INTER, synth.HIDDEN, (1, 8))
     decode = time_decode_chain((1, 8), max(3, args.steps // 2), args.warmup)
-    log(f"[bench] fused decode chain (fp32 activations, norms, SwiGLU, residuals): "
-        + ", ".join(f"B={b[1:]} {v['ms']:.3f} ms ({v['weight_gbs']:.0f} GB/s)" for b, v in decode.items()
-                    if b.startswith("b")))
+    log(f"[bench] fused decode chain (norms, SwiGLU, residuals): "
+        + ", ".join(f"{b} {v['ms']:.3f} ms ({v['weight_gbs']:.0f} GB/s)" for b, v in decode.items()
+                    if isinstance(v, dict)))
     qkvg = synth.QKVG_P4
     fused_us = time_fused(qkvg.parts, qkvg.cols, (1, 8), {
         "plain": (None, 0.0),

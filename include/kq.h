@@ -195,11 +195,17 @@ int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, 
  *                   (else KQ_ERR_RANGE).  head_eps is ignored without one;
  *   KQ_EPI_SWIGLU   n = 1 only, w from kq_repack_swiglu and rows[0] = inter:
  *                   as kq_gemv_swiglu.
+ *
+ * bf16 copies: y16 (host array of n device pointers, or NULL) names for each
+ * segment an optional second output, y16[i][b*ldy16[i] + r] = the bf16 nearest
+ * (round to nearest even) to the fp32 value written to y[i], so that a product
+ * that reads this output can take bf16 activations (ldy16[i] >= rows[i], 2-byte
+ * aligned; a NULL entry: none).
  * Otherwise as kq_gemv_multi; KQ_ERR_TYPE for an unknown code.
  */
 int kq_gemv_fused(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
-                  int64_t ldx, int batch, float *const *y, const int64_t *ldy, const int32_t *epi, float rms_eps,
-                  float head_eps, void *stream);
+                  int64_t ldx, int batch, float *const *y, const int64_t *ldy, void *const *y16, const int64_t *ldy16,
+                  const int32_t *epi, float rms_eps, float head_eps, void *stream);
 
 /*
  * SwiGLU epilogue: the gate and up projections of the feed-forward block in one
@@ -268,6 +274,8 @@ typedef struct kq_chain_step {
   int64_t rows[KQ_MAX_PROJ];      /* rows of each segment */
   float *y[KQ_MAX_PROJ];          /* device, fp32 outputs */
   int64_t ldy[KQ_MAX_PROJ];       /* output row strides (elements), >= rows */
+  void *y16[KQ_MAX_PROJ];         /* device, optional bf16 copies of the outputs (NULL: none), as kq_gemv_fused */
+  int64_t ldy16[KQ_MAX_PROJ];     /* their row strides (elements) */
   const void *x;                  /* device activations, batch rows of stride ldx */
   int64_t ldx;                    /* activation row stride (elements), >= cols */
   int32_t epilogue;               /* segment i's KQ_EPI_* code in bits 4i..4i+3 (KQ_EPI_SWIGLU: n = 1,

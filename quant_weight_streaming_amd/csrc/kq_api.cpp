@@ -190,7 +190,8 @@ struct Plan {
 // (n == 1) from kq_repack_swiglu, rows[0] = the intermediate size, 32 outputs
 // per 64-row tile.
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
-                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, int cus,
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* const* y16,
+                     const int64_t* ldy16, int cus,
                      int64_t max_grid, int force_nw, uint32_t epi, float rms_eps, float head_eps, float* partial,
                      uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
@@ -205,6 +206,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
     a.w[i] = static_cast<const uint8_t*>(w[i]);
     a.y[i] = y[i];
     a.ldy[i] = ldy[i];
+    a.y16[i] = y16 ? static_cast<uint16_t*>(y16[i]) : nullptr;
+    a.ldy16[i] = y16 && y16[i] ? ldy16[i] : 0;
     a.rows[i] = (int32_t)rows[i];
     a.tile_begin[i] = (int32_t)tiles;
     tiles += epi == (uint32_t)KQ_EPI_SWIGLU ? (rows[i] + 31) / 32 : (rows[i] + 63) / 64;
@@ -345,13 +348,28 @@ static int check_heads(int n, const int64_t* rows, uint32_t epi, float head_eps)
   return KQ_OK;
 }
 
+// Optional bf16 copies of the outputs: a row stride >= the segment's outputs, 2-byte aligned.
+static int check_y16(int n, const int64_t* rows, void* const* y16, const int64_t* ldy16) {
+  if (!y16) return KQ_OK;
+  for (int i = 0; i < n; ++i) {
+    if (!y16[i]) continue;
+    if (!ldy16) return KQ_ERR_NULL;
+    if (ldy16[i] < rows[i] || ldy16[i] > ((int64_t)1 << 40)) return KQ_ERR_SHAPE;
+    if (!aligned(y16[i], 2)) return KQ_ERR_ALIGN;
+  }
+  return KQ_OK;
+}
+
 // The weight-less RMSNorm's epsilon: 0 (no normalisation) or finite and > 0.
 static bool valid_rms_eps(float e) { return e == 0.0f || (e > 0.0f && e <= FLT_MAX); }
 
 static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream,
-                     uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f, float head_eps = 0.0f) {
+                     uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f, float head_eps = 0.0f,
+                     void* const* y16 = nullptr, const int64_t* ldy16 = nullptr) {
   int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
+  if (rc != KQ_OK) return rc;
+  rc = check_y16(n, rows, y16, ldy16);
   if (rc != KQ_OK) return rc;
   if (!valid_epilogue(n, epi)) return KQ_ERR_TYPE;
   if (!valid_rms_eps(rms_eps)) return KQ_ERR_SHAPE;
@@ -363,12 +381,14 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
   Plan p{};
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 0, epi, rms_eps, head_eps,
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 0, epi,
+                 rms_eps, head_eps,
                  st->partial,
                  st->counters, &p);
   if (rc == KQ_ERR_RANGE && wg_waves(xtype == KQ_X_F32 ? 2 * batch : batch) == 8)   // too many units per
                                                                                         // workgroup: 4-wave runs
-    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, st->cus, kMaxGroups, 4, epi, rms_eps, head_eps,
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 4, epi,
+                   rms_eps, head_eps,
                    st->partial,
                    st->counters, &p);
   if (rc != KQ_OK) return rc;
@@ -502,8 +522,8 @@ int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void* gate, co
 }
 
 int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x, int xtype,
-                  int64_t ldx, int batch, float* const* y, const int64_t* ldy, const int32_t* epi, float rms_eps,
-                  float head_eps, void* stream) {
+                  int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* const* y16, const int64_t* ldy16,
+                  const int32_t* epi, float rms_eps, float head_eps, void* stream) {
   if (n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
   uint32_t packed = 0;
   if (epi) {
@@ -517,7 +537,7 @@ int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, in
       }
     }
   }
-  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed, rms_eps, head_eps);
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed, rms_eps, head_eps, y16, ldy16);
 }
 
 int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,
@@ -589,6 +609,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     if (!valid_rms_eps(st.rms_eps)) return KQ_ERR_SHAPE;
     const int hrc = check_heads(st.n, st.rows, (uint32_t)st.epilogue, st.head_eps);
     if (hrc != KQ_OK) return hrc;
+    const int yrc = check_y16(st.n, st.rows, st.y16, st.ldy16);
+    if (yrc != KQ_OK) return yrc;
     if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
   int dev = 0;
@@ -608,7 +630,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     *lds = 0;
     for (int j = 0; j < n_steps; ++j) {
       const kq_chain_step& st = steps[j];
-      int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, cus,
+      int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, st.y16,
+                         st.ldy16, cus,
                          max_grid, nw, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, nullptr, nullptr, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && srows <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;

@@ -87,6 +87,15 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// A segment's bf16 copy of an output (the next product's activation): the fp32
+// value rounded to the nearest bf16; COH: through the device coherence point.
+template <bool COH>
+__device__ __forceinline__ void store_bf16(uint16_t* p, float v) {
+  const uint16_t h = (uint16_t)bf16_bits(v);
+  if constexpr (COH) __hip_atomic_store(p, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = h;
+}
+
 // Staging of the activations into LDS as bf16 rows of 512 bytes (RS apart).
 // B is the number of staged rows.  XF32: the activations are fp32 and each of
 // the B / 2 rows read is staged as two bf16 rows, hi = bf16(x) as row b and
@@ -644,6 +653,15 @@ __device__ __forceinline__ void head_norm_tile(GA& a, int t, int p, int lane, co
 #pragma unroll
   for (int b = 0; b < B; ++b)
     __hip_atomic_store(y + b * ldy + row_o, vo[b] * sc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.y16[p]) {
+    uint16_t* y16 = a.y16[p];
+    const int64_t ld16 = a.ldy16[p];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      store_bf16<true>(y16 + b * ld16 + row, v[b] * sc[b]);
+      store_bf16<true>(y16 + b * ld16 + row_o, vo[b] * sc[b]);
+    }
+  }
   if (lane == 0) __hip_atomic_store(a.head_ctr + h0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -666,6 +684,7 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
         const float h = v[b] / (1.0f + expf(-v[b])) * u[b];
         if constexpr (COH) __hip_atomic_store(y + b * ldy + row, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else y[b * ldy + row] = h;
+        if (a.y16[0]) store_bf16<COH>(a.y16[0] + b * a.ldy16[0] + row, h);
       }
     }
     return;
@@ -703,6 +722,10 @@ __device__ __forceinline__ void write_tile(GA& a, int t, int lane, const float* 
     for (int b = 0; b < B; ++b) {
       if constexpr (COH) __hip_atomic_store(y + b * ldy + row, o[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else y[b * ldy + row] = o[b];
+    }
+    if (a.y16[p]) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) store_bf16<COH>(a.y16[p] + b * a.ldy16[p] + row, o[b]);
     }
   }
 }

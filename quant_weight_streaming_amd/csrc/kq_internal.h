@@ -20,6 +20,8 @@ struct GemvArgs {
   const uint8_t* w[KQ_MAX_PROJ];       // repacked weights of each projection
   float* y[KQ_MAX_PROJ];               // outputs
   int64_t ldy[KQ_MAX_PROJ];            // output row strides (elements)
+  uint16_t* y16[KQ_MAX_PROJ];          // optional bf16 copies of the outputs (null: none)
+  int64_t ldy16[KQ_MAX_PROJ];          // their row strides (elements)
   int32_t rows[KQ_MAX_PROJ];           // rows of each projection
   int32_t tile_begin[KQ_MAX_PROJ + 1]; // first global tile of each projection (prefix sums)
   int32_t nproj;

@@ -38,6 +38,7 @@ class ChainStep(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int32), ("n", ctypes.c_int32), ("cols", ctypes.c_int64),
                 ("w", ctypes.c_void_p * KQ_MAX_PROJ), ("rows", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
+                ("y16", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy16", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("epilogue", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("head_eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
@@ -76,8 +77,8 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), vp]
         L.kq_gemv_multi.restype = ci
         L.kq_gemv_fused.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
-                                    ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32),
-                                    ctypes.c_float, ctypes.c_float, vp]
+                                    ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_float, ctypes.c_float, vp]
         L.kq_gemv_fused.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
@@ -172,19 +173,24 @@ def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) 
 
 
 def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rms_eps: float = 0.0,
-                  stream=None, head_eps: float = 0.0) -> None:
-    """kq_gemv_multi with a weight-less RMSNorm of x first (rms_eps > 0) and an epilogue code per segment
-    (epis: None for none; KQ_EPI_HEADNORM segments use head_eps)."""
+                  stream=None, head_eps: float = 0.0, y16s=None) -> None:
+    """kq_gemv_multi with a weight-less RMSNorm of x first (rms_eps > 0), an epilogue code per segment
+    (epis: None for none; KQ_EPI_HEADNORM segments use head_eps) and optional bf16 copies of the outputs
+    (y16s: None, or one bf16 tensor or None per segment)."""
     n = len(ws)
-    if len(rows) != n or len(ys) != n or (epis is not None and len(epis) != n):
-        raise ValueError("ws, rows, ys and epis must have the same length")
+    if len(rows) != n or len(ys) != n or (epis is not None and len(epis) != n) or (y16s is not None and len(y16s) != n):
+        raise ValueError("ws, rows, ys, epis and y16s must have the same length")
     W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in ws])
     R = (ctypes.c_int64 * n)(*rows)
     Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
     E = (ctypes.c_int32 * n)(*epis) if epis is not None else None
+    Y16 = LD16 = None
+    if y16s is not None:
+        Y16 = (ctypes.c_void_p * n)(*[t.data_ptr() if t is not None else None for t in y16s])
+        LD16 = (ctypes.c_int64 * n)(*[t.stride(0) if t is not None else 0 for t in y16s])
     _check("kq_gemv_fused", lib().kq_gemv_fused(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
-                                                x.shape[0], Y, LD, E, rms_eps, head_eps, _stream(stream)))
+                                                x.shape[0], Y, LD, Y16, LD16, E, rms_eps, head_eps, _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:
@@ -214,20 +220,23 @@ def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tens
 
 
 def kq_chain_create(steps, xtype: int, batch: int) -> int:
-    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps[, head_eps]]]) as kq_gemv_multi takes
-    them, the epilogue packed four bits per segment; returns the handle."""
+    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps[, head_eps[, y16s]]]]) as kq_gemv_multi
+    and kq_gemv_fused take them, the epilogue packed four bits per segment; returns the handle."""
     arr = (ChainStep * len(steps))()
     for st, step in zip(arr, steps):
         qtype, ws, rows, cols, x, ys = step[:6]
         st.epilogue = step[6] if len(step) > 6 else KQ_EPI_NONE
         st.rms_eps = step[7] if len(step) > 7 else 0.0
         st.head_eps = step[8] if len(step) > 8 else 0.0
+        y16s = step[9] if len(step) > 9 else None
         n = len(ws)
         if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ:
             raise ValueError("ws, rows and ys must have the same length, at most KQ_MAX_PROJ")
         st.type, st.n, st.cols = _type(qtype), n, cols
         for i in range(n):
             st.w[i], st.rows[i], st.y[i], st.ldy[i] = ws[i].data_ptr(), rows[i], ys[i].data_ptr(), ys[i].stride(0)
+            if y16s is not None and y16s[i] is not None:
+                st.y16[i], st.ldy16[i] = y16s[i].data_ptr(), y16s[i].stride(0)
         st.x, st.ldx = x.data_ptr(), x.stride(0)
     h = ctypes.c_void_p()
     _check("kq_chain_create", lib().kq_chain_create(len(steps), arr, xtype, batch, ctypes.byref(h)))

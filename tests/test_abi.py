@@ -192,19 +192,31 @@ def test_fused_rejects():
     Y = (vp * 2)(A16, A16)
     LD = (i64 * 2)(64, 64)
     E = (ctypes.c_int32 * 2)(2, 9)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, 0.0, None) == 5      # unknown code
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 0.0, None) == 5      # unknown code
     E = (ctypes.c_int32 * 2)(1, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, 0.0, None) == 5      # SwiGLU needs n = 1
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 0.0, None) == 5      # SwiGLU needs n = 1
     for eps in (-1e-5, float("inf"), float("nan")):
-        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, eps, 0.0, None) == 2
-    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, 0.0, 0.0, None) == 4
+        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, eps, 0.0, None) == 2
+    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, 0.0, 0.0, None) == 4
     # head norm: rows a multiple of KQ_HEAD_ROWS, head_eps finite and > 0
     E = (ctypes.c_int32 * 2)(4, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, E, 0.0, 1e-6, None) == 2    # 64 rows
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 1e-6, None) == 2    # 64 rows
     R2 = (i64 * 2)(128, 64)
     LD2 = (i64 * 2)(128, 64)
     for eps in (0.0, -1.0, float("inf"), float("nan")):
-        assert L.kq_gemv_fused(1, 2, W, R2, 256, A16, 1, 256, 1, Y, LD2, E, 0.0, eps, None) == 2
+        assert L.kq_gemv_fused(1, 2, W, R2, 256, A16, 1, 256, 1, Y, LD2, None, None, E, 0.0, eps, None) == 2
+    # bf16 copies: a stride for every copy, at least the segment's rows, 2-byte aligned
+    Y16 = (vp * 2)(A16, None)
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, None, None, 0.0, 0.0, None) == 1
+    LD16 = (i64 * 2)(63, 0)
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, LD16, None, 0.0, 0.0, None) == 2
+    Y16 = (vp * 2)(A16 + 1, None)
+    LD16 = (i64 * 2)(64, 0)
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, LD16, None, 0.0, 0.0, None) == 3
+    st = _step()
+    st.y16[0], st.ldy16[0] = A16, 32
+    arr = (kq.ChainStep * 1)(st)
+    assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h := ctypes.c_void_p())) == 2
     st = _step()
     st.epilogue = 3 | (2 << 4)                    # a code for a segment the step does not have
     arr = (kq.ChainStep * 1)(st)

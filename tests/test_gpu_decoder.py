@@ -46,6 +46,53 @@ def _steps(w, r, q, k, v, h):
             ("q6k", [w["down"]], [HIDDEN], INTER, h, [r], kq.KQ_EPI_RESIDUAL)]
 
 
+def _steps16(w, r, q, k, v, h, r16, q16, h16):
+    """The same layer with bf16 activations: every step also writes the bf16 copy the next product reads (the
+    residual stream itself stays fp32)."""
+    return [("q4k", w["qkv"], [QROWS, KVROWS, KVROWS], HIDDEN, r16, [q, k, v], HN | (HN << 4), RMS_EPS, HEAD_EPS,
+             [q16, None, None]),
+            ("q4k", [w["o"]], [HIDDEN], QROWS, q16, [r], kq.KQ_EPI_RESIDUAL, 0.0, 0.0, [r16]),
+            ("q4k", [w["gu"]], [INTER], HIDDEN, r16, [h], kq.KQ_EPI_SWIGLU, RMS_EPS, 0.0, [h16]),
+            ("q6k", [w["down"]], [HIDDEN], INTER, h16, [r], kq.KQ_EPI_RESIDUAL, 0.0, 0.0, [r16])]
+
+
+@pytest.mark.parametrize("batch", [1, 8, 16])
+def test_decoder_layers_chain_bf16(batch, monkeypatch):
+    """bf16 activations (the bf16 copies of the fp32 outputs): the chain equals the launches bitwise, and the copies
+    are the rounded fp32 outputs."""
+    monkeypatch.setenv("KQ_WG_WAVES", "8")
+    say(f"case decoder chain bf16 B={batch}")
+    layers = [_layer(i) for i in range(2)]
+    r0 = torch.randn(batch, HIDDEN, generator=torch.Generator().manual_seed(batch)) * 2
+
+    def bufs():
+        r = r0.clone().to(DEV)
+        return (r, torch.zeros(batch, QROWS, device=DEV), torch.zeros(batch, KVROWS, device=DEV),
+                torch.zeros(batch, KVROWS, device=DEV), torch.zeros(batch, INTER, device=DEV),
+                r.to(torch.bfloat16), torch.zeros(batch, QROWS, dtype=torch.bfloat16, device=DEV),
+                torch.zeros(batch, INTER, dtype=torch.bfloat16, device=DEV))
+    b1 = bufs()
+    ch = kq.Chain([s for _, w in layers for s in _steps16(w, *b1)], batch)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == 0
+    ch.close()
+    b2 = bufs()
+    for _, w in layers:
+        for st in _steps16(w, *b2):
+            qt, ws, rows, cols, x, ys, epi, reps, heps, y16 = st
+            codes = [(epi >> (4 * i)) & 15 for i in range(len(ws))]
+            kq.kq_gemv_fused(qt, ws, rows, cols, x, ys, codes, rms_eps=reps, head_eps=heps, y16s=y16)
+    torch.cuda.synchronize()
+    for i, (a_, b_) in enumerate(zip(b1, b2)):
+        assert torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_,
+                           b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_), f"buffer {i}"
+    r, q, k, v, h, r16, q16, h16 = b1
+    assert torch.equal(r16.view(torch.int16), r.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(q16.view(torch.int16), q.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(h16.view(torch.int16), h.to(torch.bfloat16).view(torch.int16))
+
+
 @pytest.mark.parametrize("batch", [1, 3, 8])
 def test_decoder_layers_chain(batch, monkeypatch):
     monkeypatch.setenv("KQ_WG_WAVES", "8")      # single launches with the chain's workgroup shape
