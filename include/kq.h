@@ -35,8 +35,9 @@
  *     a non-zero KQ_ERR_* code and enqueues nothing.  A failed launch returns
  *     KQ_ERR_HIP.  No C++ exception crosses the boundary.
  *   - `cols` (K) must be a positive multiple of 256; `rows` (M) >= 1.
- *   - GEMV calls on one device share a library-owned scratch area (partial sums
- *     of K-split row tiles); calls that overlap in time on one device (different
+ *   - GEMV calls on one device share a library-owned scratch area (about 69 MiB:
+ *     partial sums of K-split row tiles, the sums of squares of head-norm heads,
+ *     arrival counters); calls that overlap in time on one device (different
  *     streams without ordering) race on it.  kq_init allocates it; otherwise the
  *     first GEMV call on a device does (so that first call must not be made
  *     inside a stream capture).
@@ -290,9 +291,9 @@ typedef struct kq_chain kq_chain;
 /*
  * Plan a chain of n_steps (1..65536) steps on the current device: validates
  * every step as kq_gemv_multi would, sizes the persistent grid from the
- * kernel's occupancy, and allocates the chain's device memory (partial sums,
- * 64 MiB, plus about 2.4 KB per step for the step table and the step
- * barrier's words).  Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
+ * kernel's occupancy, and allocates the chain's device memory (partial sums
+ * and head-norm sums, about 69 MiB, plus about 2.5 KB per step for the step
+ * table and the step barrier's words).  Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
  * Every x must also satisfy ((batch-1)*ldx + cols) * element size < 2^31.
  * On success *out owns the plan; release it with kq_chain_destroy.
  */
