@@ -25,6 +25,7 @@ import ctypes
 import dataclasses
 import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -50,11 +51,19 @@ def tok_s(ms_per_step: float, batch: int = 1) -> float:
     return batch * 1e3 / ms_per_step
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed: what the kernels are built from."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library's code (comments and layout ignored) and of its build script."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "quant_weight_streaming_amd", "csrc", "*"))) + \
-            [os.path.join(ROOT, "quant_weight_streaming_amd", "build.py")]:
-        h.update(open(p, "rb").read())
+    for p in sorted(glob.glob(os.path.join(ROOT, "quant_weight_streaming_amd", "csrc", "*"))):
+        h.update(code_text(open(p).read()).encode())
+    h.update(open(os.path.join(ROOT, "quant_weight_streaming_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -292,7 +292,8 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
 
 // ---------------------------------------------------------------- matrix-core path
 //
-// With bf16 activations the products q * x of a unit go through
+// With 3 or more staged bf16 rows (bf16 activations, or fp32 activations as
+// hi and lo rows) the products q * x of a unit go through
 // v_mfma_f32_16x16x32_bf16 instead of v_dot2.  The operands are arranged
 // block-diagonally so that the instruction consumes the lane == row layout
 // as it is: for one block of 8 consecutive columns k0..k0+7,

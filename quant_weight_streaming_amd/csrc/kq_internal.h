@@ -45,13 +45,11 @@ struct GemvArgs {
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even
   // runs of upw units per wavefront over the whole unit range.
   int32_t n_win, win_base, win_extra, wg_per_win, tiles_per_wg, n_tiles;
-  float* partial;                      // scratch: [workgroups][2] (windows: [n_win][n_tiles]) x [KQ_MAX_BATCH][64]
+  float* partial;                      // scratch: [workgroups][2] (windows: [n_win][n_tiles]) slots of
+                                       // kPartialStride floats
   uint32_t* counters;                  // scratch: arrival counters per split tile, zero between calls
 };
 
-// Launch the GEMV of one weight type with workgroups of `nw` (4 or 8)
-// wavefronts, on the matrix cores (`mf`, bf16 activations and batch >= 2 only)
-// or on the dot2 VALU path.
 // Control words of a chain launch (device memory owned by the chain).
 struct ChainCtl {
   uint32_t* arrive;    // [step][workgroup]: the run's tag once the workgroup finished the step
@@ -81,6 +79,10 @@ hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t 
 template <int B, bool XF32>
 hipError_t launch_chain_wide(const ChainArgs& c, int grid, size_t lds, hipStream_t s, int* occupancy);
 
+// Launch the GEMV of one weight type over `rows` staged activation rows (the
+// batch, or twice it for fp32 activations) with workgroups of `nw` (4 or 8)
+// wavefronts, on the matrix cores (`mf`, from 2 staged rows) or on the dot2
+// VALU path.
 template <int QT>
 hipError_t launch_gemv_type(int xtype, int rows, int nw, bool mf, const GemvArgs& a, int grid, size_t lds,
                             hipStream_t s);
