@@ -258,8 +258,8 @@ int kq_gather_rows(int type, const void *w, int64_t rows, int64_t cols, const in
  * j+1 may be y of step j (or of any earlier step): fp32 activations, with ldx
  * = ldy.  A chain runs 8-wavefront workgroups, one per CU (KQ_WG_WAVES = 4 or 8
  * sets the shape of chains and single launches alike).  Single launches use the
- * same shape above batch 1; at batch 1 they default to two 4-wavefront
- * workgroups per CU.  With the same shape the results are those of the same
+ * same shape above batch 1; at batch 1 they default to one 4-wavefront
+ * workgroup per CU.  With the same shape the results are those of the same
  * kq_gemv_multi calls made in order (bitwise: each step runs the same
  * arithmetic in the same order); otherwise each step is within the GEMV's
  * tolerance of them.

@@ -93,16 +93,19 @@ static hipError_t launch_gemv(int type, int xtype, int batch, int nw, bool mf, c
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Tuning knobs, read per call: target wavefronts per CU (KQ_WAVES_PER_CU, default
-// 8) and wavefronts per workgroup (KQ_WG_WAVES, 4 or 8).  From batch 2 the
-// default is 8: one workgroup per CU stages the activations of its columns once
-// for all of its wavefronts.  At batch 1 it is 4 (two workgroups per CU, fixed
-// runs); 8 gives one workgroup per CU whose wavefronts share its units
-// dynamically, which evens out the CU's wavefronts but measured no faster.
-static int waves_per_cu() {
+// Tuning knobs, read per call: target wavefronts per CU (KQ_WAVES_PER_CU) and
+// wavefronts per workgroup (KQ_WG_WAVES, 4 or 8).  From batch 2 the default is
+// one 8-wavefront workgroup per CU, which stages the activations of its columns
+// once for all of its wavefronts.  A single launch at batch 1 runs one
+// 4-wavefront workgroup per CU with fixed runs: on the 209-launch sweep that is
+// about 5% faster than two such workgroups per CU or one of 8 wavefronts (one
+// wavefront per SIMD, twice the units per run).  A chain keeps 8 wavefronts per
+// CU at every batch (its persistent grid and its steps' plans).
+static int waves_per_cu(bool single, int srows, int nw) {
   const char* e = getenv("KQ_WAVES_PER_CU");
   const int x = e ? atoi(e) : 0;
-  return (x >= 1 && x <= 32) ? x : 8;
+  if (x >= 1 && x <= 32) return x;
+  return single && srows == 1 && nw == 4 ? 4 : 8;
 }
 
 
@@ -131,9 +134,7 @@ static int matrix_cores_from() {
 }
 
 // Wavefronts per workgroup of a single launch (KQ_WG_WAVES = 4 or 8
-// overrides): two 4-wavefront workgroups per CU at batch 1, whose larger number
-// of waves in flight shortens the launch's start; one 8-wavefront workgroup
-// per CU above.
+// overrides): 4 at batch 1 (one workgroup per CU, see waves_per_cu), 8 above.
 static int wg_waves(int batch) {
   const char* e = getenv("KQ_WG_WAVES");
   const int x = e ? atoi(e) : 0;
@@ -192,8 +193,8 @@ struct Plan {
 static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* const* y16,
                      const int64_t* ldy16, int cus,
-                     int64_t max_grid, int force_nw, uint32_t epi, float rms_eps, float head_eps, float* partial,
-                     uint32_t* counters, Plan* out) {
+                     int64_t max_grid, int force_nw, bool single, uint32_t epi, float rms_eps, float head_eps,
+                     float* partial, uint32_t* counters, Plan* out) {
   const int64_t n_cols = cols / 256;
   const bool norm = rms_eps > 0.0f;
   GemvArgs a{};
@@ -221,8 +222,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   if (n_units + 2 * n_cols + 8 * (int64_t)kMaxGroups >= INT32_MAX) return KQ_ERR_RANGE;
   const int64_t max_groups = max_grid < kMaxGroups ? max_grid : kMaxGroups;
 
-  // An even run of `upw` units per wavefront, about waves_per_cu() wavefronts
-  // per CU, nw wavefronts per workgroup.  A workgroup stages the activations
+  // An even run of `upw` units per wavefront, about `wpc` wavefronts per CU,
+  // nw wavefronts per workgroup.  A workgroup stages the activations
   // (and sub-block sums) of the columns its nw*upw units touch in LDS, within
   // `budget` bytes (64 KiB leaves room for two 4-wavefront workgroups per CU,
   // 112 KiB is for one 8-wavefront workgroup), plus its wavefronts' partial sums.
@@ -238,7 +239,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   const int64_t tile_sums = (int64_t)nw * 2 * srows * 64 * sizeof(float);
   int64_t budget = nw == 8 ? 112 * 1024 : 64 * 1024;
   if (budget > (int64_t)kMaxLds - tile_sums - 2048) budget = (int64_t)kMaxLds - tile_sums - 2048;
-  const int64_t target = (int64_t)cus * waves_per_cu();
+  const int wpc = waves_per_cu(single, srows, nw);
+  const int64_t target = (int64_t)cus * wpc;
   int64_t upw = (n_units + target - 1) / target;
   if (upw < 1) upw = 1;
   const int64_t per_col =
@@ -266,7 +268,8 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   const int forced_r = aligned_tiles();
   if (((srows >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
       n_win * tiles <= 2 * (int64_t)kMaxGroups) {
-    int64_t g_target = (int64_t)cus * waves_per_cu() / nw;
+    int64_t g_target = (int64_t)cus * wpc / nw;
+    if (g_target < 1) g_target = 1;
     if (g_target > max_groups) g_target = max_groups;
     int64_t g_win = g_target / n_win > 0 ? g_target / n_win : 1;
     int64_t r = forced_r > 0 ? forced_r : (tiles + g_win - 1) / g_win;
@@ -381,13 +384,13 @@ static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows,
   rc = device_state(dev, &st);
   if (rc != KQ_OK) return rc;
   Plan p{};
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 0, epi,
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 0, true, epi,
                  rms_eps, head_eps,
                  st->partial,
                  st->counters, &p);
   if (rc == KQ_ERR_RANGE && wg_waves(xtype == KQ_X_F32 ? 2 * batch : batch) == 8)   // too many units per
                                                                                         // workgroup: 4-wave runs
-    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 4, epi,
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 4, true, epi,
                    rms_eps, head_eps,
                    st->partial,
                    st->counters, &p);
@@ -632,7 +635,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, st.y16,
                          st.ldy16, cus,
-                         max_grid, nw, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, nullptr, nullptr, &plans[j]);
+                         max_grid, nw, false, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, nullptr, nullptr, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && srows <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;
