@@ -237,6 +237,20 @@ def test_workgroup_sizes(qtype, batch, waves, monkeypatch):
     run_case(qtype, 5 * 64 + 9, 7 * 256, batch, "bf16", 400 + batch, check_w=False)
 
 
+@pytest.mark.parametrize("qtype", ["q4k", "q6k"])
+@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("waves,per_cu", [("4", "2"), ("4", "4"), ("4", "6"), ("4", "12"), ("8", "8"), ("8", "16")])
+@pytest.mark.parametrize("cols", [20 * 256, 122 * 256])
+def test_launch_geometries(qtype, batch, waves, per_cu, cols, monkeypatch):
+    """Launch geometries (KQ_WG_WAVES x KQ_WAVES_PER_CU): runs of other lengths, so tiles split at other
+    points between wavefronts and workgroups, fewer workgroups than CUs, and grids larger than what is
+    resident at once; 41 ragged tiles of 20 columns (gate+up's K) and 5 of 122 (down's K)."""
+    monkeypatch.setenv("KQ_WG_WAVES", waves)
+    monkeypatch.setenv("KQ_WAVES_PER_CU", per_cu)
+    rows = (41 if cols == 20 * 256 else 5) * 64 - 23
+    run_case(qtype, rows, cols, batch, "bf16", 700 + batch, check_w=False)
+
+
 @pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("batch,xdtype,windows_from", [(4, "bf16", None), (8, "bf16", None), (2, "bf16", "2"),
                                                        (4, "f32", None), (1, "bf16", "1")])
