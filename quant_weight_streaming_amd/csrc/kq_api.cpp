@@ -93,6 +93,13 @@ static hipError_t launch_gemv(int type, int xtype, int batch, int nw, bool mf, c
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Wavefronts per workgroup forced by KQ_WG_WAVES (4 or 8), else 0.
+static int forced_wg_waves() {
+  const char* e = getenv("KQ_WG_WAVES");
+  const int x = e ? atoi(e) : 0;
+  return (x == 4 || x == 8) ? x : 0;
+}
+
 // Tuning knobs, read per call: target wavefronts per CU (KQ_WAVES_PER_CU) and
 // wavefronts per workgroup (KQ_WG_WAVES, 4 or 8).  From batch 2 the default is
 // one 8-wavefront workgroup per CU, which stages the activations of its columns
@@ -100,12 +107,14 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // 4-wavefront workgroup per CU with fixed runs: on the 209-launch sweep that is
 // about 5% faster than two such workgroups per CU or one of 8 wavefronts (one
 // wavefront per SIMD, twice the units per run).  A chain keeps 8 wavefronts per
-// CU at every batch (its persistent grid and its steps' plans).
+// CU at every batch (its persistent grid and its steps' plans); so does a single
+// launch whose workgroup size KQ_WG_WAVES forces, which then has the shape of a
+// chain step with the same setting.
 static int waves_per_cu(bool single, int srows, int nw) {
   const char* e = getenv("KQ_WAVES_PER_CU");
   const int x = e ? atoi(e) : 0;
   if (x >= 1 && x <= 32) return x;
-  return single && srows == 1 && nw == 4 ? 4 : 8;
+  return single && srows == 1 && nw == 4 && !forced_wg_waves() ? 4 : 8;
 }
 
 
@@ -136,10 +145,8 @@ static int matrix_cores_from() {
 // Wavefronts per workgroup of a single launch (KQ_WG_WAVES = 4 or 8
 // overrides): 4 at batch 1 (one workgroup per CU, see waves_per_cu), 8 above.
 static int wg_waves(int batch) {
-  const char* e = getenv("KQ_WG_WAVES");
-  const int x = e ? atoi(e) : 0;
-  if (x == 4 || x == 8) return x;
-  return batch == 1 ? 4 : 8;
+  const int x = forced_wg_waves();
+  return x ? x : batch == 1 ? 4 : 8;
 }
 
 // Wavefronts per workgroup of a chain (KQ_WG_WAVES overrides): 8 at every
@@ -148,9 +155,8 @@ static int wg_waves(int batch) {
 // CU runs half-empty until the step barrier; at batch 1 the eight wavefronts
 // of one workgroup instead take its units one at a time.
 static int chain_wg_waves() {
-  const char* e = getenv("KQ_WG_WAVES");
-  const int x = e ? atoi(e) : 0;
-  return (x == 4 || x == 8) ? x : 8;
+  const int x = forced_wg_waves();
+  return x ? x : 8;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS of one CU

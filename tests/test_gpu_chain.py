@@ -22,8 +22,8 @@ DEV = "cuda:0"
 
 @pytest.fixture(autouse=True)
 def _chain_shape(monkeypatch):
-    """Single launches with the chain's workgroup shape (8 wavefronts; at batch 1 single launches default to 4),
-    so a chain step and its single launch run the same arithmetic in the same order."""
+    """Single launches with the chain's workgroup shape (8 wavefronts; at batch 1 single launches default to one
+    4-wavefront workgroup per CU), so a chain step and its single launch run the same arithmetic in the same order."""
     monkeypatch.setenv("KQ_WG_WAVES", "8")
 SENTINEL = 1.0e30
 
@@ -237,6 +237,21 @@ def test_chain_dynamic_units(monkeypatch):
     torch.cuda.synchronize()
     assert ch.status() == 0
     _check_steps(steps, hosts, _singles(steps), "chain dynamic units")
+    ch.close()
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_chain_four_wave_workgroups(batch, monkeypatch):
+    """KQ_WG_WAVES=4 forces 4-wavefront workgroups on chains and single launches alike (two per CU): the
+    chain's steps still match their single launches bitwise."""
+    monkeypatch.setenv("KQ_WG_WAVES", "4")
+    say(f"case chain four-wave workgroups B={batch}")
+    steps, hosts = _independent_steps(MIXED, batch, "bf16", f"w4{batch}")
+    ch = kq.Chain(steps, batch)
+    ch.run()
+    torch.cuda.synchronize()
+    assert ch.status() == 0
+    _check_steps(steps, hosts, _singles(steps), "chain four-wave workgroups")
     ch.close()
 
 
