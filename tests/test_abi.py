@@ -27,6 +27,16 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback path: without the built library every entry point raises instead of computing on the CPU."""
+    monkeypatch.setattr(kq, "LIB_PATH", str(tmp_path / "libkq.so"))
+    monkeypatch.setattr(kq, "_lib", None)
+    with pytest.raises(ImportError):
+        kq.lib()
+    with pytest.raises(ImportError):
+        kq.kq_repacked_bytes("q4k", 64, 256)
+
+
 def test_version_and_sizes():
     assert kq.kq_abi_version() == 1
     assert kq.kq_repacked_bytes("q4k", 256, 1024) == 256 * 4 * 144
