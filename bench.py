@@ -573,7 +573,9 @@ def summarize_trace(src: str, cmd: str) -> str:
             if key == gk:
                 split[prev == gk].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
             prev = key
-        out += ["", f"gate+up at batch 1 ({gk[0]}, {gk[1]} workgroups), by what ran before it (durations in us):"]
+        out += ["", f"gate+up at batch 1 ({gk[0]}, {gk[1]} workgroups), by what ran before it (durations in us).",
+                "This is the roofline kernel: bench.py's roofline.avg_launch_us is its cost inside the sweep. The",
+                "stats line above averages every launch of the template (QKV, O and gate+up alike)."]
         for b2b, name in ((False, "after another GEMV (the sweep)"), (True, "after another gate+up (class graph)")):
             d = sorted(split[b2b])
             if d:
