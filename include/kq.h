@@ -25,6 +25,16 @@
  *   Q4_K, Q5_K: w = d * sc_g * q - dmin * m_g    (sub-blocks g of 32 weights)
  *   Q6_K      : w = d * sc_g * (q - 32)          (sub-blocks g of 16 weights)
  *
+ * Rounding of y: the quants enter the dot products as exact bf16 operands
+ * (q, or 4(q - 32) for Q6_K, with no offset), so each sub-block's sum is
+ * rounded relative to its own terms and y is within 1e-4 * sum_k |w x| of the
+ * exact product, also on rows whose sum comes from a single weight.  The one
+ * precondition: Q4_K/Q5_K add the two exact terms d*sc*sum(q x) and
+ * dmin*m*sum(x) per sub-block in fp32, so where they cancel for EVERY element
+ * of a sub-block (w = 0 with q and m nonzero, a legal but degenerate encoding)
+ * the error is bounded by 2^-19 * sum (|d sc q| + |dmin m|) |x| over that
+ * sub-block instead.
+ *
  * Conventions for every entry point:
  *   - Pointers named w, gguf, out, x, y are DEVICE pointers owned by the caller;
  *     array-of-pointer and array-of-size arguments of kq_gemv_multi are HOST

@@ -16,15 +16,26 @@
 //                     H_g of the two high bits of sub-blocks 4k..4k+3;
 //                     12: the 16 int8 sub-block scales; tail: fp16 d.
 //
-// Inside a quant word for sub-block elements 8j .. 8j+7, nibble p (bits
-// 4p..4p+3) holds element 8j+2p and bits 16+4p.. hold element 8j+2p+1, so
-// ((word >> 4p) & 0x000F000F) | 0x43004300 is a pair of bf16 values
-// (128 + q_{8j+2p}, 128 + q_{8j+2p+1}) matching the bf16 activation pair at the
-// same position.  The high-bit words put the bits of pair pi = 4j+p at bit pi
-// (Q5_K; plus 16 for the second element) or bits 2pi..2pi+1 (Q6_K; plus 16).
-// bf16 represents 128 + q exactly for q < 128, so every weight enters the dot
-// product exactly; the 128 (Q6_K: 160 = 128 + 32) offset is removed per
-// sub-block with a sum of the activations accumulated in the same order.
+// The quants become EXACT bf16 operands, with no offset, so every sub-block's
+// dot product S = sum v * x is rounded relative to sum |v x| alone:
+//   Q4_K: a quant word for sub-block elements 8j .. 8j+7 holds element 8j+k
+//         (k < 4) in the low nibble of byte k and element 8j+4+k in its high
+//         nibble.  word & 0x0F0F0F0F and (word >> 4) & 0x0F0F0F0F put one quant
+//         per byte; read as OCP fp8 e4m3, bytes 0..15 are the subnormal and
+//         first normal binade, i.e. exactly q * 2^-9, and the conversion to
+//         bf16 with scale 2^9 (v_cvt_scalef32_pk_bf16_fp8, two bytes per
+//         instruction) yields the pair (q, q') exactly.
+//   Q5_K: the same low nibbles, plus the fifth bit of element 8j+4h+k at bit
+//         8k + (2j+h) of H_g; merged into bit 4 of the byte, each byte holds
+//         q in 0..31 and v_cvt_f32_ubyte{0..3} + v_cvt_pk_bf16_f32 give
+//         exact bf16 q.
+//   Q6_K: element 8j+4h+k of a sub-block keeps its low nibble at bits 8k+4h of
+//         low word j and its two high bits, with the top one inverted, at bits
+//         8k+2m (m = 2j+h) of H_g.  The byte (nibble << 2) | (high << 6) is
+//         then the two's-complement int8 4*(q-32); the sign-extending byte
+//         conversion (v_cvt_f32_i32 with an SDWA byte select) and
+//         v_cvt_pk_bf16_f32 give exact bf16 4*(q-32), and d*sc/4 scales it.
+// Pairs follow the activation pairs (x_{2i}, x_{2i+1}) of the same position.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -87,60 +98,73 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-template <int S> __device__ __forceinline__ uint32_t shift_signed(uint32_t v) {
-  if constexpr (S > 0) return v >> S;
-  else if constexpr (S < 0) return v << (-S);
-  else return v;
-}
-
 __device__ __forceinline__ uint32_t word(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// bf16 pairs (offset + q) of sub-block G of one super-block held in chunks c[].
-// Q4_K/Q5_K: 16 pairs, offset 128; Q6_K: 8 pairs, offset 128 (q in 0..63).
+// Exact bf16 operand pairs of sub-block G of one super-block held in chunks
+// c[]: Q4_K/Q5_K q (16 pairs), Q6_K 4*(q-32) (8 pairs); see the layout above.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t v) {
+  // scale 2^9: e4m3 bytes 0..15 are q * 2^-9, so the result is exactly q
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 512.0f, HI_WORD));
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  // small integers: exact in bf16 (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
 template <int QT>
-__device__ __forceinline__ void unpack_pairs(const u32x4* c, int G, uint32_t M, uint32_t K, uint32_t* pr) {
-  if constexpr (QT == KQ_Q4_K || QT == KQ_Q5_K) {
+__device__ __forceinline__ void unpack_pairs(const u32x4* c, int G, uint32_t* pr) {
+  if constexpr (QT == KQ_Q4_K) {
     const u32x4 q = c[1 + G];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t v = word(q, j);
-      pr[4 * j + 0] = (v & M) | K;
-      pr[4 * j + 1] = ((v >> 4) & M) | K;
-      pr[4 * j + 2] = ((v >> 8) & M) | K;
-      pr[4 * j + 3] = ((v >> 12) & M) | K;
+      const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+      pr[4 * j + 0] = fp8x2_to_bf16x2<false>(lo);
+      pr[4 * j + 1] = fp8x2_to_bf16x2<true>(lo);
+      pr[4 * j + 2] = fp8x2_to_bf16x2<false>(hi);
+      pr[4 * j + 3] = fp8x2_to_bf16x2<true>(hi);
     }
-    if constexpr (QT == KQ_Q5_K) {
-      const uint32_t H = word(c[9 + G / 4], G % 4);
-      const uint32_t M5 = in_vgpr(0x00100010u);
-#define KQ_Q5_HB(PI) pr[PI] = and_or(shift_signed<(PI) - 4>(H), M5, pr[PI]);
-      KQ_Q5_HB(0) KQ_Q5_HB(1) KQ_Q5_HB(2) KQ_Q5_HB(3) KQ_Q5_HB(4) KQ_Q5_HB(5) KQ_Q5_HB(6) KQ_Q5_HB(7)
-      KQ_Q5_HB(8) KQ_Q5_HB(9) KQ_Q5_HB(10) KQ_Q5_HB(11) KQ_Q5_HB(12) KQ_Q5_HB(13) KQ_Q5_HB(14) KQ_Q5_HB(15)
-#undef KQ_Q5_HB
+  } else if constexpr (QT == KQ_Q5_K) {
+    const u32x4 q = c[1 + G];
+    const uint32_t H = word(c[9 + G / 4], G % 4);
+    const uint32_t M4 = in_vgpr(0x0F0F0F0Fu), M5 = in_vgpr(0x10101010u);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t v = word(q, t / 2);
+      const uint32_t base = (t & 1) ? ((v >> 4) & M4) : (v & M4);
+      const uint32_t hs = t <= 4 ? (H << (4 - t)) : (H >> (t - 4));
+      const uint32_t b = and_or(hs, M5, base);
+      pr[2 * t + 0] = pk_bf16((float)(b & 0xFFu), (float)((b >> 8) & 0xFFu));
+      pr[2 * t + 1] = pk_bf16((float)((b >> 16) & 0xFFu), (float)(b >> 24));
     }
   } else {
     const u32x4 lq = c[G / 2];
-    const uint32_t L0 = word(lq, (G % 2) * 2), L1 = word(lq, (G % 2) * 2 + 1);
     const uint32_t H = word(c[8 + G / 4], G % 4);
-    const uint32_t M6 = in_vgpr(0x00300030u);
-    // pair pi: nibbles of L_{pi/4} >> 4(pi%4), two high bits of H >> (2pi - 4)
-#define KQ_Q6_PAIR(PI, L, P) pr[PI] = and_or(shift_signed<2 * (PI) - 4>(H), M6, and_or(shift_signed<4 * (P)>(L), M, K));
-    KQ_Q6_PAIR(0, L0, 0) KQ_Q6_PAIR(1, L0, 1) KQ_Q6_PAIR(2, L0, 2) KQ_Q6_PAIR(3, L0, 3)
-    KQ_Q6_PAIR(4, L1, 0) KQ_Q6_PAIR(5, L1, 1) KQ_Q6_PAIR(6, L1, 2) KQ_Q6_PAIR(7, L1, 3)
-#undef KQ_Q6_PAIR
+    const uint32_t M6 = in_vgpr(0x3C3C3C3Cu), MH = in_vgpr(0xC0C0C0C0u);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t L = word(lq, (G % 2) * 2 + m / 2);
+      const uint32_t lf = ((m & 1) ? (L >> 2) : (L << 2)) & M6;
+      const uint32_t b = and_or(H << (6 - 2 * m), MH, lf);   // int8 bytes 4*(q-32)
+      pr[2 * m + 0] = pk_bf16((float)(int8_t)(b & 0xFFu), (float)(int8_t)((b >> 8) & 0xFFu));
+      pr[2 * m + 1] = pk_bf16((float)(int8_t)((b >> 16) & 0xFFu), (float)(int8_t)(b >> 24));
+    }
   }
 }
 
-// Per-sub-block coefficients from the super-block header.
-//   Q4_K/Q5_K: a[g] = d*sc_g, cm[g] = dmin*m_g * cm_scale (exact products).
-//   Q6_K     : a[g] = d*sc_g.
+// Per-sub-block coefficients from the super-block header (exact products).
+//   Q4_K/Q5_K: a[g] = d*sc_g, cm[g] = dmin*m_g.
+//   Q6_K     : a[g] = d*sc_g / 4 (the operands are 4*(q-32)).
 template <int QT>
-__device__ __forceinline__ void sb_coeffs(const u32x4* c, uint32_t d6bits, float cm_scale, float* a, float* cm) {
+__device__ __forceinline__ void sb_coeffs(const u32x4* c, uint32_t d6bits, float* a, float* cm) {
   if constexpr (QT == KQ_Q4_K || QT == KQ_Q5_K) {
     const u32x4 h = c[0];
     const float d = f16_bits_to_f32(h.x);
-    const float dm = f16_bits_to_f32(h.x >> 16) * cm_scale;
+    const float dm = f16_bits_to_f32(h.x >> 16);
     const uint32_t sc_lo = h.y & 0x3F3F3F3Fu;
     const uint32_t m_lo = h.z & 0x3F3F3F3Fu;
     const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
@@ -153,7 +177,7 @@ __device__ __forceinline__ void sb_coeffs(const u32x4* c, uint32_t d6bits, float
       cm[4 + i] = dm * (float)((m_hi >> (8 * i)) & 0xFFu);
     }
   } else {
-    const float d = f16_bits_to_f32(d6bits);
+    const float d = f16_bits_to_f32(d6bits) * 0.25f;
     const u32x4 s = c[12];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -161,7 +185,6 @@ __device__ __forceinline__ void sb_coeffs(const u32x4* c, uint32_t d6bits, float
       a[i] = d * (float)sc;
     }
     (void)cm;
-    (void)cm_scale;
   }
 }
 

@@ -13,19 +13,18 @@
 // tile (the last to arrive adds all pieces in workgroup or window order).
 // Fixed summation orders make y deterministic.
 //
-// Per super-block and lane the 4/5/6-bit quants become bf16 pairs (128 + q)
-// with shift/and-or only, and v_dot2_f32_bf16 dots them with the activation
-// pair of the same position.  All 64 lanes (rows) of a wavefront share the
-// column, so the activations are wavefront-uniform; the workgroup stages the
-// activations of its columns in LDS once and every wavefront reads them with
-// broadcast LDS loads.  Per sub-block the sum S of (128 + q) * x is corrected
-// with T, the same chain of dot2 over (128, 128) (Q6_K: (160, 160) = 128 + 32),
-// staged alongside; when every q is zero (Q6_K: 32) S and T are bitwise equal
-// and the sub-block contributes exactly zero.  Then
-//   Q4_K/Q5_K: acc += (d*sc) * (S - T) - (dmin*m/128) * T
-//   Q6_K     : acc += (d*sc) * (S - T).
-// With fp32 activations the weights are converted to exact fp32 q and used
-// with v_fma (S = sum q*x, T = sum x).
+// Per super-block and lane the 4/5/6-bit quants become exact bf16 operands
+// (kq_common.h: Q4_K/Q5_K q, Q6_K 4*(q-32)), and v_dot2_f32_bf16 dots them
+// with the activation pair of the same position.  All 64 lanes (rows) of a
+// wavefront share the column, so the activations are wavefront-uniform; the
+// workgroup stages the activations of its columns in LDS once and every
+// wavefront reads them with broadcast LDS loads.  Per sub-block g, with
+// S = sum v*x over its elements and (Q4_K/Q5_K) X = sum x, staged alongside:
+//   Q4_K/Q5_K: acc += (d*sc_g) * S - (dmin*m_g) * X
+//   Q6_K     : acc += (d*sc_g/4) * S.
+// S carries no offset, so its rounding error is relative to sum |v x|.
+// fp32 activations are staged as two bf16 rows each, hi = bf16(x) and
+// lo = bf16(x - hi), whose sums are added before the epilogue (XStage).
 //
 // The weight stream is buffered in registers: while one unit is computed the
 // next DEPTH-1 are in flight.  The main loop issues each refill before the
@@ -78,9 +77,9 @@ __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, int lane, u3
 // sub-block of one batch row; each thread issues the loads of IPT items (128
 // bytes) before it stores any of them, so a round costs one memory round trip,
 // and the first round is issued ahead of the weight prologue so that waiting
-// for it does not wait for the weights.  On the dot2 path the store also forms
-// T, the item's activation sum in the dot product's own order (bf16: the same
-// dot2 chain over (128,128), Q6_K (160,160); fp32: sum x), at T[ic * SB + g][b].
+// for it does not wait for the weights.  On the dot2 path of Q4_K/Q5_K the
+// store also forms T, the item's activation sum X (a dot2 chain over (1, 1)),
+// at T[ic * SB + g][b].
 // fp32 -> bf16 bits, round to nearest even (finite values).
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -179,8 +178,8 @@ struct XStage {
       }
       if (i < n) {
         const int g = i % SB, q = i / SB, b = q % BU, ic = q / BU;
-        const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;  // bf16 (160,160) / (128,128)
-        // T: the sub-block's products with every weight at the offset, per staged row
+        const uint32_t kc = 0x3F803F80u;   // bf16 (1, 1)
+        // T: the sub-block's activation sum X, per staged row
         auto tsum = [&](const u32x4& w, float t) {
           t = dot2_bf16(kc, w.x, t);
           t = dot2_bf16(kc, w.y, t);
@@ -237,32 +236,34 @@ struct XStage {
 };
 
 // Accumulate one unit into acc[B].  Xc / Tc: the staged (bf16) activations and
-// sums of the unit's column.  The (sub-block, batch row) steps are
-// software-pipelined: each step reads the next step's activations from LDS
-// before its own dot products, and a scheduling barrier keeps the compiler from
-// hoisting reads any further (which would cost registers and occupancy).
+// (Q4_K/Q5_K) sub-block activation sums of the unit's column.  The (sub-block,
+// batch row) steps are software-pipelined: each step reads the next step's
+// activations from LDS before its own dot products, and a scheduling barrier
+// keeps the compiler from hoisting reads any further (which would cost
+// registers and occupancy).
 template <int QT, int B>
 __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, const uint32_t* Xc, const float* Tc,
-                                             float* acc, uint32_t M, uint32_t K) {
+                                             float* acc) {
   using F = Fmt<QT>;
   constexpr int SB = F::kSubBlocks, NP = F::kPairs;
+  constexpr bool MINS = QT != KQ_Q6_K;
   constexpr int XW = 128;                           // 32-bit words per staged row
   constexpr int NV = NP / 4;                        // 16-byte LDS reads per sub-block and batch row
   constexpr int SWD = F::kSubW / 2;
   float ca[SB], cm[SB];
-  sb_coeffs<QT>(buf, d6, 0.0078125f, ca, cm);
+  sb_coeffs<QT>(buf, d6, ca, cm);
   u32x4 xc[NV], xn[NV];
-  float tc, tn = 0.0f;
+  float tc = 0.0f, tn = 0.0f;
   {
     const u32x4* xl = reinterpret_cast<const u32x4*>(Xc);
 #pragma unroll
     for (int v = 0; v < NV; ++v) xc[v] = xl[v];
-    tc = Tc[0];
+    if constexpr (MINS) tc = Tc[0];
   }
   uint32_t pr[NP];
 #pragma unroll
   for (int g = 0; g < SB; ++g) {
-    unpack_pairs<QT>(buf, g, M, K, pr);
+    unpack_pairs<QT>(buf, g, pr);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const int gn = (b + 1 < B) ? g : g + 1, bn = (b + 1 < B) ? b + 1 : 0;
@@ -270,7 +271,7 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         const u32x4* xl = reinterpret_cast<const u32x4*>(Xc + bn * XW + gn * SWD);
 #pragma unroll
         for (int v = 0; v < NV; ++v) xn[v] = xl[v];
-        tn = Tc[gn * B + bn];
+        if constexpr (MINS) tn = Tc[gn * B + bn];
       }
       float s = 0.0f;
 #pragma unroll
@@ -280,8 +281,8 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         s = dot2_bf16(pr[4 * v + 2], xc[v].z, s);
         s = dot2_bf16(pr[4 * v + 3], xc[v].w, s);
       }
-      acc[b] = __builtin_fmaf(ca[g], s - tc, acc[b]);
-      if constexpr (QT != KQ_Q6_K) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
+      acc[b] = __builtin_fmaf(ca[g], s, acc[b]);
+      if constexpr (MINS) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
 #pragma unroll
       for (int v = 0; v < NV; ++v) xc[v] = xn[v];
       tc = tn;
@@ -297,7 +298,7 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
 // v_mfma_f32_16x16x32_bf16 instead of v_dot2.  The operands are arranged
 // block-diagonally so that the instruction consumes the lane == row layout
 // as it is: for one block of 8 consecutive columns k0..k0+7,
-//   B operand: lane l supplies its own row's 8 weights (128 + q, bf16), which is
+//   B operand: lane l supplies its own row's 8 exact bf16 operands, which is
 //              B[8j + kk][n] with n = l % 16, j = l / 16;
 //   A operand: A[4j + b][8j + kk] = x[b][k0 + kk] and zero for the other 24 of
 //              the 32 columns of row 4j + b, so lane la holds x[la % 4] when
@@ -307,11 +308,9 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
 //              batch row (four batch rows per instruction; a second set covers
 //              batch rows 4..7).
 // A sub-block is 4 (Q6_K: 2) such instructions accumulating in place, then
-// scaled on the VALU as in the dot2 path.  The activation sum T is the same
-// sequence of instructions with every weight equal to the offset (128, Q6_K
-// 160); the matrix core evaluates each output position with the same
-// arithmetic, so T is computed once per column and sub-block while staging,
-// and a sub-block whose quants are all zero (Q6_K: 32) gives S == T exactly.
+// scaled on the VALU as in the dot2 path.  For Q4_K/Q5_K the activation sum X
+// of each column's sub-blocks is the same instruction sequence with every
+// operand 1, computed once per column and sub-block while staging.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -368,14 +367,14 @@ __device__ __forceinline__ void mfma_chain2<2>(f32x4& s0, f32x4& s1, const bf16x
 // Byte offsets inside the workgroup's LDS for the matrix-core path:
 //   X [ic][b][256] bf16 in rows of kXRow = 528 bytes (the 16-byte pad puts the
 //   four batch rows one instruction reads in different LDS banks), then
-//   T [ic][g][NB][4] floats, then Z, 512 zero bytes that the inactive operand
-//   lanes read.
+//   (Q4_K/Q5_K) T [ic][g][NB][4] floats, the sub-block activation sums, then Z,
+//   512 zero bytes that the inactive operand lanes read.
 template <int QT, int B>
 struct MfmaLds {
   static constexpr int NB = (B + 3) / 4;                       // operand sets of 4 batch rows
   static constexpr int kXRow = 528;                            // bytes per staged row of x
   static constexpr int kXCol = B * kXRow;                      // bytes of x per column
-  static constexpr int kTCol = Fmt<QT>::kSubBlocks * NB * 16;  // bytes of T per column
+  static constexpr int kTCol = QT == KQ_Q6_K ? 0 : Fmt<QT>::kSubBlocks * NB * 16;  // bytes of T per column
   static constexpr int kPerCol = kXCol + kTCol;
 };
 
@@ -387,13 +386,11 @@ __device__ __forceinline__ int a_operand_offset(int lane, int gb, int ic, int x_
   return active ? x_base + (ic * B + b) * 528 : z_base;
 }
 
-// T for the matrix-core path, from the staged activations (after a barrier):
-// T[ic][g][gb][b'] = the sub-block's products with every weight equal to the
-// offset, as the same instruction sequence computes them.  The matrix core
-// gives every output position the same arithmetic (the value does not depend
-// on the lane group that holds it), so one chain serves four items: lane group
-// j = lane / 16 takes item 4c + j's activations into its block of the operand.
-// A wavefront runs two chains interleaved.
+// T for the matrix-core path of Q4_K/Q5_K, from the staged activations (after a
+// barrier): T[ic][g][gb][b'] = the sub-block's activation sum, as the same
+// instruction sequence computes it with every operand 1.  One chain serves four
+// items: lane group j = lane / 16 takes item 4c + j's activations into its block
+// of the operand.  A wavefront runs two chains interleaved.
 template <int QT, int B, int NW>
 __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int lane) {
   using F = Fmt<QT>;
@@ -401,7 +398,8 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
   constexpr int NB = L::NB, SB = F::kSubBlocks, KB = F::kSubW / 8;
   constexpr int H = NB <= 2 ? 2 : 1;                  // chains in flight (registers allow two up to NB 2)
   const int t_base = len * L::kXCol, z_base = t_base + len * L::kTCol;
-  const uint32_t kc = (QT == KQ_Q6_K) ? 0x43204320u : 0x43004300u;
+  static_assert(QT != KQ_Q6_K, "Q6_K has no mins and needs no activation sums");
+  const uint32_t kc = 0x3F803F80u;   // bf16 (1, 1)
   const bf16x8 bconst = __builtin_bit_cast(bf16x8, u32x4{kc, kc, kc, kc});
   const int nt = len * SB, nch = (nt + 3) / 4;
   for (int c0 = wid; c0 < nch; c0 += H * NW) {
@@ -454,18 +452,19 @@ __device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int
 // two operand sets, each sub-block's operands are read just before use.
 template <int QT, int B, bool LEAN>
 __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6, const uint8_t* const* ap,
-                                                  const float* Tc, float* acc, uint32_t M, uint32_t K) {
+                                                  const float* Tc, float* acc) {
   using F = Fmt<QT>;
   constexpr int SB = F::kSubBlocks, NP = F::kPairs, KB = F::kSubW / 8, NB = MfmaLds<QT, B>::NB;
+  constexpr bool MINS = QT != KQ_Q6_K;
   float ca[SB], cm[SB];
-  sb_coeffs<QT>(buf, d6, 0.0078125f, ca, cm);
+  sb_coeffs<QT>(buf, d6, ca, cm);
   auto scale = [&](int g, int gb, const f32x4& S, const f32x4& t) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (4 * gb + r < B) {
         float& v = acc[4 * gb + r];
-        v = __builtin_fmaf(ca[g], S[r] - t[r], v);
-        if constexpr (QT != KQ_Q6_K) v = __builtin_fmaf(-cm[g], t[r], v);
+        v = __builtin_fmaf(ca[g], S[r], v);
+        if constexpr (MINS) v = __builtin_fmaf(-cm[g], t[r], v);
       }
     }
   };
@@ -481,8 +480,9 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
         for (int gb = 0; gb < NB; ++gb)
           A[gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
 #pragma unroll
-      for (int gb = 0; gb < NB; ++gb) Tv[gb] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
-      unpack_pairs<QT>(buf, g, M, K, pr);
+      for (int gb = 0; gb < NB; ++gb)
+        Tv[gb] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
+      unpack_pairs<QT>(buf, g, pr);
       bf16x8 bop[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -502,14 +502,15 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
         for (int gb = 0; gb < NB; ++gb)
           A[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
 #pragma unroll
-      for (int gb = 0; gb < NB; ++gb) Tv[h][gb] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+      for (int gb = 0; gb < NB; ++gb)
+        Tv[h][gb] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
     };
     read_operands(0, 0);
 #pragma unroll
     for (int g = 0; g < SB; ++g) {
       const int h = g & 1;
       if (g + 1 < SB) read_operands(g + 1, h ^ 1);
-      unpack_pairs<QT>(buf, g, M, K, pr);
+      unpack_pairs<QT>(buf, g, pr);
       bf16x8 bop[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -525,7 +526,7 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
     constexpr int NPAIR = (NB + 1) / 2;
 #pragma unroll
     for (int g = 0; g < SB; ++g) {
-      unpack_pairs<QT>(buf, g, M, K, pr);
+      unpack_pairs<QT>(buf, g, pr);
       bf16x8 bop[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -541,7 +542,7 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
               A[i][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-            Tv[i] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+            Tv[i] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
           }
         }
         f32x4 S[2];
@@ -565,14 +566,14 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
             A[h][i][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-          Tv[h][i] = *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4);
+          Tv[h][i] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
         }
       }
     };
     read_pair(0, 0, 0);
 #pragma unroll
     for (int g = 0; g < SB; ++g) {
-      unpack_pairs<QT>(buf, g, M, K, pr);
+      unpack_pairs<QT>(buf, g, pr);
       bf16x8 bop[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -960,13 +961,14 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   const int c0w = cs + U0 % cw;                    // staged columns c0w, c0w+1, ... (mod n_cols)
   const int len = min(cw, U1 - U0);
   uint32_t* X = lds_words;
-  float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);
+  float* T = reinterpret_cast<float*>(lds_words + a.tsb * B * XW);   // Q4_K/Q5_K sub-block sums (dot2 path)
+  constexpr int TSB = QT == KQ_Q6_K ? 0 : SB;                         // T entries per column and row
   // the staged columns' sums of squares (normalised launches only), then the
   // per-wavefront tile sums [NW][tpw][B][64]
   const bool norm = a.rms_eps > 0.0f;
   float* Q2 = MF ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds_words) +
                                             a.tsb * MfmaLds<QT, B>::kPerCol + 512)
-                 : T + a.tsb * SB * B;
+                 : T + a.tsb * TSB * B;
   float* P = norm ? Q2 + ((a.tsb * B + 3) & ~3) : Q2;
   if (!norm) Q2 = nullptr;
   // DYN (batch 1, one 8-wavefront workgroup per CU): instead of fixed runs the
@@ -977,12 +979,13 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   // wavefront computed what.  P then holds the counter (16 bytes) and the slots
   // [U1 - U0][B][64].
   constexpr bool DYN = dyn_units<B, NW, MF>();
+  // the dynamic prologue fills buffer k with unit wid + k * NW and the LDS
+  // counter starts past them; that numbering is written for two buffers
+  static_assert(!DYN || DEPTH == 2, "dynamic units assume two weight buffers");
   const int u0 = DYN ? U0 + wid : U0 + wid * upw;
   const int u1 = DYN ? U1 : min(u0 + upw, U1);
   const bool active = u0 < U1;
   const int t0 = u0 / cw;                          // first tile of this wavefront
-  const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
-
   // The weight stream runs DEPTH-1 units ahead of the unit being computed.
   // The first DEPTH-1 units' loads go out before the activations are staged,
   // so their latency overlaps the staging.
@@ -1021,17 +1024,17 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   }
   {
     uint8_t* Xb = reinterpret_cast<uint8_t*>(lds_words);
-    xs.template store<!MF>(Xb, T, Q2, len, 0);
+    xs.template store<!MF && TSB != 0>(Xb, T, Q2, len, 0);
     const int nr = XStage<QT, B, XF32, NW, kRS>::rounds(len);
     for (int r = 1; r < nr; ++r) {
       xs.template load<CHAIN>(a, c0w, len, r);
-      xs.template store<!MF>(Xb, T, Q2, len, r);
+      xs.template store<!MF && TSB != 0>(Xb, T, Q2, len, r);
     }
     if constexpr (MF) {
       const int z_base = len * MfmaLds<QT, B>::kPerCol;
       if (threadIdx.x < 32) *reinterpret_cast<u32x4*>(Xb + z_base + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
-      stage_T_mfma<QT, B, NW>(Xb, len, wid, lane);
+      if constexpr (QT != KQ_Q6_K) stage_T_mfma<QT, B, NW>(Xb, len, wid, lane);
     }
   }
   __syncthreads();
@@ -1077,7 +1080,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         float acc[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-        process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+        process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * TSB * B, acc);
 #pragma unroll
         for (int b = 0; b < B; ++b) S[(kb[k] * B + b) * kTileRows + lane] = acc[b];
       }
@@ -1101,9 +1104,9 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         for (int gb = 0; gb < NB; ++gb) ap[gb] = base + a_operand_offset<B>(lane, gb, ic, 0, z_base);
         process_unit_mfma<QT, B, CHAIN>(buf[k], d6[k], ap,
                                  reinterpret_cast<const float*>(base + t_base + ic * MfmaLds<QT, B>::kTCol),
-                                 acc, M, K);
+                                 acc);
       } else {
-        process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * SB * B, acc, M, K);
+        process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * TSB * B, acc);
       }
       if (c == cs + cw - 1 || u + 1 == u1) {
         float* pw = P + ((wid * a.tpw + (t - t0)) * B) * kTileRows;

@@ -89,8 +89,8 @@ hipError_t launch_gemv_type(int xtype, int rows, int nw, bool mf, const GemvArgs
 
 // The dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols` columns
 // needs on the chosen path: per column the activations of every batch row and
-// their sub-block sums (matrix cores: rows padded to 528 bytes, then a 512-byte
-// zero block), plus each wavefront's partial sums of the tiles its run touches
+// (Q4_K/Q5_K) their sub-block sums (matrix cores: rows padded to 528 bytes,
+// then a 512-byte zero block), plus each wavefront's partial sums of the tiles its run touches
 // (dynamic workgroups: a counter and one slot per unit).
 // Workgroups whose wavefronts take units dynamically (see gemv_block).
 template <int B, int NW, bool MF>
@@ -106,7 +106,7 @@ inline size_t gemv_lds_bytes(int type, int rows, int nw, bool mf, int staged_col
   const size_t partials = (dyn_units(rows, nw, mf) ? 16 + (size_t)run_units * rows * 64 * sizeof(float)
                                                    : (size_t)nw * tpw * rows * 64 * sizeof(float)) +
                           (norm ? (size_t)((staged_cols * rows + 3) & ~3) * sizeof(float) : 0);
-  const int sb = type == KQ_Q6_K ? 16 : 8;
+  const int sb = type == KQ_Q6_K ? 0 : 8;   // staged sub-block activation sums per column (Q6_K has no mins)
   if (mf) {
     const int nb = (rows + 3) / 4;
     return (size_t)staged_cols * (rows * 528 + sb * nb * 16) + 512 + partials;

@@ -28,6 +28,8 @@ template <> struct Repack<KQ_Q4_K> {
     const uint32_t b = byte_at(W, qs_off + 32 * c + (r % 32));
     return (r < 32) ? (b & 15u) : (b >> 4);
   }
+  // word j of sub-block g: element 32g + 8j + k (k < 4) in the low nibble of
+  // byte k, element 32g + 8j + 4 + k in its high nibble
   template <int N> static __device__ __forceinline__ void quant_chunks(const uint32_t (&W)[N], int qs_off, u32x4* ch) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -36,9 +38,9 @@ template <> struct Repack<KQ_Q4_K> {
       for (int j = 0; j < 4; ++j) {
         uint32_t o = 0;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          o |= nib(W, qs_off, 32 * g + 8 * j + 2 * p) << (4 * p);
-          o |= nib(W, qs_off, 32 * g + 8 * j + 2 * p + 1) << (16 + 4 * p);
+        for (int k = 0; k < 4; ++k) {
+          o |= nib(W, qs_off, 32 * g + 8 * j + k) << (8 * k);
+          o |= nib(W, qs_off, 32 * g + 8 * j + 4 + k) << (8 * k + 4);
         }
         v[j] = o;
       }
@@ -65,17 +67,18 @@ template <> struct Repack<KQ_Q5_K> {
     for (int i = 0; i < kWords; ++i) W[i] = p[i];
     ch[0] = u32x4{W[0], W[1], W[2], W[3]};
     Repack<KQ_Q4_K>::quant_chunks(W, 48, ch);
+    // fifth bit of element 32g + 8j + 4h + k at bit 8k + (2j + h) of H_g
     uint32_t H[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       uint32_t o = 0;
 #pragma unroll
-      for (int pi = 0; pi < 16; ++pi) {
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int e = 32 * g + 2 * pi + s;          // = 32g + 8j + 2p + s with pi = 4j + p
-          const uint32_t bit = (byte_at(W, 16 + e % 32) >> g) & 1u;
-          o |= bit << (pi + 16 * s);
+        for (int k = 0; k < 4; ++k) {
+          const int i = 8 * (t / 2) + 4 * (t % 2) + k;   // element 32g + i
+          const uint32_t bit = (byte_at(W, 16 + i) >> g) & 1u;
+          o |= bit << (8 * k + t);
         }
       }
       H[g] = o;
@@ -105,6 +108,8 @@ template <> struct Repack<KQ_Q6_K> {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(sb);
 #pragma unroll
     for (int i = 0; i < kHalves; ++i) U[i] = p[i];
+    // element 16g + 8j + 4h + k: low nibble at bits 8k + 4h of L[g][j]; its two
+    // high bits, the top one inverted, at bits 8k + 2m (m = 2j + h) of H[g]
     uint32_t L[16][2], H[16];
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
@@ -113,12 +118,12 @@ template <> struct Repack<KQ_Q6_K> {
       for (int j = 0; j < 2; ++j) {
         uint32_t o = 0;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int e = 16 * g + 8 * j + 2 * pp + s;
-            o |= lo(U, e) << (4 * pp + 16 * s);
-            h |= hi(U, e) << (2 * (4 * j + pp) + 16 * s);
+          for (int k = 0; k < 4; ++k) {
+            const int e = 16 * g + 8 * j + 4 * hh + k;
+            o |= lo(U, e) << (8 * k + 4 * hh);
+            h |= (hi(U, e) ^ 2u) << (8 * k + 2 * (2 * j + hh));
           }
         }
         L[g][j] = o;
@@ -176,7 +181,7 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint8_t* __restrict__
 // fp32 dequantisation of one super-block (row 64t + lane, column c) of the
 // repacked layout, whose unit starts at `tb`, into o[0..255].
 template <int QT>
-__device__ __forceinline__ void dequant_superblock(const uint8_t* tb, int lane, float* o, uint32_t M, uint32_t K) {
+__device__ __forceinline__ void dequant_superblock(const uint8_t* tb, int lane, float* o) {
   using F = Fmt<QT>;
   u32x4 ch[F::kChunks];
 #pragma unroll
@@ -185,20 +190,20 @@ __device__ __forceinline__ void dequant_superblock(const uint8_t* tb, int lane, 
   uint32_t d6 = 0;
   if constexpr (QT == KQ_Q6_K) d6 = reinterpret_cast<const uint16_t*>(tb + 13 * kChunkStride)[lane];
   float a[F::kSubBlocks], cm[F::kSubBlocks];
-  sb_coeffs<QT>(ch, d6, 1.0f, a, cm);
+  sb_coeffs<QT>(ch, d6, a, cm);
 #pragma unroll
   for (int g = 0; g < F::kSubBlocks; ++g) {
     uint32_t pr[F::kPairs];
-    unpack_pairs<QT>(ch, g, M, K, pr);
+    unpack_pairs<QT>(ch, g, pr);
 #pragma unroll
     for (int i = 0; i < F::kPairs; ++i) {
       const int e = g * F::kSubW + 2 * i;
-      if constexpr (QT == KQ_Q6_K) {
-        o[e] = a[g] * (bf16_lo(pr[i]) - 160.0f);
-        o[e + 1] = a[g] * (bf16_hi(pr[i]) - 160.0f);
-      } else {
-        o[e] = __builtin_fmaf(a[g], bf16_lo(pr[i]) - 128.0f, -cm[g]);
-        o[e + 1] = __builtin_fmaf(a[g], bf16_hi(pr[i]) - 128.0f, -cm[g]);
+      if constexpr (QT == KQ_Q6_K) {   // (d*sc/4) * 4(q-32): an exact product
+        o[e] = a[g] * bf16_lo(pr[i]);
+        o[e + 1] = a[g] * bf16_hi(pr[i]);
+      } else {                         // one rounding of d*sc*q - dmin*m
+        o[e] = __builtin_fmaf(a[g], bf16_lo(pr[i]), -cm[g]);
+        o[e + 1] = __builtin_fmaf(a[g], bf16_hi(pr[i]), -cm[g]);
       }
     }
   }
@@ -209,7 +214,6 @@ __device__ __forceinline__ void dequant_superblock(const uint8_t* tb, int lane, 
 template <int QT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out,
                                                       int64_t rows, int n_cols, int64_t total, int64_t ldo) {
-  const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
   for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
     const int lane = (int)(gid & 63);
     const int64_t unit = gid >> 6;
@@ -217,7 +221,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
     const int c = (int)(unit - t * n_cols);
     const int64_t row = t * kTileRows + lane;
     if (row >= rows) continue;
-    dequant_superblock<QT>(w + unit * tile_bytes<QT>(), lane, out + row * ldo + (int64_t)c * 256, M, K);
+    dequant_superblock<QT>(w + unit * tile_bytes<QT>(), lane, out + row * ldo + (int64_t)c * 256);
   }
 }
 
@@ -229,7 +233,6 @@ template <int QT>
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ w, const int32_t* __restrict__ ids,
                                                      float* __restrict__ out, int64_t rows, int n_cols, int64_t total,
                                                      int64_t ldo) {
-  const uint32_t M = in_vgpr(0x000F000Fu), K = in_vgpr(0x43004300u);
   for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
     const int64_t i = gid / n_cols;
     const int c = (int)(gid - i * n_cols);
@@ -240,7 +243,7 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
       continue;
     }
     const int64_t t = row / kTileRows;
-    dequant_superblock<QT>(w + (t * n_cols + c) * tile_bytes<QT>(), (int)(row - t * kTileRows), o, M, K);
+    dequant_superblock<QT>(w + (t * n_cols + c) * tile_bytes<QT>(), (int)(row - t * kTileRows), o);
   }
 }
 
