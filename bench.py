@@ -105,10 +105,15 @@ class Sweep:
             self.y[B] = [[torch.empty((B, r), dtype=torch.float32, device=dev) for r in parts]
                          for _, _, _, parts in self.entries]
         self._keep = []
+        # one workspace for every call of the sweep: they all run in order on one stream (eager or replayed)
+        self.work = torch.empty(kq.KQ_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+        kq.kq_workspace_init(self.work)
+        torch.cuda.synchronize()
 
     def calls(self, B: int, stream: int):
         """Pre-marshalled C-ABI calls of one step (minimal Python work per launch)."""
         L = self.kq.lib()
+        wsp, wsb = self.work.data_ptr(), self.work.numel()
         out = []
         for i, (layer, spec, reps, parts) in enumerate(self.entries):
             x, ys = self.x[B][i], self.y[B][i]
@@ -120,12 +125,12 @@ class Sweep:
                 Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
                 LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
                 self._keep += [W, R, Y, LD]
-                out.append((L.kq_gemv_multi, (t, n, W, R, spec.cols, x.data_ptr(), 1, x.stride(0), B, Y, LD, stream),
-                            spec.name))
+                out.append((L.kq_gemv_multi, (t, n, W, R, spec.cols, x.data_ptr(), 1, x.stride(0), B, Y, LD, wsp, wsb,
+                                               stream), spec.name))
             else:
                 fn = getattr(L, {"q4k": "kq_gemv_q4k", "q5k": "kq_gemv_q5k", "q6k": "kq_gemv_q6k"}[spec.qtype])
                 out.append((fn, (reps[0].data_ptr(), spec.rows, spec.cols, x.data_ptr(), 1, x.stride(0), B,
-                                 ys[0].data_ptr(), ys[0].stride(0), stream), spec.name))
+                                 ys[0].data_ptr(), ys[0].stride(0), wsp, wsb, stream), spec.name))
         return out
 
 

@@ -45,12 +45,20 @@
  *     a non-zero KQ_ERR_* code and enqueues nothing.  A failed launch returns
  *     KQ_ERR_HIP.  No C++ exception crosses the boundary.
  *   - `cols` (K) must be a positive multiple of 256; `rows` (M) >= 1.
- *   - GEMV calls on one device share a library-owned scratch area (about 69 MiB:
- *     partial sums of K-split row tiles, the sums of squares of head-norm heads,
- *     arrival counters); calls that overlap in time on one device (different
- *     streams without ordering) race on it.  kq_init allocates it; otherwise the
- *     first GEMV call on a device does (so that first call must not be made
- *     inside a stream capture).
+ *   - The library allocates no memory on any GEMV call path and keeps no
+ *     mutable global state.  GEMV calls whose outputs are split across
+ *     workgroups need device scratch (partial sums of K-split row tiles,
+ *     arrival counters, the heads' sums of squares of a head-norm epilogue):
+ *     the CALLER passes it as a workspace, `ws` (device, 16-byte aligned) of
+ *     `ws_bytes` bytes.  KQ_WORKSPACE_BYTES is enough for any call;
+ *     kq_gemv_workspace_bytes gives the exact need of one call.  Its first
+ *     64 KiB are counters that must be zero before the first use
+ *     (kq_workspace_init) and that every call leaves zero again.  One
+ *     workspace serves any number of calls ordered on one stream; calls that
+ *     may overlap in time (unordered streams, threads) need distinct
+ *     workspaces, exactly as they need distinct outputs.  A NULL, misaligned
+ *     or too small workspace returns KQ_ERR_WORKSPACE and enqueues nothing.
+ *     Every call is then thread-safe and may be captured in a HIP graph.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -62,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 1
+#define KQ_ABI_VERSION 2
 
 /* weight formats */
 #define KQ_Q4_K 1
@@ -107,6 +115,11 @@ extern "C" {
 #define KQ_ERR_RANGE 8  /* problem too large for 32-bit tile indexing */
 #define KQ_ERR_TIMEOUT 9 /* a chain step's wait for the previous step gave up (kq_chain_status) */
 #define KQ_ERR_DEVICE 10 /* a chain was run with another device current than the one it was made on */
+#define KQ_ERR_WORKSPACE 11 /* workspace NULL, not 16-byte aligned, or smaller than the call needs */
+
+/* Workspace bytes that suffice for any GEMV call (69 MiB; most calls need far
+ * less, see kq_gemv_workspace_bytes). */
+#define KQ_WORKSPACE_BYTES 72417280u
 
 /* Version of this ABI (KQ_ABI_VERSION). */
 int kq_abi_version(void);
@@ -115,10 +128,26 @@ int kq_abi_version(void);
 const char *kq_status_str(int status);
 
 /*
- * Allocate this library's per-device scratch on `device` (the HIP ordinal).
- * Optional: GEMV calls allocate it on first use.  Returns KQ_OK if present.
+ * Check that `device` (the HIP ordinal) exists and can be queried.  Allocates
+ * nothing.  Returns KQ_OK, else KQ_ERR_DEVICE / KQ_ERR_HIP.
  */
 int kq_init(int device);
+
+/*
+ * Exact workspace bytes of one GEMV call with these shapes and options on the
+ * current device (the launch geometry depends on its CU count), as
+ * kq_gemv_fused takes them: epi may be NULL, rms_eps as there.  0 if the
+ * arguments are invalid.  Host-only query; allocates nothing.
+ */
+size_t kq_gemv_workspace_bytes(int type, int n, const int64_t *rows, int64_t cols, int xtype, int batch,
+                               const int32_t *epi, float rms_eps);
+
+/*
+ * Prepare a workspace for its first use: zero its counter block (the first
+ * 64 KiB) with a kernel on `stream` (no memset node, so it may be captured).
+ * bytes >= 64 KiB and ws 16-byte aligned, else KQ_ERR_WORKSPACE.
+ */
+int kq_workspace_init(void *ws, size_t bytes, void *stream);
 
 /*
  * Size in bytes of the repacked form of a rows x cols matrix of `type`, or 0 if
@@ -151,14 +180,15 @@ int kq_repack(int type, int64_t rows, int64_t cols, const void *gguf, void *out,
  *   x    : fp32 or bf16 activations, batch rows of stride ldx elements; 16-byte
  *          aligned and ldx * element size a multiple of 16.
  *   y    : fp32 output, batch rows of stride ldy >= rows; 4-byte aligned.
+ *   ws, ws_bytes : the caller's workspace (see the conventions above).
  * Deterministic: the same inputs give bitwise the same y on every run.
  */
 int kq_gemv_q4k(const void *w, int64_t rows, int64_t cols, const void *x, int xtype, int64_t ldx, int batch,
-                float *y, int64_t ldy, void *stream);
+                float *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 int kq_gemv_q5k(const void *w, int64_t rows, int64_t cols, const void *x, int xtype, int64_t ldx, int batch,
-                float *y, int64_t ldy, void *stream);
+                float *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 int kq_gemv_q6k(const void *w, int64_t rows, int64_t cols, const void *x, int xtype, int64_t ldx, int batch,
-                float *y, int64_t ldy, void *stream);
+                float *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * n projections of one type that read the same x (QKV, gate+up), in ONE launch:
@@ -167,7 +197,8 @@ int kq_gemv_q6k(const void *w, int64_t rows, int64_t cols, const void *x, int xt
  * Same per-matrix rules as kq_gemv_q4k.  1 <= n <= KQ_MAX_PROJ.
  */
 int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
-                  int64_t ldx, int batch, float *const *y, const int64_t *ldy, void *stream);
+                  int64_t ldx, int batch, float *const *y, const int64_t *ldy, void *ws, size_t ws_bytes,
+                  void *stream);
 
 /*
  * out[r*ldo + k] = dequant(W)[r, k] as fp32 (the single correctly rounded value
@@ -216,7 +247,7 @@ int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, 
  */
 int kq_gemv_fused(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
                   int64_t ldx, int batch, float *const *y, const int64_t *ldy, void *const *y16, const int64_t *ldy16,
-                  const int32_t *epi, float rms_eps, float head_eps, void *stream);
+                  const int32_t *epi, float rms_eps, float head_eps, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * SwiGLU epilogue: the gate and up projections of the feed-forward block in one
@@ -238,7 +269,7 @@ int kq_gemv_fused(int type, int n, const void *const *w, const int64_t *rows, in
 int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void *gate, const void *up, void *out,
                      void *stream);
 int kq_gemv_swiglu(int type, const void *w, int64_t inter, int64_t cols, const void *x, int xtype, int64_t ldx,
-                   int batch, float *y, int64_t ldy, void *stream);
+                   int batch, float *y, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Row gather: the embedding lookup of a token, the step before layer 0 of a
@@ -301,9 +332,10 @@ typedef struct kq_chain kq_chain;
 /*
  * Plan a chain of n_steps (1..65536) steps on the current device: validates
  * every step as kq_gemv_multi would, sizes the persistent grid from the
- * kernel's occupancy, and allocates the chain's device memory (partial sums
- * and head-norm sums, about 69 MiB, plus about 2.5 KB per step for the step
- * table and the step barrier's words).  Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
+ * kernel's occupancy, and allocates the chain's device memory (the step table,
+ * the step barrier's words, about 2.5 KB per step, and one workspace of the
+ * largest step's size) and one pinned host word for its time-out flag.
+ * Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
  * Every x must also satisfy ((batch-1)*ldx + cols) * element size < 2^31.
  * On success *out owns the plan; release it with kq_chain_destroy.
  */
@@ -312,15 +344,32 @@ int kq_chain_create(int n_steps, const kq_chain_step *steps, int xtype, int batc
 /*
  * Enqueue one run of the chain on `stream` (one kernel launch, no allocation;
  * may be captured in a HIP graph).  Runs of one chain must not overlap in time
- * (they share its control words); different chains are independent.  The
- * device current at the call must be the chain's (else KQ_ERR_DEVICE).
+ * (they share its control words and workspace); different chains are
+ * independent.  The device current at the call must be the chain's (else
+ * KQ_ERR_DEVICE).
+ *
+ * Time-outs: every wait of a step for the previous one is bounded (about a
+ * second; the environment variable KQ_CHAIN_SPIN, read at each run, sets the
+ * poll limit).  When one gives up, the run's results are invalid: the device
+ * sets the chain's error word and a pinned host word, the rest of the run's
+ * waits give up at once, and any later run of the chain does nothing until
+ * kq_chain_status has reset it.  kq_chain_run itself returns KQ_ERR_TIMEOUT,
+ * enqueuing nothing, once the host word is set (no device synchronisation).
  */
 int kq_chain_run(kq_chain *c, void *stream);
 
 /*
+ * Non-synchronising: KQ_ERR_TIMEOUT if a run's wait has given up since the
+ * last reset (as far as the device has progressed), else KQ_OK.
+ */
+int kq_chain_query(kq_chain *c);
+
+/*
  * Synchronous: waits for the device, then returns KQ_ERR_TIMEOUT if a step's
- * wait in any run since the last call gave up (its results are then invalid;
- * a wait gives up after about a second), else KQ_OK; clears the flag.
+ * wait in any run since the last call gave up, else KQ_OK.  In the first case
+ * it also resets the chain (its split-tile and head counters, which a
+ * workgroup that stopped waiting may have left non-zero, and both error
+ * words), so the next run is valid again.
  */
 int kq_chain_status(kq_chain *c);
 

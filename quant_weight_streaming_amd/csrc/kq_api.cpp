@@ -26,58 +26,13 @@ int64_t sb_bytes(int type) {
 }
 
 
-// Scratch for row tiles whose columns span several workgroups: two partial-sum
-// slots and one arrival counter per workgroup.  The counters are zero between
-// calls (the last arrival of a tile resets its counter), so they are cleared
-// once, at allocation.
-constexpr int kMaxGroups = 8192;
-// then the per-head sums of squares of KQ_EPI_HEADNORM launches ([tile][2][KQ_MAX_BATCH]),
-// and after the tile counters one counter per head
-constexpr size_t kPartialFloats = (size_t)kMaxGroups * 2 * kPartialStride;
-constexpr size_t kHeadSsFloats = (size_t)kMaxGroups * 2 * KQ_MAX_BATCH;
-constexpr size_t kPartialBytes = (kPartialFloats + kHeadSsFloats) * sizeof(float);
-constexpr size_t kCounterBytes = (size_t)2 * kMaxGroups * sizeof(uint32_t);
-static_assert(kHeadRows == 2 * 64, "a head is two row tiles");
-constexpr int kMaxDevices = 64;
-
-struct DeviceState {
-  bool ready = false;
-  int cus = 0;
-  float* partial = nullptr;
-  uint32_t* counters = nullptr;
-};
-
-static std::mutex g_mu;
-static DeviceState g_dev[kMaxDevices];
-
-static int device_state(int dev, DeviceState** out) {
-  if (dev < 0 || dev >= kMaxDevices) return KQ_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceState& s = g_dev[dev];
-  if (!s.ready) {
-    int prev = 0;
-    if (hipGetDevice(&prev) != hipSuccess) return KQ_ERR_HIP;
-    if (hipSetDevice(dev) != hipSuccess) return KQ_ERR_HIP;
-    int rc = KQ_OK;
-    void* p = nullptr;
-    void* c = nullptr;
-    if (hipDeviceGetAttribute(&s.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) rc = KQ_ERR_HIP;
-    if (rc == KQ_OK && hipMalloc(&p, kPartialBytes) != hipSuccess) rc = KQ_ERR_NOMEM;
-    if (rc == KQ_OK && hipMalloc(&c, kCounterBytes) != hipSuccess) rc = KQ_ERR_NOMEM;
-    if (rc == KQ_OK && hipMemset(c, 0, kCounterBytes) != hipSuccess) rc = KQ_ERR_HIP;
-    if (rc == KQ_OK && hipDeviceSynchronize() != hipSuccess) rc = KQ_ERR_HIP;
-    if (rc != KQ_OK) {
-      if (p) (void)hipFree(p);
-      if (c) (void)hipFree(c);
-      (void)hipSetDevice(prev);
-      return rc;
-    }
-    s.partial = static_cast<float*>(p);
-    s.counters = static_cast<uint32_t*>(c);
-    s.ready = true;
-    (void)hipSetDevice(prev);
-  }
-  *out = &s;
+// CUs of the current device (the launch geometry is planned for them).
+static int current_device_cus(int* dev_out, int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || *cus < 1)
+    return KQ_ERR_HIP;
+  if (dev_out) *dev_out = dev;
   return KQ_OK;
 }
 
@@ -184,12 +139,26 @@ static int validate(int type, int n, const void* const* w, const int64_t* rows, 
 // Launch plan of one GEMV (or multi-projection) call.
 struct Plan {
   GemvArgs a;
-  int nw;        // wavefronts per workgroup
-  bool mf;       // matrix-core path
-  int64_t grid;  // workgroups, a multiple of 8
-  size_t lds;    // dynamic LDS per workgroup
-  int rows;      // staged activation rows: the batch, or twice it for fp32 activations
+  int nw;            // wavefronts per workgroup
+  bool mf;           // matrix-core path
+  int64_t grid;      // workgroups, a multiple of 8
+  size_t lds;        // dynamic LDS per workgroup
+  int rows;          // staged activation rows: the batch, or twice it for fp32 activations
+  int64_t slots;     // partial-sum slots of split tiles
+  int slot_floats;   // floats per slot
+  bool heads;        // a head-norm segment: the heads' sums of squares follow the slots
+  size_t ws_bytes;   // workspace the call needs
 };
+
+// Point the plan's workspace arguments into `ws` (layout in kq_internal.h).
+static void assign_workspace(Plan& p, uint8_t* ws) {
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+  float* partial = reinterpret_cast<float*>(ws + kCounterBytes);
+  p.a.counters = counters;
+  p.a.head_ctr = counters + kMaxGroups;
+  p.a.partial = partial;
+  p.a.head_ss = partial + p.slots * p.slot_floats;
+}
 
 // Launch geometry of a validated call on a device with `cus` CUs, using at most
 // `max_grid` workgroups (a multiple of 8).
@@ -200,7 +169,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* const* y16,
                      const int64_t* ldy16, int cus,
                      int64_t max_grid, int force_nw, bool single, uint32_t epi, float rms_eps, float head_eps,
-                     float* partial, uint32_t* counters, Plan* out) {
+                     Plan* out) {
   const int64_t n_cols = cols / 256;
   const bool norm = rms_eps > 0.0f;
   GemvArgs a{};
@@ -305,10 +274,6 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   a.n_units = (int32_t)n_units;
   a.upw = (int32_t)upw;
   a.tsb = (int32_t)tcols;
-  a.partial = partial;
-  a.counters = counters;
-  a.head_ss = partial ? partial + kPartialFloats : nullptr;
-  a.head_ctr = counters ? counters + kMaxGroups : nullptr;
   out->a = a;
   out->nw = nw;
   out->mf = mf;
@@ -326,6 +291,13 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   out->lds = gemv_lds_bytes(type, srows, nw, mf, (int)tcols, (int)run_units, a.tpw, norm);
   out->rows = srows;
   if (out->lds > kMaxLds) return KQ_ERR_RANGE;
+  // workspace: the counter block, one slot per (workgroup, 0/1) of even runs or per (window, tile), and
+  // the heads' sums of squares
+  out->slots = a.tiles_per_wg > 0 ? (int64_t)a.n_win * a.n_tiles : 2 * grid;
+  out->slot_floats = partial_stride(batch);
+  out->heads = heads;
+  out->ws_bytes = kCounterBytes + (size_t)out->slots * out->slot_floats * sizeof(float) +
+                  (heads ? (size_t)tiles * 2 * KQ_MAX_BATCH * sizeof(float) : 0);
   return KQ_OK;
 }
 
@@ -372,35 +344,50 @@ static int check_y16(int n, const int64_t* rows, void* const* y16, const int64_t
 // The weight-less RMSNorm's epsilon: 0 (no normalisation) or finite and > 0.
 static bool valid_rms_eps(float e) { return e == 0.0f || (e > 0.0f && e <= FLT_MAX); }
 
-static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
-                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream,
-                     uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f, float head_eps = 0.0f,
-                     void* const* y16 = nullptr, const int64_t* ldy16 = nullptr) {
+// Host-side checks of one call's arguments (every GEMV entry point).
+static int validate_call(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                         int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, uint32_t epi,
+                         float rms_eps, float head_eps, void* const* y16, const int64_t* ldy16) {
   int rc = validate(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy);
   if (rc != KQ_OK) return rc;
   rc = check_y16(n, rows, y16, ldy16);
   if (rc != KQ_OK) return rc;
   if (!valid_epilogue(n, epi)) return KQ_ERR_TYPE;
   if (!valid_rms_eps(rms_eps)) return KQ_ERR_SHAPE;
-  rc = check_heads(n, rows, epi, head_eps);
+  return check_heads(n, rows, epi, head_eps);
+}
+
+// Validate one call and plan it for the current device (every GEMV entry point
+// and the workspace query).
+static int plan_call(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, uint32_t epi,
+                     float rms_eps, float head_eps, void* const* y16, const int64_t* ldy16, Plan* p) {
+  int rc = validate_call(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, epi, rms_eps, head_eps, y16, ldy16);
   if (rc != KQ_OK) return rc;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
-  DeviceState* st = nullptr;
-  rc = device_state(dev, &st);
+  int cus = 0;
+  rc = current_device_cus(nullptr, &cus);
   if (rc != KQ_OK) return rc;
+  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, cus, kMaxGroups, 0, true, epi,
+                 rms_eps, head_eps, p);
+  // too many units per 8-wavefront workgroup: 4-wavefront runs
+  if (rc == KQ_ERR_RANGE && wg_waves(xtype == KQ_X_F32 ? 2 * batch : batch) == 8)
+    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, cus, kMaxGroups, 4, true, epi,
+                   rms_eps, head_eps, p);
+  return rc;
+}
+
+static int gemv_impl(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                     int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* ws,
+                     size_t ws_bytes, void* stream, uint32_t epi = KQ_EPI_NONE, float rms_eps = 0.0f,
+                     float head_eps = 0.0f, void* const* y16 = nullptr, const int64_t* ldy16 = nullptr) {
+  int rc = validate_call(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, epi, rms_eps, head_eps, y16, ldy16);
+  if (rc != KQ_OK) return rc;
+  if (!ws || !aligned(ws, 16)) return KQ_ERR_WORKSPACE;
   Plan p{};
-  rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 0, true, epi,
-                 rms_eps, head_eps,
-                 st->partial,
-                 st->counters, &p);
-  if (rc == KQ_ERR_RANGE && wg_waves(xtype == KQ_X_F32 ? 2 * batch : batch) == 8)   // too many units per
-                                                                                        // workgroup: 4-wave runs
-    rc = plan_gemv(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, y16, ldy16, st->cus, kMaxGroups, 4, true, epi,
-                   rms_eps, head_eps,
-                   st->partial,
-                   st->counters, &p);
+  rc = plan_call(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, epi, rms_eps, head_eps, y16, ldy16, &p);
   if (rc != KQ_OK) return rc;
+  if (ws_bytes < p.ws_bytes) return KQ_ERR_WORKSPACE;
+  assign_workspace(p, static_cast<uint8_t*>(ws));
   if (launch_gemv(type, xtype, p.rows, p.nw, p.mf, p.a, (int)p.grid, p.lds, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return KQ_ERR_HIP;
@@ -468,7 +455,9 @@ struct kq_chain {
   int grid = 0;
   size_t lds = 0;
   kq::ChainArgs args{};
-  void* mem = nullptr;   // one allocation: step table, control words, partial sums, tile counters
+  void* mem = nullptr;          // one allocation: step table, control words, the steps' workspace
+  uint32_t* counters = nullptr; // the workspace's counter block (reset after a run whose wait gave up)
+  uint32_t* flag = nullptr;     // pinned host word, set by the device when a wait gives up
 };
 
 using namespace kq;
@@ -490,13 +479,52 @@ const char* kq_status_str(int status) {
     case KQ_ERR_RANGE: return "problem too large";
     case KQ_ERR_TIMEOUT: return "a chain step's wait for the previous step gave up";
     case KQ_ERR_DEVICE: return "chain run on another device than the one it was made on";
+    case KQ_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than the call needs";
     default: return "unknown status";
   }
 }
 
 int kq_init(int device) {
-  DeviceState* st = nullptr;
-  return device_state(device, &st);
+  int n = 0, cus = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return KQ_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
+size_t kq_gemv_workspace_bytes(int type, int n, const int64_t* rows, int64_t cols, int xtype, int batch,
+                               const int32_t* epi, float rms_eps) {
+  if (n < 1 || n > KQ_MAX_PROJ || !rows) return 0;
+  // the plan depends on shapes and options only; stand-in pointers pass validation
+  const void* w[KQ_MAX_PROJ];
+  float* y[KQ_MAX_PROJ];
+  int64_t ldy[KQ_MAX_PROJ];
+  for (int i = 0; i < n; ++i) {
+    w[i] = reinterpret_cast<const void*>((uintptr_t)256);
+    y[i] = reinterpret_cast<float*>((uintptr_t)256);
+    ldy[i] = rows[i];
+  }
+  uint32_t packed = 0;
+  if (epi) {
+    if (n == 1 && epi[0] == KQ_EPI_SWIGLU) packed = KQ_EPI_SWIGLU;
+    else
+      for (int i = 0; i < n; ++i) packed |= ((uint32_t)epi[i] & 15u) << (4 * i);
+  }
+  Plan p{};
+  // head-norm segments need a valid epsilon to plan; its value does not change the plan
+  if (plan_call(type, n, w, rows, cols, reinterpret_cast<const void*>((uintptr_t)256), xtype, cols, batch, y, ldy,
+                packed, rms_eps, 1.0f, nullptr, nullptr, &p) != KQ_OK)
+    return 0;
+  return p.ws_bytes;
+}
+
+int kq_workspace_init(void* ws, size_t bytes, void* stream) {
+  if (!ws) return KQ_ERR_NULL;
+  if (!aligned(ws, 16) || bytes < kCounterBytes) return KQ_ERR_WORKSPACE;
+  if (launch_zero_words(static_cast<uint32_t*>(ws), kCounterBytes / 4, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
 }
 
 size_t kq_repacked_bytes(int type, int64_t rows, int64_t cols) {
@@ -532,7 +560,7 @@ int kq_repack_swiglu(int type, int64_t inter, int64_t cols, const void* gate, co
 
 int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x, int xtype,
                   int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* const* y16, const int64_t* ldy16,
-                  const int32_t* epi, float rms_eps, float head_eps, void* stream) {
+                  const int32_t* epi, float rms_eps, float head_eps, void* ws, size_t ws_bytes, void* stream) {
   if (n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
   uint32_t packed = 0;
   if (epi) {
@@ -546,33 +574,35 @@ int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, in
       }
     }
   }
-  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream, packed, rms_eps, head_eps, y16, ldy16);
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, ws, ws_bytes, stream, packed, rms_eps,
+                   head_eps, y16, ldy16);
 }
 
 int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,
-                   int batch, float* y, int64_t ldy, void* stream) {
+                   int batch, float* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   if (inter > (int64_t)INT32_MAX / 2 - 64) return KQ_ERR_RANGE;
-  return gemv_impl(type, 1, &w, &inter, cols, x, xtype, ldx, batch, &y, &ldy, stream, KQ_EPI_SWIGLU);
+  return gemv_impl(type, 1, &w, &inter, cols, x, xtype, ldx, batch, &y, &ldy, ws, ws_bytes, stream, KQ_EPI_SWIGLU);
 }
 
 int kq_gemv_q4k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
-                float* y, int64_t ldy, void* stream) {
-  return gemv_impl(KQ_Q4_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, stream);
+                float* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return gemv_impl(KQ_Q4_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, ws, ws_bytes, stream);
 }
 
 int kq_gemv_q5k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
-                float* y, int64_t ldy, void* stream) {
-  return gemv_impl(KQ_Q5_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, stream);
+                float* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return gemv_impl(KQ_Q5_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, ws, ws_bytes, stream);
 }
 
 int kq_gemv_q6k(const void* w, int64_t rows, int64_t cols, const void* x, int xtype, int64_t ldx, int batch,
-                float* y, int64_t ldy, void* stream) {
-  return gemv_impl(KQ_Q6_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, stream);
+                float* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return gemv_impl(KQ_Q6_K, 1, &w, &rows, cols, x, xtype, ldx, batch, &y, &ldy, ws, ws_bytes, stream);
 }
 
 int kq_gemv_multi(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x, int xtype,
-                  int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* stream) {
-  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, stream);
+                  int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* ws, size_t ws_bytes,
+                  void* stream) {
+  return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, ws, ws_bytes, stream);
 }
 
 int kq_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo, void* stream) {
@@ -622,11 +652,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     if (yrc != KQ_OK) return yrc;
     if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return KQ_ERR_HIP;
+  int dev = 0, cus = 0;
+  if (current_device_cus(&dev, &cus) != KQ_OK) return KQ_ERR_HIP;
 
   // Persistent grid: the designed workgroups per CU (two of 4 wavefronts, one
   // of 8), fewer if the occupancy of the chain kernel says so.
@@ -641,7 +668,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
       const kq_chain_step& st = steps[j];
       int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, st.y16,
                          st.ldy16, cus,
-                         max_grid, nw, false, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, nullptr, nullptr, &plans[j]);
+                         max_grid, nw, false, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && srows <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;
@@ -675,33 +702,42 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   const size_t steps_bytes = round_up((size_t)n_steps * sizeof(ChainStep), 256);
   // control words: arrive[n_steps][groups], done[n_steps], epoch, error
   const size_t ctl_bytes = round_up(((size_t)n_steps * (groups + 1) + 2) * sizeof(uint32_t), 256);
-  const size_t total = steps_bytes + ctl_bytes + kPartialBytes + kCounterBytes;
+  // the steps run one after another and share one workspace of the largest step's size
+  size_t ws_bytes = kCounterBytes;
+  for (int j = 0; j < n_steps; ++j) ws_bytes = plans[j].ws_bytes > ws_bytes ? plans[j].ws_bytes : ws_bytes;
+  const size_t total = steps_bytes + ctl_bytes + ws_bytes;
   if (hipMalloc(&c->mem, total) != hipSuccess) {
     delete c;
     return KQ_ERR_NOMEM;
   }
+  if (hipHostMalloc(reinterpret_cast<void**>(&c->flag), sizeof(uint32_t),
+                    hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+    (void)hipFree(c->mem);
+    delete c;
+    return KQ_ERR_NOMEM;
+  }
+  *reinterpret_cast<volatile uint32_t*>(c->flag) = 0;
+  uint32_t* d_flag = nullptr;
   uint8_t* base = static_cast<uint8_t*>(c->mem);
   ChainStep* d_steps = reinterpret_cast<ChainStep*>(base);
   uint32_t* d_ctl = reinterpret_cast<uint32_t*>(base + steps_bytes);
-  float* d_partial = reinterpret_cast<float*>(base + steps_bytes + ctl_bytes);
-  uint32_t* d_counters = reinterpret_cast<uint32_t*>(base + steps_bytes + ctl_bytes + kPartialBytes);
+  uint8_t* d_ws = base + steps_bytes + ctl_bytes;
   std::vector<ChainStep> h(n_steps);
   for (int j = 0; j < n_steps; ++j) {
+    assign_workspace(plans[j], d_ws);
     h[j].a = plans[j].a;
-    h[j].a.partial = d_partial;
-    h[j].a.counters = d_counters;
-    h[j].a.head_ss = d_partial + kPartialFloats;
-    h[j].a.head_ctr = d_counters + kMaxGroups;
     h[j].type = steps[j].type;
     h[j].grid = (int32_t)plans[j].grid;
   }
   rc = KQ_OK;
-  if (hipMemcpy(d_steps, h.data(), (size_t)n_steps * sizeof(ChainStep), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_counters, 0, kCounterBytes) != hipSuccess ||
+  if (hipHostGetDevicePointer(reinterpret_cast<void**>(&d_flag), c->flag, 0) != hipSuccess ||
+      hipMemcpy(d_steps, h.data(), (size_t)n_steps * sizeof(ChainStep), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_ws, 0, kCounterBytes) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess)
     rc = KQ_ERR_HIP;
   if (rc != KQ_OK) {
     (void)hipFree(c->mem);
+    (void)hipHostFree(c->flag);
     delete c;
     return rc;
   }
@@ -712,10 +748,11 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   c->mf = plans[0].mf;
   c->grid = (int)groups;
   c->lds = lds;
+  c->counters = reinterpret_cast<uint32_t*>(d_ws);
   c->args.steps = d_steps;
   c->args.n_steps = n_steps;
   uint32_t* d_done = d_ctl + (size_t)n_steps * groups;
-  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_steps, d_done + n_steps + 1, (uint32_t)groups, chain_spin()};
+  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_steps, d_done + n_steps + 1, d_flag, (uint32_t)groups, 0};
   *out = c;
   return KQ_OK;
 }
@@ -725,10 +762,20 @@ int kq_chain_run(kq_chain* c, void* stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
   if (dev != c->dev) return KQ_ERR_DEVICE;
-  if (launch_chain(c->xtype, c->rows, c->args, c->nw, c->mf, c->grid, c->lds, static_cast<hipStream_t>(stream),
+  // an earlier run's wait gave up: its results were invalid and the chain's counters may be
+  // inconsistent; nothing runs until kq_chain_status has reset the chain
+  if (*reinterpret_cast<volatile uint32_t*>(c->flag)) return KQ_ERR_TIMEOUT;
+  ChainArgs args = c->args;
+  args.ctl.spin = chain_spin();
+  if (launch_chain(c->xtype, c->rows, args, c->nw, c->mf, c->grid, c->lds, static_cast<hipStream_t>(stream),
                    nullptr) != hipSuccess)
     return KQ_ERR_HIP;
   return KQ_OK;
+}
+
+int kq_chain_query(kq_chain* c) {
+  if (!c) return KQ_ERR_NULL;
+  return *reinterpret_cast<volatile uint32_t*>(c->flag) ? KQ_ERR_TIMEOUT : KQ_OK;
 }
 
 int kq_chain_status(kq_chain* c) {
@@ -740,10 +787,14 @@ int kq_chain_status(kq_chain* c) {
   if (hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(&err, c->args.ctl.error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
     rc = KQ_ERR_HIP;
-  if (rc == KQ_OK && err) {
-    rc = hipMemset(c->args.ctl.error, 0, sizeof(err)) == hipSuccess && hipDeviceSynchronize() == hipSuccess
+  if (rc == KQ_OK && (err || *reinterpret_cast<volatile uint32_t*>(c->flag))) {
+    // reset: the split-tile and head counters (a workgroup that stopped waiting may have entered a
+    // step early and left them non-zero), the device error word and the host flag
+    rc = hipMemset(c->counters, 0, kCounterBytes) == hipSuccess &&
+                 hipMemset(c->args.ctl.error, 0, sizeof(err)) == hipSuccess && hipDeviceSynchronize() == hipSuccess
              ? KQ_ERR_TIMEOUT
              : KQ_ERR_HIP;
+    *reinterpret_cast<volatile uint32_t*>(c->flag) = 0;
   }
   (void)hipSetDevice(prev);
   return rc;
@@ -753,7 +804,9 @@ int kq_chain_destroy(kq_chain* c) {
   if (!c) return KQ_OK;
   int prev = 0, rc = KQ_OK;
   if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(c->dev) != hipSuccess) rc = KQ_ERR_HIP;
-  if (rc == KQ_OK && (hipDeviceSynchronize() != hipSuccess || hipFree(c->mem) != hipSuccess)) rc = KQ_ERR_HIP;
+  if (rc == KQ_OK && (hipDeviceSynchronize() != hipSuccess || hipFree(c->mem) != hipSuccess ||
+                      hipHostFree(c->flag) != hipSuccess))
+    rc = KQ_ERR_HIP;
   (void)hipSetDevice(prev);
   delete c;
   return rc;

@@ -742,14 +742,14 @@ __device__ __forceinline__ void rms_scale(const GA& a, float* v, const float* ss
   for (int b = 0; b < B; ++b) v[b] *= 1.0f / sqrtf(ss[b] / k + a.rms_eps);
 }
 
-// A piece's sums of x^2 go to the slot's words kPartialQ + b, lane b < B.
+// A piece's sums of x^2 go to the slot's words partial_q(B) + b, lane b < B.
 template <int B>
 __device__ __forceinline__ void publish_q(float* slot, int lane, const float* q) {
   float mine = 0.0f;
 #pragma unroll
   for (int b = 0; b < B; ++b)
     if (lane == b) mine = q[b];
-  if (lane < B) __hip_atomic_store(slot + kPartialQ + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane < B) __hip_atomic_store(slot + partial_q(B) + lane, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroup L holds its sum for tile t, whose columns other workgroups share.
@@ -764,7 +764,7 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
   const int n_cols = a.n_cols;
   const bool norm = a.rms_eps > 0.0f;
   const int slot = (t == (L * wgu) / n_cols) ? 0 : 1;
-  float* mine = a.partial + (int64_t)(L * 2 + slot) * kPartialStride;
+  float* mine = a.partial + (int64_t)(L * 2 + slot) * partial_stride(B);
 #pragma unroll
   for (int b = 0; b < B; ++b)
     __hip_atomic_store(mine + b * kTileRows + lane, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -789,13 +789,13 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
     for (int j = 0; j < PR; ++j) {
       const int l = l0 + j;
       const int sl = (t == (l * wgu) / n_cols) ? 0 : 1;
-      const float* pp = a.partial + (int64_t)(l * 2 + sl) * kPartialStride;
+      const float* pp = a.partial + (int64_t)(l * 2 + sl) * partial_stride(B);
 #pragma unroll
       for (int b = 0; b < B; ++b)
         v[j][b] = l <= lb ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                           : 0.0f;
       qv[j] = norm && l <= lb && lane < B
-                  ? __hip_atomic_load(pp + kPartialQ + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  ? __hip_atomic_load(pp + partial_q(B) + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                   : 0.0f;
     }
 #pragma unroll
@@ -822,7 +822,7 @@ __device__ __forceinline__ void hand_off(GA& a, int t, int L, int wgu, int lane,
 template <int B, bool COH, class GA>
 __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, const float* v, const float* q) {
   const bool norm = a.rms_eps > 0.0f;
-  float* mine = a.partial + (int64_t)(w * a.n_tiles + t) * kPartialStride;
+  float* mine = a.partial + (int64_t)(w * a.n_tiles + t) * partial_stride(B);
 #pragma unroll
   for (int b = 0; b < B; ++b)
     __hip_atomic_store(mine + b * kTileRows + lane, v[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -842,14 +842,14 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
     float pv[PR][B], qv[PR];
 #pragma unroll
     for (int j = 0; j < PR; ++j) {
-      const float* pp = a.partial + (int64_t)((w0 + j) * a.n_tiles + t) * kPartialStride;
+      const float* pp = a.partial + (int64_t)((w0 + j) * a.n_tiles + t) * partial_stride(B);
 #pragma unroll
       for (int b = 0; b < B; ++b)
         pv[j][b] = w0 + j < a.n_win
                        ? __hip_atomic_load(pp + b * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                        : 0.0f;
       qv[j] = norm && w0 + j < a.n_win && lane < B
-                  ? __hip_atomic_load(pp + kPartialQ + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  ? __hip_atomic_load(pp + partial_q(B) + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                   : 0.0f;
     }
 #pragma unroll
@@ -883,6 +883,14 @@ __device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A wait gave up: set the device error word (later waits of the run then give
+// up at once, and later runs do nothing) and the host-visible word that
+// kq_chain_run and kq_chain_query read without a device synchronisation.
+__device__ __forceinline__ void chain_fail(const ChainCtl& c) {
+  store_coherent(c.error, 1u);
+  __hip_atomic_store(c.error_host, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __device__ __forceinline__ void chain_collect(const ChainCtl& c, int step, uint32_t tag) {
   const uint32_t* arr = c.arrive + (size_t)step * c.groups;
   uint32_t n = 0;
@@ -891,11 +899,14 @@ __device__ __forceinline__ void chain_collect(const ChainCtl& c, int step, uint3
     int mine = 1;
     for (uint32_t g = threadIdx.x; g < c.groups; g += blockDim.x) mine &= load_coherent(arr + g) == tag;
     all = __syncthreads_and(mine);
-    if (all || ++n > c.spin) break;
+    if (all) break;
+    // bounded: give up after `spin` polls, or at once once another wait of the run has
+    const int quit = __syncthreads_or(threadIdx.x == 0 && (++n > c.spin || load_coherent(c.error) != 0u));
+    if (quit) break;
     __builtin_amdgcn_s_sleep(1);
   }
   if (threadIdx.x == 0) {
-    if (!all) store_coherent(c.error, 1u);
+    if (!all) chain_fail(c);
     store_coherent(c.done + step, tag);
   }
 }
@@ -909,8 +920,8 @@ __device__ __forceinline__ void chain_wait(const ChainCtl& c, int step, uint32_t
   } else if (threadIdx.x == 0) {
     uint32_t n = 0;
     while (load_coherent(c.done + step - 1) != tag) {
-      if (++n > c.spin) {
-        store_coherent(c.error, 1u);
+      if (++n > c.spin || load_coherent(c.error) != 0u) {
+        chain_fail(c);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -1242,6 +1253,11 @@ typedef const __attribute__((address_space(4))) ChainStep ConstChainStep;
 template <int B, bool XF32, bool MF, int NW>
 __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
   ConstChainStep* steps = (ConstChainStep*)(c.steps);
+  // a wait of an earlier run gave up (and the chain has not been reset): the
+  // counters may be inconsistent, so this run does nothing.  (A workgroup that
+  // starts after a wait of this same run gave up returns too; that run's
+  // results are invalid and reported either way.)
+  if (__builtin_amdgcn_readfirstlane(load_coherent(c.ctl.error)) != 0u) return;
   const uint32_t tag = __builtin_amdgcn_readfirstlane(load_coherent(c.ctl.epoch)) + 1u;
   for (int j = 0; j < c.n_steps; ++j) {
     ConstChainStep& st = steps[j];

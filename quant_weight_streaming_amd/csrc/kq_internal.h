@@ -9,12 +9,27 @@
 namespace kq {
 
 
-// Kernel arguments of one GEMV launch (one or several projections sharing x).
-// floats per partial-sum slot: [KQ_MAX_BATCH][64] row sums, then (normalised
-// launches) the piece's sums of x^2 per batch row at kPartialQ
 constexpr int kHeadRows = 128;        // outputs per head of a KQ_EPI_HEADNORM segment (head_dim)
-constexpr int kPartialQ = KQ_MAX_BATCH * 64;
-constexpr int kPartialStride = kPartialQ + 64;
+
+// Workspace of one GEMV call (caller-owned device memory, see kq.h):
+//   [0, kCounterBytes)  arrival counters: kMaxGroups for split tiles (indexed by
+//                       workgroup, or by tile with column windows), then
+//                       kMaxGroups for head-norm heads (indexed by first tile).
+//                       Zero between calls: every call leaves them zero.
+//   then the partial-sum slots of split tiles, n_slots x partial_stride(B) floats
+//   (B = the call's batch): [B][64] row sums, then the piece's sums of x^2 per
+//   batch row (normalised launches) at partial_q(B);
+//   then, for launches with a head-norm segment, [tile][2][KQ_MAX_BATCH] floats of
+//   the heads' tile sums of squares.
+constexpr int kMaxGroups = 8192;
+constexpr size_t kCounterBytes = (size_t)2 * kMaxGroups * sizeof(uint32_t);
+__host__ __device__ constexpr int partial_q(int b) { return b * 64; }
+__host__ __device__ constexpr int partial_stride(int b) { return b * 64 + 64; }
+constexpr size_t kWorkspaceMax = kCounterBytes + (size_t)2 * kMaxGroups * partial_stride(KQ_MAX_BATCH) * sizeof(float) +
+                                 (size_t)kMaxGroups * 2 * KQ_MAX_BATCH * sizeof(float);
+static_assert(kWorkspaceMax == KQ_WORKSPACE_BYTES, "kq.h states the largest workspace a call can need");
+
+// Kernel arguments of one GEMV launch (one or several projections sharing x).
 
 struct GemvArgs {
   const uint8_t* w[KQ_MAX_PROJ];       // repacked weights of each projection
@@ -38,16 +53,16 @@ struct GemvArgs {
                                        // one segment whose tile t holds 32 gate and 32 up rows
   float rms_eps;                       // > 0: x is normalised first, x / sqrt(mean(x^2) + rms_eps) per batch row
   float head_eps;                      // KQ_EPI_HEADNORM segments: the per-head norm's epsilon
-  float* head_ss;                      // scratch: [tile][2][KQ_MAX_BATCH] sums of squares of the heads' tiles
-  uint32_t* head_ctr;                  // scratch: arrival counters per head (by its first tile), zero between calls
+  float* head_ss;                      // workspace: [tile][2][KQ_MAX_BATCH] sums of squares of the heads' tiles
+  uint32_t* head_ctr;                  // workspace: arrival counters per head (by its first tile), zero between calls
   // Whole-tile workgroups (tiles_per_wg > 0): n_win column windows, window w
   // covers win_base (+1 for w < win_extra) columns; wg_per_win workgroups per
   // window each take tiles_per_wg whole tiles of it.  tiles_per_wg == 0: even
   // runs of upw units per wavefront over the whole unit range.
   int32_t n_win, win_base, win_extra, wg_per_win, tiles_per_wg, n_tiles;
-  float* partial;                      // scratch: [workgroups][2] (windows: [n_win][n_tiles]) slots of
-                                       // kPartialStride floats
-  uint32_t* counters;                  // scratch: arrival counters per split tile, zero between calls
+  float* partial;                      // workspace: [workgroups][2] (windows: [n_win][n_tiles]) slots of
+                                       // partial_stride(batch) floats
+  uint32_t* counters;                  // workspace: arrival counters per split tile, zero between calls
 };
 
 // Control words of a chain launch (device memory owned by the chain).
@@ -56,6 +71,7 @@ struct ChainCtl {
   uint32_t* done;      // [step]: the run's tag once every workgroup finished the step
   uint32_t* epoch;     // tag of the last completed run
   uint32_t* error;     // set when a wait gave up
+  uint32_t* error_host;// pinned host word, set with the error word (read by the host without a sync)
   uint32_t groups;     // workgroups of the launch
   uint32_t spin;       // polls before a wait gives up
 };
@@ -119,6 +135,8 @@ hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, f
                           hipStream_t s);
 hipError_t launch_gather(int type, const void* w, int64_t rows, int64_t cols, const int32_t* ids, int64_t n,
                          float* out, int64_t ldo, hipStream_t s);
+// Zero n 32-bit words with a kernel (graph-capturable, unlike a memset node).
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 
 int64_t sb_bytes(int type);
 

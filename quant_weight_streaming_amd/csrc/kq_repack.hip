@@ -247,6 +247,10 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
   }
 }
 
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
 static int grid_for(int64_t total) {
   int64_t g = (total + 255) / 256;
   return (int)(g < 65536 ? (g > 0 ? g : 1) : 65536);
@@ -294,6 +298,11 @@ hipError_t launch_gather(int type, const void* w, int64_t rows, int64_t cols, co
     case KQ_Q6_K: hipLaunchKernelGGL(gather_kernel<KQ_Q6_K>, dim3(grid_for(total)), dim3(256), 0, s, in, ids, out, rows, n_cols, total, ldo); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for((int64_t)n)), dim3(256), 0, s, p, (int64_t)n);
   return hipGetLastError();
 }
 

@@ -24,13 +24,15 @@ TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
           5: "KQ_ERR_TYPE", 6: "KQ_ERR_HIP", 7: "KQ_ERR_NOMEM", 8: "KQ_ERR_RANGE", 9: "KQ_ERR_TIMEOUT",
-          10: "KQ_ERR_DEVICE"}
+          10: "KQ_ERR_DEVICE", 11: "KQ_ERR_WORKSPACE"}
+KQ_WORKSPACE_BYTES = 72417280     # enough for any GEMV call (kq.h)
 STATUS_CODE = {v: k for k, v in STATUS.items()}
-EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
+EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_gemv_workspace_bytes", "kq_workspace_init",
+           "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
            "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_fused", "kq_dequant", "kq_gather_rows",
            "kq_repack_swiglu",
            "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
-           "kq_chain_status", "kq_chain_destroy")
+           "kq_chain_query", "kq_chain_status", "kq_chain_destroy")
 
 
 class ChainStep(ctypes.Structure):
@@ -65,20 +67,26 @@ def lib() -> ctypes.CDLL:
         L.kq_status_str.restype = ctypes.c_char_p
         L.kq_init.argtypes = [ci]
         L.kq_init.restype = ci
+        L.kq_gemv_workspace_bytes.argtypes = [ci, ci, ctypes.POINTER(i64), i64, ci, ci,
+                                              ctypes.POINTER(ctypes.c_int32), ctypes.c_float]
+        L.kq_gemv_workspace_bytes.restype = ctypes.c_size_t
+        L.kq_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
+        L.kq_workspace_init.restype = ci
         L.kq_repacked_bytes.argtypes = [ci, i64, i64]
         L.kq_repacked_bytes.restype = ctypes.c_size_t
         L.kq_repack.argtypes = [ci, i64, i64, vp, vp, vp]
         L.kq_repack.restype = ci
         for n in ("kq_gemv_q4k", "kq_gemv_q5k", "kq_gemv_q6k"):
             f = getattr(L, n)
-            f.argtypes = [vp, i64, i64, vp, ci, i64, ci, vp, i64, vp]
+            f.argtypes = [vp, i64, i64, vp, ci, i64, ci, vp, i64, vp, ctypes.c_size_t, vp]
             f.restype = ci
         L.kq_gemv_multi.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
-                                    ctypes.POINTER(vp), ctypes.POINTER(i64), vp]
+                                    ctypes.POINTER(vp), ctypes.POINTER(i64), vp, ctypes.c_size_t, vp]
         L.kq_gemv_multi.restype = ci
         L.kq_gemv_fused.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
                                     ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
-                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_float, ctypes.c_float, vp]
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_float, ctypes.c_float, vp,
+                                    ctypes.c_size_t, vp]
         L.kq_gemv_fused.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
@@ -86,11 +94,11 @@ def lib() -> ctypes.CDLL:
         L.kq_gather_rows.restype = ci
         L.kq_repack_swiglu.argtypes = [ci, i64, i64, vp, vp, vp, vp]
         L.kq_repack_swiglu.restype = ci
-        L.kq_gemv_swiglu.argtypes = [ci, vp, i64, i64, vp, ci, i64, ci, vp, i64, vp]
+        L.kq_gemv_swiglu.argtypes = [ci, vp, i64, i64, vp, ci, i64, ci, vp, i64, vp, ctypes.c_size_t, vp]
         L.kq_gemv_swiglu.restype = ci
         L.kq_chain_create.argtypes = [ci, ctypes.POINTER(ChainStep), ci, ci, ctypes.POINTER(vp)]
         L.kq_chain_create.restype = ci
-        for n in ("kq_chain_status", "kq_chain_destroy"):
+        for n in ("kq_chain_query", "kq_chain_status", "kq_chain_destroy"):
             getattr(L, n).argtypes = [vp]
             getattr(L, n).restype = ci
         L.kq_chain_run.argtypes = [vp, vp]
@@ -132,6 +140,42 @@ def kq_init(device: int = 0) -> None:
     _check("kq_init", lib().kq_init(device))
 
 
+def kq_gemv_workspace_bytes(qtype, rows, cols: int, xtype: int, batch: int, epis=None, rms_eps: float = 0.0) -> int:
+    n = len(rows)
+    R = (ctypes.c_int64 * n)(*rows)
+    E = (ctypes.c_int32 * n)(*epis) if epis is not None else None
+    return int(lib().kq_gemv_workspace_bytes(_type(qtype), n, R, cols, xtype, batch, E, rms_eps))
+
+
+def kq_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check("kq_workspace_init", lib().kq_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(),
+                                                        _stream(stream)))
+
+
+_workspaces = {}
+
+
+def workspace(stream=None) -> torch.Tensor:
+    """This binding's workspace for `stream` (default: the current stream): KQ_WORKSPACE_BYTES of device
+    memory that torch allocates on the stream's device the first time the stream is used, prepared with
+    kq_workspace_init on that stream.  One per stream, so calls on unordered streams never share one."""
+    h = _stream(stream)
+    dev = torch.cuda.current_device()
+    key = (dev, h)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.empty(KQ_WORKSPACE_BYTES, dtype=torch.uint8, device=f"cuda:{dev}")
+        kq_workspace_init(ws, h)
+        _workspaces[key] = ws
+    return ws
+
+
+def _ws(ws, stream):
+    """(pointer, bytes) of the caller's workspace tensor, or of the stream's own."""
+    t = ws if ws is not None else workspace(stream)
+    return t.data_ptr(), t.numel() * t.element_size()
+
+
 def kq_repacked_bytes(qtype, rows: int, cols: int) -> int:
     return int(lib().kq_repacked_bytes(_type(qtype), rows, cols))
 
@@ -140,27 +184,28 @@ def kq_repack(qtype, rows: int, cols: int, gguf: torch.Tensor, out: torch.Tensor
     _check("kq_repack", lib().kq_repack(_type(qtype), rows, cols, gguf.data_ptr(), out.data_ptr(), _stream(stream)))
 
 
-def _gemv(fn: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+def _gemv(fn: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: torch.Tensor, stream=None,
+          work=None) -> None:
     if x.dim() != 2 or y.dim() != 2:
         raise ValueError("x is [batch, ldx], y is [batch, ldy]")
     f = getattr(lib(), fn)
     _check(fn, f(w.data_ptr(), rows, cols, x.data_ptr(), _xtype(x), x.stride(0), x.shape[0], y.data_ptr(),
-                 y.stride(0), _stream(stream)))
+                 y.stride(0), *_ws(work, stream), _stream(stream)))
 
 
-def kq_gemv_q4k(w, rows, cols, x, y, stream=None):
-    _gemv("kq_gemv_q4k", w, rows, cols, x, y, stream)
+def kq_gemv_q4k(w, rows, cols, x, y, stream=None, work=None):
+    _gemv("kq_gemv_q4k", w, rows, cols, x, y, stream, work)
 
 
-def kq_gemv_q5k(w, rows, cols, x, y, stream=None):
-    _gemv("kq_gemv_q5k", w, rows, cols, x, y, stream)
+def kq_gemv_q5k(w, rows, cols, x, y, stream=None, work=None):
+    _gemv("kq_gemv_q5k", w, rows, cols, x, y, stream, work)
 
 
-def kq_gemv_q6k(w, rows, cols, x, y, stream=None):
-    _gemv("kq_gemv_q6k", w, rows, cols, x, y, stream)
+def kq_gemv_q6k(w, rows, cols, x, y, stream=None, work=None):
+    _gemv("kq_gemv_q6k", w, rows, cols, x, y, stream, work)
 
 
-def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) -> None:
+def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None, work=None) -> None:
     n = len(ws)
     if len(rows) != n or len(ys) != n:
         raise ValueError("ws, rows and ys must have the same length")
@@ -169,11 +214,11 @@ def kq_gemv_multi(qtype, ws, rows, cols: int, x: torch.Tensor, ys, stream=None) 
     Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
     _check("kq_gemv_multi", lib().kq_gemv_multi(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
-                                                x.shape[0], Y, LD, _stream(stream)))
+                                                x.shape[0], Y, LD, *_ws(work, stream), _stream(stream)))
 
 
 def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rms_eps: float = 0.0,
-                  stream=None, head_eps: float = 0.0, y16s=None) -> None:
+                  stream=None, head_eps: float = 0.0, y16s=None, work=None) -> None:
     """kq_gemv_multi with a weight-less RMSNorm of x first (rms_eps > 0), an epilogue code per segment
     (epis: None for none; KQ_EPI_HEADNORM segments use head_eps) and optional bf16 copies of the outputs
     (y16s: None, or one bf16 tensor or None per segment)."""
@@ -190,7 +235,8 @@ def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rm
         Y16 = (ctypes.c_void_p * n)(*[t.data_ptr() if t is not None else None for t in y16s])
         LD16 = (ctypes.c_int64 * n)(*[t.stride(0) if t is not None else 0 for t in y16s])
     _check("kq_gemv_fused", lib().kq_gemv_fused(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
-                                                x.shape[0], Y, LD, Y16, LD16, E, rms_eps, head_eps, _stream(stream)))
+                                                x.shape[0], Y, LD, Y16, LD16, E, rms_eps, head_eps, *_ws(work, stream),
+                                                _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:
@@ -205,10 +251,10 @@ def kq_repack_swiglu(qtype, inter: int, cols: int, gate: torch.Tensor, up: torch
 
 
 def kq_gemv_swiglu(qtype, w: torch.Tensor, inter: int, cols: int, x: torch.Tensor, y: torch.Tensor,
-                   stream=None) -> None:
+                   stream=None, work=None) -> None:
     _check("kq_gemv_swiglu", lib().kq_gemv_swiglu(_type(qtype), w.data_ptr(), inter, cols, x.data_ptr(), _xtype(x),
                                                   x.stride(0), x.shape[0], y.data_ptr(), y.stride(0),
-                                                  _stream(stream)))
+                                                  *_ws(work, stream), _stream(stream)))
 
 
 def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tensor, out: torch.Tensor,
@@ -247,6 +293,11 @@ def kq_chain_run(handle: int, stream=None) -> None:
     _check("kq_chain_run", lib().kq_chain_run(handle, _stream(stream)))
 
 
+def kq_chain_query(handle: int) -> int:
+    """KQ_OK, or KQ_ERR_TIMEOUT once a run's wait has given up (no device synchronisation); does not raise."""
+    return lib().kq_chain_query(handle)
+
+
 def kq_chain_status(handle: int) -> int:
     """KQ_OK, or the status code (KQ_ERR_TIMEOUT when a wait gave up); does not raise."""
     return lib().kq_chain_status(handle)
@@ -275,6 +326,9 @@ class Chain:
     def status(self) -> int:
         return kq_chain_status(self.handle)
 
+    def query(self) -> int:
+        return kq_chain_query(self.handle)
+
     def close(self) -> None:
         if self.handle:
             kq_chain_destroy(self.handle)
@@ -297,10 +351,10 @@ def repack(qtype: str, gguf: torch.Tensor, rows: int, cols: int, stream=None) ->
 
 
 def gemv(qtype: str, w: torch.Tensor, rows: int, cols: int, x: torch.Tensor, y: torch.Tensor = None,
-         stream=None) -> torch.Tensor:
+         stream=None, work=None) -> torch.Tensor:
     if y is None:
         y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=x.device)
-    GEMV[qtype](w, rows, cols, x, y, stream)
+    GEMV[qtype](w, rows, cols, x, y, stream, work)
     return y
 
 

@@ -38,7 +38,7 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 def test_version_and_sizes():
-    assert kq.kq_abi_version() == 1
+    assert kq.kq_abi_version() == 2
     assert kq.kq_repacked_bytes("q4k", 256, 1024) == 256 * 4 * 144
     assert kq.kq_repacked_bytes("q5k", 1, 256) == 64 * 176          # one zero-padded tile
     assert kq.kq_repacked_bytes("q6k", 65, 512) == 2 * 2 * 64 * 210
@@ -48,6 +48,7 @@ def test_version_and_sizes():
 
 
 A16 = 0x10000  # a fake, 16-byte aligned "device" address: validation fails before any use
+WS = (A16, kq.KQ_WORKSPACE_BYTES)   # a fake workspace of the documented size
 
 
 @pytest.mark.parametrize("args,code", [
@@ -69,7 +70,7 @@ A16 = 0x10000  # a fake, 16-byte aligned "device" address: validation fails befo
 ])
 def test_gemv_rejects(args, code):
     for fn in ("kq_gemv_q4k", "kq_gemv_q5k", "kq_gemv_q6k"):
-        assert getattr(kq.lib(), fn)(*args, None) == code
+        assert getattr(kq.lib(), fn)(*args, *WS, None) == code
 
 
 def test_multi_and_others_reject():
@@ -79,13 +80,13 @@ def test_multi_and_others_reject():
     R = (i64 * 2)(64, 64)
     Y = (vp * 2)(A16, A16)
     LD = (i64 * 2)(64, 64)
-    assert L.kq_gemv_multi(9, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None) == 5
-    assert L.kq_gemv_multi(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None) == 4
-    assert L.kq_gemv_multi(1, 9, W, R, 256, A16, 1, 256, 1, Y, LD, None) == 4
+    assert L.kq_gemv_multi(9, 2, W, R, 256, A16, 1, 256, 1, Y, LD, *WS, None) == 5
+    assert L.kq_gemv_multi(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, *WS, None) == 4
+    assert L.kq_gemv_multi(1, 9, W, R, 256, A16, 1, 256, 1, Y, LD, *WS, None) == 4
     Yb = (vp * 2)(A16, None)
-    assert L.kq_gemv_multi(1, 2, W, R, 256, A16, 1, 256, 1, Yb, LD, None) == 1
+    assert L.kq_gemv_multi(1, 2, W, R, 256, A16, 1, 256, 1, Yb, LD, *WS, None) == 1
     Rb = (i64 * 2)(64, 0)
-    assert L.kq_gemv_multi(1, 2, W, Rb, 256, A16, 1, 256, 1, Y, LD, None) == 2
+    assert L.kq_gemv_multi(1, 2, W, Rb, 256, A16, 1, 256, 1, Y, LD, *WS, None) == 2
     assert L.kq_repack(1, 64, 256, None, A16, None) == 1
     assert L.kq_repack(1, 64, 300, A16, A16, None) == 2
     assert L.kq_repack(1, 64, 256, A16 + 2, A16, None) == 3       # Q4_K input needs 4-byte alignment
@@ -148,6 +149,7 @@ def test_chain_other_rejects():
     assert L.kq_chain_create(1, arr, 1, 1, None) == 1
     assert L.kq_chain_run(None, None) == 1
     assert L.kq_chain_status(None) == 1
+    assert L.kq_chain_query(None) == 1
     assert L.kq_chain_destroy(None) == 0
     assert L.kq_status_str(9) == b"a chain step's wait for the previous step gave up"
 
@@ -176,9 +178,9 @@ def test_swiglu_rejects():
     assert L.kq_repack_swiglu(1, 0, 256, A16, A16, A16, None) == 2
     assert L.kq_repack_swiglu(1, 64, 300, A16, A16, A16, None) == 2
     assert L.kq_repack_swiglu(1, 64, 256, A16, A16, A16 + 4, None) == 3
-    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 256, 17, A16, 64, None) == 4
-    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 128, 1, A16, 64, None) == 2
-    assert L.kq_gemv_swiglu(1, None, 64, 256, A16, 1, 256, 1, A16, 64, None) == 1
+    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 256, 17, A16, 64, *WS, None) == 4
+    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 128, 1, A16, 64, *WS, None) == 2
+    assert L.kq_gemv_swiglu(1, None, 64, 256, A16, 1, 256, 1, A16, 64, *WS, None) == 1
 
 
 def test_chain_rejects_bad_epilogue():
@@ -202,27 +204,27 @@ def test_fused_rejects():
     Y = (vp * 2)(A16, A16)
     LD = (i64 * 2)(64, 64)
     E = (ctypes.c_int32 * 2)(2, 9)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 0.0, None) == 5      # unknown code
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 0.0, *WS, None) == 5      # unknown code
     E = (ctypes.c_int32 * 2)(1, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 0.0, None) == 5      # SwiGLU needs n = 1
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 0.0, *WS, None) == 5      # SwiGLU needs n = 1
     for eps in (-1e-5, float("inf"), float("nan")):
-        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, eps, 0.0, None) == 2
-    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, 0.0, 0.0, None) == 4
+        assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, eps, 0.0, *WS, None) == 2
+    assert L.kq_gemv_fused(1, 0, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, 0.0, 0.0, *WS, None) == 4
     # head norm: rows a multiple of KQ_HEAD_ROWS, head_eps finite and > 0
     E = (ctypes.c_int32 * 2)(4, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 1e-6, None) == 2    # 64 rows
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, E, 0.0, 1e-6, *WS, None) == 2    # 64 rows
     R2 = (i64 * 2)(128, 64)
     LD2 = (i64 * 2)(128, 64)
     for eps in (0.0, -1.0, float("inf"), float("nan")):
-        assert L.kq_gemv_fused(1, 2, W, R2, 256, A16, 1, 256, 1, Y, LD2, None, None, E, 0.0, eps, None) == 2
+        assert L.kq_gemv_fused(1, 2, W, R2, 256, A16, 1, 256, 1, Y, LD2, None, None, E, 0.0, eps, *WS, None) == 2
     # bf16 copies: a stride for every copy, at least the segment's rows, 2-byte aligned
     Y16 = (vp * 2)(A16, None)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, None, None, 0.0, 0.0, None) == 1
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, None, None, 0.0, 0.0, *WS, None) == 1
     LD16 = (i64 * 2)(63, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, LD16, None, 0.0, 0.0, None) == 2
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, LD16, None, 0.0, 0.0, *WS, None) == 2
     Y16 = (vp * 2)(A16 + 1, None)
     LD16 = (i64 * 2)(64, 0)
-    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, LD16, None, 0.0, 0.0, None) == 3
+    assert L.kq_gemv_fused(1, 2, W, R, 256, A16, 1, 256, 1, Y, LD, Y16, LD16, None, 0.0, 0.0, *WS, None) == 3
     st = _step()
     st.y16[0], st.ldy16[0] = A16, 32
     arr = (kq.ChainStep * 1)(st)
@@ -239,3 +241,37 @@ def test_fused_rejects():
     st = _step(epilogue=4, head_eps=1e-6)           # a head-norm segment of 64 rows
     arr = (kq.ChainStep * 1)(st)
     assert L.kq_chain_create(1, arr, 1, 1, ctypes.byref(h)) == 2
+
+
+def test_workspace_rules():
+    """The library allocates nothing: a GEMV call without a usable workspace is refused on the host."""
+    L = kq.lib()
+    args = (A16, 64, 256, A16, 1, 256, 1, A16, 64)
+    for fn in ("kq_gemv_q4k", "kq_gemv_q5k", "kq_gemv_q6k"):
+        assert getattr(L, fn)(*args, None, kq.KQ_WORKSPACE_BYTES, None) == 11          # no workspace
+        assert getattr(L, fn)(*args, A16 + 8, kq.KQ_WORKSPACE_BYTES, None) == 11       # misaligned
+        assert getattr(L, fn)(A16, 64, 300, A16, 1, 300, 1, A16, 64, None, 0, None) == 2   # arguments first
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    W, R, Y, LD = (vp * 1)(A16), (i64 * 1)(64), (vp * 1)(A16), (i64 * 1)(64)
+    assert L.kq_gemv_multi(1, 1, W, R, 256, A16, 1, 256, 1, Y, LD, None, 0, None) == 11
+    assert L.kq_gemv_fused(1, 1, W, R, 256, A16, 1, 256, 1, Y, LD, None, None, None, 0.0, 0.0, None, 0, None) == 11
+    assert L.kq_gemv_swiglu(1, A16, 64, 256, A16, 1, 256, 1, A16, 64, None, 0, None) == 11
+    assert L.kq_workspace_init(None, kq.KQ_WORKSPACE_BYTES, None) == 1
+    assert L.kq_workspace_init(A16 + 4, kq.KQ_WORKSPACE_BYTES, None) == 11
+    assert L.kq_workspace_init(A16, 65535, None) == 11                               # smaller than the counters
+    assert L.kq_status_str(11) == b"workspace missing, misaligned or smaller than the call needs"
+    # the size query returns 0 for invalid arguments
+    assert kq.kq_gemv_workspace_bytes("q4k", [64], 300, kq.KQ_X_BF16, 1) == 0
+    assert kq.kq_gemv_workspace_bytes("q4k", [64], 256, kq.KQ_X_BF16, 17) == 0
+    assert kq.kq_gemv_workspace_bytes(9, [64], 256, kq.KQ_X_BF16, 1) == 0
+
+
+def test_workspace_bound_matches_layout():
+    """KQ_WORKSPACE_BYTES = the counter block + two slots of 16 batch rows per workgroup for the largest grid
+    + the heads' sums of squares (the layout the library documents)."""
+    counters = 2 * 8192 * 4
+    slots = 2 * 8192 * (16 * 64 + 64) * 4
+    heads = 8192 * 2 * 16 * 4
+    assert kq.KQ_WORKSPACE_BYTES == counters + slots + heads
+    src = open(os.path.join(ROOT, "include", "kq.h")).read()
+    assert re.search(r"#define KQ_WORKSPACE_BYTES (\d+)u", src).group(1) == str(kq.KQ_WORKSPACE_BYTES)

@@ -199,30 +199,36 @@ def test_chain_graph_replay():
 
 
 def test_chain_wait_that_gives_up_is_reported(monkeypatch):
-    """With no polls allowed (KQ_CHAIN_SPIN=0) a wait that finds the previous step unfinished gives up:
-    the run ends and kq_chain_status says so (the results are then invalid); a chain made with the
-    default limit afterwards runs clean.  Step 1 gives every workgroup work, so every workgroup waits
-    for step 0, and the first to finish step 0 finds it unfinished."""
+    """With no polls allowed (KQ_CHAIN_SPIN=0, read at each run) a wait that finds the previous step unfinished
+    gives up: the run's results are invalid, the host-visible flag says so without a device synchronisation
+    (kq_chain_query), the next kq_chain_run is refused, and kq_chain_status reports it and resets the chain.
+    The same chain then runs clean with the default limit and matches its single launches bitwise (so the
+    time-out left no stale split-tile counters behind).  Step 1 gives every workgroup work, so every
+    workgroup waits for step 0, and the first to finish step 0 finds it unfinished."""
     batch = 1
+    timeout = kq.STATUS_CODE["KQ_ERR_TIMEOUT"]
     say("case chain spin 0")
     specs = [("q6k", (64 * 64,), 122 * 256), ("q4k", (16384,), 4096), ("q4k", (256,), 1024)]
     steps, hosts = _independent_steps(specs, batch, "bf16", "spin")
+    ch = kq.Chain(steps, batch)
     monkeypatch.setenv("KQ_CHAIN_SPIN", "0")
-    ch = kq.Chain(steps, batch)
     ch.run()
     torch.cuda.synchronize()
-    assert ch.status() == kq.STATUS_CODE["KQ_ERR_TIMEOUT"]
-    assert ch.status() == 0                    # reading the flag cleared it
-    ch.close()
+    assert ch.query() == timeout               # host-visible, no synchronisation
+    with pytest.raises(kq.KQError) as err:     # refused: nothing is enqueued until a reset
+        ch.run()
+    assert err.value.code == timeout
+    assert ch.status() == timeout              # reports and resets
+    assert ch.query() == 0 and ch.status() == 0
     monkeypatch.delenv("KQ_CHAIN_SPIN")
-    ch = kq.Chain(steps, batch)
-    for s in steps:
-        for y in s[5]:
-            y.fill_(SENTINEL)
-    ch.run()
-    torch.cuda.synchronize()
-    assert ch.status() == 0
-    _check_steps(steps, hosts, _singles(steps), "after a time-out")
+    for rep in range(2):
+        for s in steps:
+            for y in s[5]:
+                y.fill_(SENTINEL)
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        _check_steps(steps, hosts, _singles(steps), f"the same chain after a time-out, run {rep}")
     ch.close()
 
 
