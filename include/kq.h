@@ -128,8 +128,10 @@ int kq_abi_version(void);
 const char *kq_status_str(int status);
 
 /*
- * Check that `device` (the HIP ordinal) exists and can be queried.  Allocates
- * nothing.  Returns KQ_OK, else KQ_ERR_DEVICE / KQ_ERR_HIP.
+ * Check that `device` (the HIP ordinal) exists and can be queried, and look up
+ * the device address of its kq_gemv_fused_noalloc scratch (otherwise done at
+ * that entry point's first call on the device).  Allocates nothing.  Returns
+ * KQ_OK, else KQ_ERR_DEVICE / KQ_ERR_HIP.
  */
 int kq_init(int device);
 
@@ -248,6 +250,25 @@ int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, 
 int kq_gemv_fused(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x, int xtype,
                   int64_t ldx, int batch, float *const *y, const int64_t *ldy, void *const *y16, const int64_t *ldy16,
                   const int32_t *epi, float rms_eps, float head_eps, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kq_gemv_fused for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without (ws, ws_bytes) and the same results bitwise.  Its
+ * workspace is a static array of KQ_NOALLOC_SCRATCH_BYTES (8 MiB) in the
+ * library's device code, one copy per GPU, which each GPU holds until the
+ * process ends; the entry point calls no hipMalloc, hipFree or allocating
+ * routine.  A call whose workspace need (kq_gemv_workspace_bytes) exceeds it
+ * is refused with KQ_ERR_WORKSPACE, enqueueing nothing.  Each call first
+ * clears the array's counter block with a kernel on `stream`.  Every call on
+ * one GPU shares that GPU's array: calls that may overlap in time on one GPU
+ * (unordered streams, threads) race and give wrong results; order them.
+ */
+#define KQ_NOALLOC_SCRATCH_BYTES 8388608u
+int kq_gemv_fused_noalloc(int type, int n, const void *const *w, const int64_t *rows, int64_t cols, const void *x,
+                          int xtype, int64_t ldx, int batch, float *const *y, const int64_t *ldy,
+                          void *const *y16, const int64_t *ldy16, const int32_t *epi, float rms_eps, float head_eps,
+                          void *stream);
 
 /*
  * SwiGLU epilogue: the gate and up projections of the feed-forward block in one

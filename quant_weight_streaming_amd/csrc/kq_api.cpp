@@ -26,6 +26,34 @@ int64_t sb_bytes(int type) {
 }
 
 
+// Workspace of kq_gemv_fused_noalloc, for callers that cannot allocate: one
+// copy per GPU in the code object's static memory, held until the process
+// ends.  Host code never uses the name `scratch` as an address (on the host it
+// is only a stand-in for the symbol): the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+static_assert(kStaticScratchBytes == KQ_NOALLOC_SCRATCH_BYTES, "kq.h states the static scratch size");
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's `scratch` (looked up on first use).
+static int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KQ_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KQ_OK;
+}
+
 // CUs of the current device (the launch geometry is planned for them).
 static int current_device_cus(int* dev_out, int* cus) {
   int dev = 0;
@@ -485,11 +513,16 @@ const char* kq_status_str(int status) {
 }
 
 int kq_init(int device) {
-  int n = 0, cus = 0;
+  int n = 0, cus = 0, prev = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return KQ_ERR_DEVICE;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
     return KQ_ERR_HIP;
-  return KQ_OK;
+  // look up this device's static scratch now, with the device current
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) return KQ_ERR_HIP;
+  void* p = nullptr;
+  const int rc = static_scratch(&p);
+  (void)hipSetDevice(prev);
+  return rc;
 }
 
 size_t kq_gemv_workspace_bytes(int type, int n, const int64_t* rows, int64_t cols, int xtype, int batch,
@@ -576,6 +609,41 @@ int kq_gemv_fused(int type, int n, const void* const* w, const int64_t* rows, in
   }
   return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, ws, ws_bytes, stream, packed, rms_eps,
                    head_eps, y16, ldy16);
+}
+
+int kq_gemv_fused_noalloc(int type, int n, const void* const* w, const int64_t* rows, int64_t cols, const void* x,
+                          int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy,
+                          void* const* y16, const int64_t* ldy16, const int32_t* epi, float rms_eps, float head_eps,
+                          void* stream) {
+  if (n < 1 || n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
+  uint32_t packed = 0;
+  if (epi) {
+    if (n == 1 && epi[0] == KQ_EPI_SWIGLU) {
+      packed = KQ_EPI_SWIGLU;
+      if (rows && rows[0] > (int64_t)INT32_MAX / 2 - 64) return KQ_ERR_RANGE;
+    } else {
+      for (int i = 0; i < n; ++i) {
+        if (!segment_code(epi[i])) return KQ_ERR_TYPE;
+        packed |= (uint32_t)epi[i] << (4 * i);
+      }
+    }
+  }
+  int rc = validate_call(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, packed, rms_eps, head_eps, y16,
+                         ldy16);
+  if (rc != KQ_OK) return rc;
+  Plan p{};
+  rc = plan_call(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, packed, rms_eps, head_eps, y16, ldy16, &p);
+  if (rc != KQ_OK) return rc;
+  if (p.ws_bytes > kStaticScratchBytes) return KQ_ERR_WORKSPACE;   // beyond the static scratch: refused
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != KQ_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the previous call on this GPU left the counters zero; clear them anyway (a kernel, not a memset node)
+  if (launch_zero_words(static_cast<uint32_t*>(ws), kCounterBytes / 4, s) != hipSuccess) return KQ_ERR_HIP;
+  assign_workspace(p, static_cast<uint8_t*>(ws));
+  if (launch_gemv(type, xtype, p.rows, p.nw, p.mf, p.a, (int)p.grid, p.lds, s) != hipSuccess) return KQ_ERR_HIP;
+  return KQ_OK;
 }
 
 int kq_gemv_swiglu(int type, const void* w, int64_t inter, int64_t cols, const void* x, int xtype, int64_t ldx,

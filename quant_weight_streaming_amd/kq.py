@@ -26,10 +26,12 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4:
           5: "KQ_ERR_TYPE", 6: "KQ_ERR_HIP", 7: "KQ_ERR_NOMEM", 8: "KQ_ERR_RANGE", 9: "KQ_ERR_TIMEOUT",
           10: "KQ_ERR_DEVICE", 11: "KQ_ERR_WORKSPACE"}
 KQ_WORKSPACE_BYTES = 72417280     # enough for any GEMV call (kq.h)
+KQ_NOALLOC_SCRATCH_BYTES = 8388608  # the static scratch of kq_gemv_fused_noalloc (kq.h)
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_gemv_workspace_bytes", "kq_workspace_init",
            "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
-           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_fused", "kq_dequant", "kq_gather_rows",
+           "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_fused", "kq_gemv_fused_noalloc", "kq_dequant",
+           "kq_gather_rows",
            "kq_repack_swiglu",
            "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
            "kq_chain_query", "kq_chain_status", "kq_chain_destroy")
@@ -88,6 +90,11 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_float, ctypes.c_float, vp,
                                     ctypes.c_size_t, vp]
         L.kq_gemv_fused.restype = ci
+        L.kq_gemv_fused_noalloc.argtypes = [ci, ci, ctypes.POINTER(vp), ctypes.POINTER(i64), i64, vp, ci, i64, ci,
+                                            ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(vp),
+                                            ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32), ctypes.c_float,
+                                            ctypes.c_float, vp]
+        L.kq_gemv_fused_noalloc.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
         L.kq_gather_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, vp]
@@ -237,6 +244,26 @@ def kq_gemv_fused(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rm
     _check("kq_gemv_fused", lib().kq_gemv_fused(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0),
                                                 x.shape[0], Y, LD, Y16, LD16, E, rms_eps, head_eps, *_ws(work, stream),
                                                 _stream(stream)))
+
+
+def kq_gemv_fused_noalloc(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=None, rms_eps: float = 0.0,
+                          stream=None, head_eps: float = 0.0, y16s=None) -> None:
+    """kq_gemv_fused on the library's static scratch: no workspace argument, no allocation."""
+    n = len(ws)
+    if len(rows) != n or len(ys) != n or (epis is not None and len(epis) != n) or (y16s is not None and len(y16s) != n):
+        raise ValueError("ws, rows, ys, epis and y16s must have the same length")
+    W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in ws])
+    R = (ctypes.c_int64 * n)(*rows)
+    Y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    LD = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
+    E = (ctypes.c_int32 * n)(*epis) if epis is not None else None
+    Y16 = LD16 = None
+    if y16s is not None:
+        Y16 = (ctypes.c_void_p * n)(*[t.data_ptr() if t is not None else None for t in y16s])
+        LD16 = (ctypes.c_int64 * n)(*[t.stride(0) if t is not None else 0 for t in y16s])
+    _check("kq_gemv_fused_noalloc",
+           lib().kq_gemv_fused_noalloc(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0), x.shape[0],
+                                       Y, LD, Y16, LD16, E, rms_eps, head_eps, _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:
