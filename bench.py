@@ -14,6 +14,11 @@ the roofline of the dominant kernel and the CPU oracle baseline are reported in
 the same JSON line.  Decode priced as weight bytes per token follows the Core AI
 card's decode table ("23.7 x 17.9 GB is 424 GB/s of traffic").
 
+Also reported: per-step median/min/max, the three single-GEMV workloads (the small Q4_K GEMV's latency,
+gate+up and the head over rotated weight copies), the CPU oracle on one thread for those three, the
+achievable HBM read rate (kq_stream_read), GPU power and clocks under load before and after the timed
+work (amd-smi), and the host CPU model.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-c4]
        python bench.py --profile-kernel N     # only the dominant kernel, N launches (for rocprofv3)
        python bench.py --copy-calibration N   # N plain device copies of 1 GiB (counter calibration)
@@ -134,9 +139,28 @@ class Sweep:
         return out
 
 
-def time_chain(sw: Sweep, B: int, steps: int, warmup: int) -> float:
+def step_stats(per_step_ms) -> dict:
+    """Median, min and max of per-step times (ms)."""
+    d = sorted(per_step_ms)
+    return dict(median=round(d[len(d) // 2], 4), min=round(d[0], 4), max=round(d[-1], 4), n=len(d))
+
+
+def timed_steps(run, steps: int, stream):
+    """HIP events on `stream` around each of `steps` calls of run(): (mean ms, [ms per step])."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[-1]) / steps, per
+
+
+def time_chain(sw: Sweep, B: int, steps: int, warmup: int, per_step: dict = None) -> float:
     """The whole sweep as one chain launch (step j+1 reads its x only after step j's y is complete);
-    returns ms per step."""
+    returns ms per step (per-step times in per_step['chain'] if given)."""
     torch, kq = sw.torch, sw.kq
     chain = kq.Chain([(spec.qtype, reps, parts, spec.cols, sw.x[B][i], sw.y[B][i])
                       for i, (layer, spec, reps, parts) in enumerate(sw.entries)], B)
@@ -144,16 +168,13 @@ def time_chain(sw: Sweep, B: int, steps: int, warmup: int) -> float:
     for _ in range(warmup):
         chain.run(stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        chain.run(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms, per = timed_steps(lambda: chain.run(stream), steps, stream)
     if chain.status() != 0:
         raise RuntimeError("a chain step's wait gave up: the chain timing is invalid")
     chain.close()
-    return e0.elapsed_time(e1) / steps
+    if per_step is not None:
+        per_step["chain"] = step_stats(per)
+    return ms
 
 
 def time_gather(rows: int, cols: int, batches, reps: int = 64) -> dict:
@@ -349,21 +370,16 @@ def run_calls(calls):
             raise RuntimeError(f"{name}: GEMV launch failed with status {rc}")
 
 
-def time_sweep(sw: Sweep, B: int, steps: int, warmup: int):
-    """Plain stream launches and hipGraph replay of the whole sweep; returns ms per step for both."""
+def time_sweep(sw: Sweep, B: int, steps: int, warmup: int, per_step: dict = None):
+    """Plain stream launches and hipGraph replay of the whole sweep; returns ms per step for both
+    (per-step times in per_step['plain'] and per_step['graph'] if given)."""
     torch = sw.torch
     stream = torch.cuda.current_stream()
     calls = sw.calls(B, stream.cuda_stream)
     for _ in range(warmup):
         run_calls(calls)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        run_calls(calls)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    plain_ms = e0.elapsed_time(e1) / steps
+    plain_ms, plain_per = timed_steps(lambda: run_calls(calls), steps, stream)
     ref = [[y.clone() for y in ys] for ys in sw.y[B]]
 
     g = torch.cuda.CUDAGraph()
@@ -378,13 +394,11 @@ def time_sweep(sw: Sweep, B: int, steps: int, warmup: int):
             if not torch.equal(y, r):
                 raise RuntimeError(f"graph replay differs from eager launch (GEMV {i}, B={B})")
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / steps
+    graph_ms, graph_per = timed_steps(g.replay, steps, stream)
     del g
+    if per_step is not None:
+        per_step["plain"] = step_stats(plain_per)
+        per_step["graph"] = step_stats(graph_per)
     return plain_ms, graph_ms
 
 
@@ -452,6 +466,185 @@ def kernel_times(sw: Sweep, B: int, reps: int = 3):
                          avg_us=round(ms * 1e3, 2), weight_gbs=round(weight_gbs(wb, ms), 1),
                          weight_bytes=wb, x_bytes=B * spec.cols * 2, y_bytes=B * spec.rows * 4)
     return out
+
+
+def host_info() -> dict:
+    """The host CPU's model name (lscpu) and the cores this process may use."""
+    import subprocess
+    model = ""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception as e:          # no lscpu: say so in the record
+        model = f"unknown ({type(e).__name__})"
+    return dict(cpu_model=model, cores=len(os.sched_getaffinity(0)))
+
+
+def smi_under_load(run, warm_s: float = 1.0, max_s: float = 6.0) -> dict:
+    """GPU power and clocks read by amd-smi while run() keeps the GPU busy (an idle GPU reads its
+    deep-sleep clocks): run() repeats for warm_s seconds, then amd-smi runs as a child process while run()
+    keeps repeating until it returns."""
+    import subprocess
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < warm_s:
+        run()
+        torch.cuda.synchronize()
+    try:
+        pr = subprocess.Popen(["amd-smi", "metric", "-p", "-c", "--json"], stdout=subprocess.PIPE,
+                              stderr=subprocess.DEVNULL, text=True)
+    except Exception as e:
+        return dict(error=f"amd-smi not run: {type(e).__name__}")
+    t0 = time.time()
+    while pr.poll() is None and time.time() - t0 < max_s:
+        run()
+        torch.cuda.synchronize()
+    try:
+        out, _ = pr.communicate(timeout=30)
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        gfx = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        return dict(power_w=g["power"]["socket_power"]["value"], gfx_mhz_mean=round(sum(gfx) / len(gfx), 1),
+                    gfx_mhz_min=min(gfx), gfx_mhz_max=max(gfx), mem_mhz=g["clock"]["mem_0"]["clk"]["value"],
+                    seconds_under_load=round(time.time() - t0, 2))
+    except Exception as e:
+        if pr.poll() is None:
+            pr.kill()
+        return dict(error=f"amd-smi output not read: {type(e).__name__}")
+
+
+def read_ceiling(gib: int = 4, reps: int = 10) -> dict:
+    """The achievable HBM read rate: kq_stream_read over `gib` GiB (far beyond the 256 MB Infinity
+    Cache) with the GEMV's own loads, HIP events per read, median."""
+    import torch
+    from quant_weight_streaming_amd import kq
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    kq.kq_stream_read(buf, sink, stream)
+    _, per = timed_steps(lambda: kq.kq_stream_read(buf, sink, stream), reps, stream)
+    del buf
+    med = sorted(per)[len(per) // 2]
+    return dict(gbs=round((gib << 30) / med / 1e6, 1), best_gbs=round((gib << 30) / min(per) / 1e6, 1),
+                bytes=gib << 30, median_ms=round(med, 4),
+                how="kq_stream_read: every byte read once with 128-bit nontemporal buffer loads, 16 per "
+                    "wavefront in flight, 16 workgroups of 4 wavefronts per CU; median of 10 reads")
+
+
+def single_gemvs(sw: Sweep, kt1: dict, reps: int = 8) -> dict:
+    """The three single-GEMV workloads: the small Q4_K 256x1024 GEMV with fp32 x (latency only: it fits in
+    cache), gate+up alone over rotated weight copies, and the head alone over two rotated copies (so no
+    launch finds its weights in the 256 MB Infinity Cache)."""
+    import statistics
+    torch, kq, synth = sw.torch, sw.kq, sw.synth
+    stream = torch.cuda.current_stream()
+    out = {}
+    # config 0: latency of one launch, eager (launch overhead included) and inside a graph of 100
+    c0 = synth.CONFIGS[0]["gemv"]
+    g = synth.gen_weights("q4k", c0.rows, c0.cols, 0, device="cuda:0")
+    w0 = kq.repack("q4k", g, c0.rows, c0.cols)
+    x0 = synth.gen_x(1, c0.cols, 0, "f32", device="cuda:0")
+    y0 = torch.empty((1, c0.rows), device="cuda:0")
+    for _ in range(10):
+        kq.gemv("q4k", w0, c0.rows, c0.cols, x0, y0, stream, sw.work)
+    torch.cuda.synchronize()
+    _, eager = timed_steps(lambda: kq.gemv("q4k", w0, c0.rows, c0.cols, x0, y0, stream, sw.work), 50, stream)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(100):
+            kq.gemv("q4k", w0, c0.rows, c0.cols, x0, y0, torch.cuda.current_stream(), sw.work)
+    gr.replay()
+    torch.cuda.synchronize()
+    _, per = timed_steps(gr.replay, 5, stream)
+    out["c0_q4k_256x1024_b1_f32"] = dict(
+        eager_us=dict(median=round(statistics.median(eager) * 1e3, 2), min=round(min(eager) * 1e3, 2),
+                      max=round(max(eager) * 1e3, 2)),
+        in_graph_us=round(statistics.median(per) * 1e3 / 100, 2),
+        note="147,456 weight bytes: latency only, the matrix sits in cache")
+    del gr
+    # config 1: gate+up alone, 52 distinct weight copies back to back (the sweep's class graph)
+    gu = kt1["gate_up"]
+    out["c1_gate_up_q4k_62464x5120_b1"] = dict(avg_us=gu["avg_us"], weight_gbs=gu["weight_gbs"],
+                                               pct_of_hbm_peak=round(100 * gu["weight_gbs"] / HBM_PEAK_GBS, 2),
+                                               rotated_copies=52, launches=gu["launches"])
+    # config 2: the head alone, two copies alternating
+    head = [e for e in sw.entries if e[1].name == "head"][0]
+    spec, reps0 = head[1], head[2]
+    g2 = synth.gen_weights("q6k", spec.rows, spec.cols, synth.seed_of("bench-head-copy"), device="cuda:0")
+    w2 = kq.repack("q6k", g2, spec.rows, spec.cols)
+    del g2
+    xh = synth.gen_x(1, spec.cols, 7, device="cuda:0")
+    yh = torch.empty((1, spec.rows), device="cuda:0")
+    copies = [reps0[0], w2]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for i in range(2 * reps):
+            kq.gemv("q6k", copies[i % 2], spec.rows, spec.cols, xh, yh, torch.cuda.current_stream(), sw.work)
+    gr.replay()
+    torch.cuda.synchronize()
+    _, per = timed_steps(gr.replay, 3, stream)
+    us = statistics.median(per) * 1e3 / (2 * reps)
+    wb = spec.rows * spec.cols // 256 * 210
+    out["c2_head_q6k_131072x5120_b1"] = dict(avg_us=round(us, 2), weight_gbs=round(wb / us / 1e3, 1),
+                                             pct_of_hbm_peak=round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 2),
+                                             rotated_copies=2, launches=2 * reps * 3)
+    del gr, w2
+    torch.cuda.empty_cache()
+    return out
+
+
+def oracle_one_thread(frac1: float = 0.01, frac2: float = 0.005) -> dict:
+    """The C oracle on ONE thread for the three single-GEMV workloads: the whole small GEMV, and the first
+    rows of gate+up and of the head (fraction frac1 / frac2), extrapolated by rows to the whole GEMV (the
+    oracle's time is linear in rows)."""
+    import numpy as np
+    import torch
+    from oracle import oracle as O
+    from quant_weight_streaming_amd import synth
+    Or = O.default()
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        prev = gomp.omp_get_max_threads()
+        gomp.omp_set_num_threads(1)
+    except OSError:
+        return dict(error="libgomp not found: thread count not set")
+    out = {}
+    try:
+        for key, spec, xd, frac in (("c0_q4k_256x1024_b1_f32", synth.CONFIGS[0]["gemv"], "f32", 1.0),
+                                    ("c1_gate_up_q4k_62464x5120_b1", synth.GATE_UP, "bf16", frac1),
+                                    ("c2_head_q6k_131072x5120_b1", synth.HEAD, "bf16", frac2)):
+            rs = max(1, int(round(spec.rows * frac)))
+            g = synth.gen_weights(spec.qtype, rs, spec.cols, synth.seed_of("oracle-1t", key)).numpy()
+            x = synth.gen_x(1, spec.cols, 3, xd)
+            xh = x.numpy() if xd == "f32" else x.view(torch.int16).numpy().view(np.uint16)
+            t = time.perf_counter()
+            Or.gemv(spec.qtype, rs, spec.cols, g, xh)
+            dt = time.perf_counter() - t
+            full = dt * spec.rows / rs
+            wb = spec.rows * spec.cols // 256 * synth.SB_BYTES[spec.qtype]
+            out[key] = dict(rows_timed=rs, seconds_timed=round(dt, 4), seconds_whole_gemv=round(full, 4),
+                            weight_gbs=round(wb / full / 1e9, 4))
+    finally:
+        gomp.omp_set_num_threads(prev)
+    out["threads"] = 1
+    return out
+
+
+def profile_roofline() -> dict:
+    """The roofline kernel's mean duration inside the sweep from the committed rocprofv3 kernel-trace summary,
+    if it was taken of the current kernels."""
+    p = os.path.join(ROOT, "profiles", "gemv_sweep52_kernel_trace.txt")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m = re.search(r"kernel hash: ([0-9a-f]+)", txt)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(r"after another GEMV \(the sweep\)\s+(\d+) dispatches, mean\s+([0-9.]+)", txt)
+    return dict(avg_launch_us=float(m.group(2)), dispatches=int(m.group(1))) if m else None
 
 
 def cpu_baseline(sw: Sweep, frac: float):
@@ -555,7 +748,8 @@ def summarize_trace(src: str, cmd: str) -> str:
         if key not in label:
             label[key] = order[i % len(order)]
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    out = [f"command: {cmd}", "", "rocprofv3 kernel stats (kq kernels; durations in us):",
+    out = [f"command: {cmd}", f"kernel hash: {kernel_source_hash()}", "",
+           "rocprofv3 kernel stats (kq kernels; durations in us):",
            f"{'kernel':44s} {'calls':>6s} {'avg':>9s} {'min':>9s} {'max':>9s}"]
     for r in stats:
         out.append(f"{r['Name'].split('(')[0].replace('void ', ''):44s} {int(r['Calls']):6d} "
@@ -695,11 +889,18 @@ def main():
         log(f"[bench] oracle probe {rate:.3f} GB/s -> sample fraction {frac:.3f}")
 
     VERIFY = (2, 3, 4, 12, 16)     # speculative-verify block sizes for the cost staircase
+    host = host_info()
     sw = Sweep(3, "q4k", (1, 8) + VERIFY, 0.0, frac)
-    res = {}
+    # clocks and power under load, before the timed work (an idle GPU shows its deep-sleep clocks)
+    smi_chain = sw.kq.Chain([(spec.qtype, reps, parts, spec.cols, sw.x[1][i], sw.y[1][i])
+                             for i, (layer, spec, reps, parts) in enumerate(sw.entries)], 1)
+    smi_before = smi_under_load(smi_chain.run)
+    log(f"[bench] amd-smi under load before timing: {smi_before}")
+    res, per_step = {}, {}
     for B in (1, 8):
-        plain, graph = time_sweep(sw, B, args.steps, args.warmup)
-        chain = time_chain(sw, B, args.steps, args.warmup)
+        per_step[B] = {}
+        plain, graph = time_sweep(sw, B, args.steps, args.warmup, per_step[B])
+        chain = time_chain(sw, B, args.steps, args.warmup, per_step[B])
         res[B] = dict(plain_ms=plain, graph_ms=graph, chain_ms=chain)
         log(f"[bench] cfg3 B={B}: plain {plain:.3f} ms ({sw.weight_bytes / plain / 1e6:.0f} GB/s), "
             f"graph {graph:.3f} ms ({sw.weight_bytes / graph / 1e6:.0f} GB/s), "
@@ -719,6 +920,16 @@ def main():
     kt1 = kernel_times(sw, 1)
     kt8 = kernel_times(sw, 8)
     gu_in_sweep_us = kernel_time_in_sweep(sw, 1, "gate_up")
+    singles = single_gemvs(sw, kt1)
+    log(f"[bench] single GEMVs: {singles}")
+    smi_after = smi_under_load(smi_chain.run)
+    smi_chain.close()
+    log(f"[bench] amd-smi under load after timing: {smi_after}")
+    ceiling = read_ceiling()
+    log(f"[bench] read ceiling: {ceiling['gbs']} GB/s")
+    if not args.no_cpu:
+        singles["oracle_one_thread"] = oracle_one_thread()
+        log(f"[bench] oracle on one thread: {singles['oracle_one_thread']}")
     cpu = cpu_baseline(sw, frac) if not args.no_cpu else None
     swiglu_us = time_swiglu(synth.INTER, synth.HIDDEN, (1, 8))
     decode = time_decode_chain((1, 8), max(3, args.steps // 2), args.warmup)
@@ -735,6 +946,7 @@ def main():
     log(f"[bench] gate+up with SwiGLU epilogue (Q4_K 2 x {synth.INTER}x{synth.HIDDEN}): {swiglu_us} us "
         f"(plain gate+up: {kt1['gate_up']['avg_us']} / {kt8['gate_up']['avg_us']} us)")
     if cpu:
+        cpu["cpu_model"] = host["cpu_model"]
         log(f"[bench] cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads over {cpu['seconds']} s")
 
     # roofline of the dominant kernel (gate+up, batch 1): algorithmic bytes per launch / the mean cost of
@@ -742,13 +954,21 @@ def main():
     gu = kt1["gate_up"]
     alg = gu["weight_bytes"] + gu["x_bytes"] + gu["y_bytes"]
     achieved = alg / (gu_in_sweep_us * 1e-6) / 1e9
+    prof = profile_roofline()
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=load_traffic("gate_up_q4k_b1_traffic"),
                     kernel="gemv_kernel<Q4_K, B=1, bf16> (gate+up 62464x5120, one launch over both halves)",
                     algorithmic_bytes_per_launch=alg, avg_launch_us=round(gu_in_sweep_us, 2),
                     timing="sweep graph minus the same graph without the 52 gate+up launches, per launch "
                            "(HIP events, medians of 9 alternated replays)",
-                    avg_launch_us_back_to_back=gu["avg_us"])
+                    avg_launch_us_back_to_back=gu["avg_us"],
+                    read_ceiling_gbs=ceiling["gbs"], frac_of_read_ceiling=round(achieved / ceiling["gbs"], 4),
+                    profile=(dict(avg_launch_us=prof["avg_launch_us"], dispatches=prof["dispatches"],
+                                  achieved=round(alg / (prof["avg_launch_us"] * 1e-6) / 1e9, 1),
+                                  frac=round(alg / (prof["avg_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                  source="profiles/gemv_sweep52_kernel_trace.txt (rocprofv3 kernel trace, gate+up "
+                                         "dispatches that follow another GEMV)")
+                             if prof else None))
 
     c4 = None
     if not args.no_c4:
@@ -832,6 +1052,11 @@ def main():
         "batch1_all": {"chain_ms": round(res[1]["chain_ms"], 4), "graph_ms": round(res[1]["graph_ms"], 4),
                        "plain_ms": round(res[1]["plain_ms"], 4),
                        "graph_weight_gbs": round(weight_gbs(bytes3, res[1]["graph_ms"]), 1)},
+        "per_step_ms": {f"b{B}": v for B, v in per_step.items()},
+        "single_gemvs": singles,
+        "read_ceiling": ceiling,
+        "smi": {"before": smi_before, "after": smi_after},
+        "host": host,
         "verify_cost_staircase": stair,
         "gate_up_swiglu_epilogue_us": swiglu_us,
         "qkvg_6656_fused_us": fused_us,

@@ -210,6 +210,18 @@ int kq_gemv_multi(int type, int n, const void *const *w, const int64_t *rows, in
 int kq_dequant(int type, const void *w, int64_t rows, int64_t cols, float *out, int64_t ldo, void *stream);
 
 /*
+ * Measurement: read `bytes` (a multiple of 16) of device memory at p
+ * (16-byte aligned) once, with the GEMV's own loads (128-bit nontemporal
+ * buffer loads, many in flight) and no arithmetic.  Its rate is the
+ * achievable HBM read rate that the weight streaming is held against (a
+ * decode step costs its weight bytes: "Muse-Glimmer-30B (text decoder) -
+ * Apple Core AI", decode table and the paragraph after it).  `sink`: one
+ * device word, written only if the xor of all data equals a fixed value, so
+ * that the loads cannot be dropped.  bytes == 0 enqueues nothing.
+ */
+int kq_stream_read(const void *p, size_t bytes, uint32_t *sink, void *stream);
+
+/*
  * kq_gemv_multi with the work either side of the projections folded into the
  * launch ("Muse-Glimmer-30B (text decoder) - Apple Core AI", section "The
  * architecture, and what the port had to do about it"):

@@ -673,6 +673,20 @@ int kq_gemv_multi(int type, int n, const void* const* w, const int64_t* rows, in
   return gemv_impl(type, n, w, rows, cols, x, xtype, ldx, batch, y, ldy, ws, ws_bytes, stream);
 }
 
+int kq_stream_read(const void* p, size_t bytes, uint32_t* sink, void* stream) {
+  if (!p || !sink) return KQ_ERR_NULL;
+  if (!aligned(p, 16) || !aligned(sink, 4) || bytes % 16 != 0) return KQ_ERR_ALIGN;
+  if (bytes == 0) return KQ_OK;
+  int cus = 0;
+  if (current_device_cus(nullptr, &cus) != KQ_OK) return KQ_ERR_HIP;
+  // workgroups of 4 wavefronts per CU (KQ_READ_WG_PER_CU overrides, 1..32)
+  const char* e = getenv("KQ_READ_WG_PER_CU");
+  const int per_cu = e && atoi(e) >= 1 && atoi(e) <= 32 ? atoi(e) : 16;
+  if (launch_stream_read(p, bytes, sink, cus * per_cu, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KQ_ERR_HIP;
+  return KQ_OK;
+}
+
 int kq_dequant(int type, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldo, void* stream) {
   if (!sb_bytes(type)) return KQ_ERR_TYPE;
   if (!w || !out) return KQ_ERR_NULL;

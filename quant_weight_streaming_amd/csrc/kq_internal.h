@@ -135,6 +135,8 @@ hipError_t launch_dequant(int type, const void* w, int64_t rows, int64_t cols, f
                           hipStream_t s);
 hipError_t launch_gather(int type, const void* w, int64_t rows, int64_t cols, const int32_t* ids, int64_t n,
                          float* out, int64_t ldo, hipStream_t s);
+// Read `bytes` (a multiple of 16) from p once with the GEMV's loads (the achievable read rate).
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, int groups, hipStream_t s);
 // Zero n 32-bit words with a kernel (graph-capturable, unlike a memset node).
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t s);
 

@@ -31,7 +31,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_gemv_workspace_bytes", "kq_workspace_init",
            "kq_repacked_bytes", "kq_repack", "kq_gemv_q4k",
            "kq_gemv_q5k", "kq_gemv_q6k", "kq_gemv_multi", "kq_gemv_fused", "kq_gemv_fused_noalloc", "kq_dequant",
-           "kq_gather_rows",
+           "kq_gather_rows", "kq_stream_read",
            "kq_repack_swiglu",
            "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
            "kq_chain_query", "kq_chain_status", "kq_chain_destroy")
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32), ctypes.c_float,
                                             ctypes.c_float, vp]
         L.kq_gemv_fused_noalloc.restype = ci
+        L.kq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.kq_stream_read.restype = ci
         L.kq_dequant.argtypes = [ci, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ci
         L.kq_gather_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, vp]
@@ -264,6 +266,12 @@ def kq_gemv_fused_noalloc(qtype, ws, rows, cols: int, x: torch.Tensor, ys, epis=
     _check("kq_gemv_fused_noalloc",
            lib().kq_gemv_fused_noalloc(_type(qtype), n, W, R, cols, x.data_ptr(), _xtype(x), x.stride(0), x.shape[0],
                                        Y, LD, Y16, LD16, E, rms_eps, head_eps, _stream(stream)))
+
+
+def kq_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of `buf` once with the GEMV's loads (the achievable read rate)."""
+    _check("kq_stream_read", lib().kq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                                  sink.data_ptr(), _stream(stream)))
 
 
 def kq_dequant(qtype, w: torch.Tensor, rows: int, cols: int, out: torch.Tensor, stream=None) -> None:

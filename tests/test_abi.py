@@ -275,3 +275,12 @@ def test_workspace_bound_matches_layout():
     assert kq.KQ_WORKSPACE_BYTES == counters + slots + heads
     src = open(os.path.join(ROOT, "include", "kq.h")).read()
     assert re.search(r"#define KQ_WORKSPACE_BYTES (\d+)u", src).group(1) == str(kq.KQ_WORKSPACE_BYTES)
+
+
+def test_stream_read_rejects():
+    L = kq.lib()
+    assert L.kq_stream_read(None, 1024, A16, None) == 1
+    assert L.kq_stream_read(A16, 1024, None, None) == 1
+    assert L.kq_stream_read(A16 + 8, 1024, A16, None) == 3
+    assert L.kq_stream_read(A16, 1000, A16, None) == 3
+    assert L.kq_stream_read(A16, 0, A16, None) == 0          # nothing to read: nothing enqueued
