@@ -86,9 +86,16 @@ class Sweep:
         dev = "cuda:0"
         t0 = time.time()
         for layer, spec in (entries if entries is not None else synth.sweep(gate_up_type)):
+            parts = list(spec.parts) or [spec.rows]
+            if spec.types:       # a mixed-type projection: each part drawn and repacked in its own type
+                reps = [kq.repack(t, synth.gen_weights(t, r, spec.cols, synth.seed_of(cfg, layer, spec.name, i),
+                                                       device=dev), r, spec.cols)
+                        for i, (t, r) in enumerate(zip(spec.part_types(), parts))]
+                self.weight_bytes += spec.weight_bytes()
+                self.entries.append((layer, spec, reps, parts))
+                continue
             g = synth.gen_weights(spec.qtype, spec.rows, spec.cols, synth.seed_of(cfg, layer, spec.name),
                                   device=dev, merge_frac=merge if spec.qtype == "q4k" else 0.0)
-            parts = list(spec.parts) or [spec.rows]
             starts = [0]
             for r in parts:
                 starts.append(starts[-1] + r)
@@ -123,6 +130,19 @@ class Sweep:
         for i, (layer, spec, reps, parts) in enumerate(self.entries):
             x, ys = self.x[B][i], self.y[B][i]
             t = self.kq.TYPE_ID[spec.qtype]
+            if spec.types:       # mixed types: one multi-projection launch per type
+                pt = spec.part_types()
+                for qt in dict.fromkeys(pt):
+                    idx = [k for k, u in enumerate(pt) if u == qt]
+                    n = len(idx)
+                    W = (ctypes.c_void_p * n)(*[reps[k].data_ptr() for k in idx])
+                    R = (ctypes.c_int64 * n)(*[parts[k] for k in idx])
+                    Y = (ctypes.c_void_p * n)(*[ys[k].data_ptr() for k in idx])
+                    LD = (ctypes.c_int64 * n)(*[ys[k].stride(0) for k in idx])
+                    self._keep += [W, R, Y, LD]
+                    out.append((L.kq_gemv_multi, (self.kq.TYPE_ID[qt], n, W, R, spec.cols, x.data_ptr(), 1,
+                                                   x.stride(0), B, Y, LD, wsp, wsb, stream), spec.name))
+                continue
             if len(parts) > 1:
                 n = len(parts)
                 W = (ctypes.c_void_p * n)(*[w.data_ptr() for w in reps])
@@ -162,7 +182,7 @@ def time_chain(sw: Sweep, B: int, steps: int, warmup: int, per_step: dict = None
     """The whole sweep as one chain launch (step j+1 reads its x only after step j's y is complete);
     returns ms per step (per-step times in per_step['chain'] if given)."""
     torch, kq = sw.torch, sw.kq
-    chain = kq.Chain([(spec.qtype, reps, parts, spec.cols, sw.x[B][i], sw.y[B][i])
+    chain = kq.Chain([(spec.part_types() if spec.types else spec.qtype, reps, parts, spec.cols, sw.x[B][i], sw.y[B][i])
                       for i, (layer, spec, reps, parts) in enumerate(sw.entries)], B)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -460,8 +480,9 @@ def kernel_times(sw: Sweep, B: int, reps: int = 3):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / (n_rep * len(calls))
         del g
-        spec = next(s for _, s, _, _ in sw.entries if s.name == name)
-        wb = spec.rows * spec.cols // 256 * sw.synth.SB_BYTES[spec.qtype]
+        specs = [s for _, s, _, _ in sw.entries if s.name == name]
+        spec = specs[0]
+        wb = sum(s.weight_bytes() for s in specs) / len(specs)
         out[name] = dict(qtype=spec.qtype, rows=spec.rows, cols=spec.cols, launches=n_rep * len(calls),
                          avg_us=round(ms * 1e3, 2), weight_gbs=round(weight_gbs(wb, ms), 1),
                          weight_bytes=wb, x_bytes=B * spec.cols * 2, y_bytes=B * spec.rows * 4)
@@ -844,6 +865,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-c4", action="store_true", help="skip the Q5_K / merged-sub-block sweep")
     ap.add_argument("--no-p4", action="store_true", help="skip the 6656-hidden decoder's sweep")
+    ap.add_argument("--no-q4km", action="store_true", help="skip the Q4_K_M-style mixed-type sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--profile-kernel", type=int, default=0)
     ap.add_argument("--profile-batch", type=int, default=1, help="batch of the --profile-kernel launches")
@@ -1016,6 +1038,26 @@ def main():
         p4["embedding_gather_us"] = time_gather(synth.VOCAB_P4, synth.HIDDEN_P4, (1, 8))
         log(f"[bench] p4 embedding gather: {p4['embedding_gather_us']}")
 
+    # the Q4_K_M-style type mix: mixed-type QKV steps (Q4_K q/k, Q6_K v) and down alternating Q6_K / Q4_K
+    q4km = None
+    if not args.no_q4km:
+        torch.cuda.empty_cache()
+        swm = Sweep("q4km", "q4k", (1, 8), 0.0, 0.0, entries=synth.sweep_q4km())
+        q4km = {"workload": "52 x {QKV 4608x5120 (q, k Q4_K; v Q6_K; one chain step), O Q4_K 5120x4096, gate+up "
+                            "Q4_K 62464x5120, down 5120x31232 (Q6_K even layers, Q4_K odd)} + head Q6_K 131072x5120",
+                "weight_bytes": swm.weight_bytes}
+        for B in (1, 8):
+            plain, graph = time_sweep(swm, B, max(3, args.steps // 2), args.warmup)
+            chain = time_chain(swm, B, max(3, args.steps // 2), args.warmup)
+            best = min(graph, chain)
+            q4km[f"b{B}"] = dict(graph_ms=round(graph, 4), chain_ms=round(chain, 4), plain_ms=round(plain, 4),
+                                 weight_gbs=round(weight_gbs(swm.weight_bytes, best), 1),
+                                 pct_of_hbm_peak=round(100 * weight_gbs(swm.weight_bytes, best) / HBM_PEAK_GBS, 2),
+                                 tok_s=round(tok_s(best, B), 1))
+            log(f"[bench] q4km B={B}: graph {graph:.3f} ms, chain {chain:.3f} ms "
+                f"({swm.weight_bytes / best / 1e6:.0f} GB/s)")
+        del swm
+
     # the sweep's time per token: the faster of the two ways of running the same dependent sequence
     def best(r):
         return ("chain", r["chain_ms"]) if r["chain_ms"] < r["graph_ms"] else ("graph", r["graph_ms"])
@@ -1065,6 +1107,7 @@ def main():
         "kernels_b8": kt8,
         "c4_q5k_merged": c4,
         "hidden6656_sweep": p4,
+        "q4km_mixed_sweep": q4km,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_hash": kernel_source_hash(),

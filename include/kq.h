@@ -340,6 +340,15 @@ int kq_gather_rows(int type, const void *w, int64_t rows, int64_t cols, const in
  *
  * kq_chain_step describes one step exactly as kq_gemv_multi takes it (n = 1 for
  * a single matrix).  All steps share xtype and batch.
+ *
+ * Mixed weight types: the segments of one step may have different K-quant
+ * types (`types`), as in the mixed-type GGUF builds (the SGLang Day-0 post's
+ * GGUF checkpoints, "Q4KM" and "Q4K-Dynamic"; e.g. Q4_K q/k rows with Q6_K v
+ * rows in one QKV projection).  The step still reads x once per workgroup and
+ * runs in the same launch: its segments of each type form one sub-step, and
+ * the sub-steps after the first run without waiting for it (they share x and
+ * write other outputs).  Each sub-step's results are bitwise those of the
+ * kq_gemv_fused call over its segments with the chain's workgroup shape.
  */
 typedef struct kq_chain_step {
   int32_t type;                   /* KQ_Q4_K / KQ_Q5_K / KQ_Q6_K */
@@ -358,6 +367,7 @@ typedef struct kq_chain_step {
   float rms_eps;                  /* > 0: weight-less RMSNorm of x first, as kq_gemv_fused; 0: none */
   float head_eps;                 /* epsilon of KQ_EPI_HEADNORM segments, as kq_gemv_fused */
   int32_t reserved;               /* set to 0 */
+  int32_t types[KQ_MAX_PROJ];     /* segment i's weight type; 0 = `type` (a zeroed array: one type) */
 } kq_chain_step;
 
 typedef struct kq_chain kq_chain;

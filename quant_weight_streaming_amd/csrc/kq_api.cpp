@@ -463,6 +463,63 @@ static hipError_t launch_chain(int xtype, int rows, const ChainArgs& c, int nw, 
   }
 }
 
+// One planned unit of a chain: a step, or the segments of one weight type of a
+// step with mixed types.  `wait`: the first sub-step of a step waits at the step
+// barrier; the others share its x and run without waiting.
+struct SubStep {
+  int type = 0, n = 0;
+  int64_t cols = 0, ldx = 0;
+  const void* x = nullptr;
+  const void* w[KQ_MAX_PROJ] = {};
+  int64_t rows[KQ_MAX_PROJ] = {};
+  float* y[KQ_MAX_PROJ] = {};
+  int64_t ldy[KQ_MAX_PROJ] = {};
+  void* y16[KQ_MAX_PROJ] = {};
+  int64_t ldy16[KQ_MAX_PROJ] = {};
+  uint32_t epi = 0;
+  float rms_eps = 0.0f, head_eps = 0.0f;
+  bool wait = true;
+};
+
+// Split a chain step into one sub-step per weight type (segment i's type is
+// types[i], or the step's type where that is 0), in the order the types first
+// appear; each sub-step keeps its segments' order and epilogue codes.
+static int split_by_type(const kq_chain_step& st, std::vector<SubStep>& out) {
+  if (!valid_epilogue(st.n, (uint32_t)st.epilogue)) return KQ_ERR_TYPE;
+  int seg_type[KQ_MAX_PROJ], order[3], nt = 0;
+  for (int i = 0; i < st.n; ++i) {
+    seg_type[i] = st.types[i] ? st.types[i] : st.type;
+    if (!sb_bytes(seg_type[i])) return KQ_ERR_TYPE;
+    bool seen = false;
+    for (int k = 0; k < nt; ++k) seen |= order[k] == seg_type[i];
+    if (!seen) order[nt++] = seg_type[i];
+  }
+  const bool swiglu = (uint32_t)st.epilogue == (uint32_t)KQ_EPI_SWIGLU;
+  for (int g = 0; g < nt; ++g) {
+    SubStep u;
+    u.type = order[g];
+    u.cols = st.cols;
+    u.x = st.x;
+    u.ldx = st.ldx;
+    u.rms_eps = st.rms_eps;
+    u.head_eps = st.head_eps;
+    u.wait = g == 0;
+    for (int i = 0; i < st.n; ++i) {
+      if (seg_type[i] != u.type) continue;
+      const int k = u.n++;
+      u.w[k] = st.w[i];
+      u.rows[k] = st.rows[i];
+      u.y[k] = st.y[i];
+      u.ldy[k] = st.ldy[i];
+      u.y16[k] = st.y16[i];
+      u.ldy16[k] = st.ldy16[i];
+      u.epi |= swiglu ? (uint32_t)KQ_EPI_SWIGLU : (((uint32_t)st.epilogue >> (4 * i)) & 15u) << (4 * k);
+    }
+    out.push_back(u);
+  }
+  return KQ_OK;
+}
+
 // Polls before a chain step's wait gives up (KQ_CHAIN_SPIN overrides; about a
 // second at the default).
 static uint32_t chain_spin() {
@@ -484,7 +541,8 @@ struct kq_chain {
   size_t lds = 0;
   kq::ChainArgs args{};
   void* mem = nullptr;          // one allocation: step table, control words, the steps' workspace
-  uint32_t* counters = nullptr; // the workspace's counter block (reset after a run whose wait gave up)
+  uint32_t* counters = nullptr; // the workspace (its counter blocks are reset after a run whose wait gave up)
+  size_t ws_bytes = 0;
   uint32_t* flag = nullptr;     // pinned host word, set by the device when a wait gives up
 };
 
@@ -722,18 +780,28 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   if (xtype != KQ_X_F32 && xtype != KQ_X_BF16) return KQ_ERR_TYPE;
   if (batch < 1 || batch > (xtype == KQ_X_F32 ? KQ_MAX_BATCH_F32 : KQ_MAX_BATCH)) return KQ_ERR_BATCH;
   const int64_t esize = xtype == KQ_X_F32 ? 4 : 2;
+  // A step whose segments have different weight types becomes one sub-step per type (the segments of
+  // that type, in order, with their epilogue codes): the sub-steps share the step's x and write
+  // different outputs, so the later ones run without waiting for the earlier ones.
+  std::vector<SubStep> subs;
   for (int j = 0; j < n_steps; ++j) {
     const kq_chain_step& st = steps[j];
-    const int rc = validate(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy);
+    if (st.n < 1 || st.n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
+    int rc = split_by_type(st, subs);
     if (rc != KQ_OK) return rc;
-    if (!valid_epilogue(st.n, (uint32_t)st.epilogue)) return KQ_ERR_TYPE;
-    if (!valid_rms_eps(st.rms_eps)) return KQ_ERR_SHAPE;
-    const int hrc = check_heads(st.n, st.rows, (uint32_t)st.epilogue, st.head_eps);
-    if (hrc != KQ_OK) return hrc;
-    const int yrc = check_y16(st.n, st.rows, st.y16, st.ldy16);
-    if (yrc != KQ_OK) return yrc;
-    if (((int64_t)(batch - 1) * st.ldx + st.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
   }
+  for (const SubStep& u : subs) {
+    const int rc = validate(u.type, u.n, u.w, u.rows, u.cols, u.x, xtype, u.ldx, batch, u.y, u.ldy);
+    if (rc != KQ_OK) return rc;
+    if (!valid_epilogue(u.n, u.epi)) return KQ_ERR_TYPE;
+    if (!valid_rms_eps(u.rms_eps)) return KQ_ERR_SHAPE;
+    const int hrc = check_heads(u.n, u.rows, u.epi, u.head_eps);
+    if (hrc != KQ_OK) return hrc;
+    const int yrc = check_y16(u.n, u.rows, u.y16, u.ldy16);
+    if (yrc != KQ_OK) return yrc;
+    if (((int64_t)(batch - 1) * u.ldx + u.cols) * esize >= ((int64_t)1 << 31)) return KQ_ERR_RANGE;
+  }
+  const int n_sub = (int)subs.size();
   int dev = 0, cus = 0;
   if (current_device_cus(&dev, &cus) != KQ_OK) return KQ_ERR_HIP;
 
@@ -741,16 +809,15 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   // of 8), fewer if the occupancy of the chain kernel says so.
   kq_chain* c = new (std::nothrow) kq_chain;
   if (!c) return KQ_ERR_NOMEM;
-  std::vector<Plan> plans(n_steps);
+  std::vector<Plan> plans(n_sub);
   const int srows = xtype == KQ_X_F32 ? 2 * batch : batch;
   int nw = chain_wg_waves();
   auto plan_all = [&](int64_t max_grid, size_t* lds) {
     *lds = 0;
-    for (int j = 0; j < n_steps; ++j) {
-      const kq_chain_step& st = steps[j];
-      int rc = plan_gemv(st.type, st.n, st.w, st.rows, st.cols, st.x, xtype, st.ldx, batch, st.y, st.ldy, st.y16,
-                         st.ldy16, cus,
-                         max_grid, nw, false, (uint32_t)st.epilogue, st.rms_eps, st.head_eps, &plans[j]);
+    for (int j = 0; j < n_sub; ++j) {
+      const SubStep& u = subs[j];
+      int rc = plan_gemv(u.type, u.n, u.w, u.rows, u.cols, u.x, xtype, u.ldx, batch, u.y, u.ldy, u.y16, u.ldy16,
+                         cus, max_grid, nw, false, u.epi, u.rms_eps, u.head_eps, &plans[j]);
       if (rc == KQ_ERR_RANGE && nw == 8 && srows <= 8) {   // every step then runs with 4-wavefront workgroups
         nw = 4;
         return (int)KQ_ERR_RANGE;
@@ -781,12 +848,23 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     return rc;
   }
 
-  const size_t steps_bytes = round_up((size_t)n_steps * sizeof(ChainStep), 256);
-  // control words: arrive[n_steps][groups], done[n_steps], epoch, error
-  const size_t ctl_bytes = round_up(((size_t)n_steps * (groups + 1) + 2) * sizeof(uint32_t), 256);
-  // the steps run one after another and share one workspace of the largest step's size
+  const size_t steps_bytes = round_up((size_t)n_sub * sizeof(ChainStep), 256);
+  // control words: arrive[n_sub][groups], done[n_sub], epoch, error
+  const size_t ctl_bytes = round_up(((size_t)n_sub * (groups + 1) + 2) * sizeof(uint32_t), 256);
+  // Steps run one after another and share one workspace; the sub-steps of one step may run at the
+  // same time, so each has its own region of it: the workspace is the largest step's sum of regions.
+  std::vector<size_t> ws_off(n_sub);
   size_t ws_bytes = kCounterBytes;
-  for (int j = 0; j < n_steps; ++j) ws_bytes = plans[j].ws_bytes > ws_bytes ? plans[j].ws_bytes : ws_bytes;
+  for (int j = 0; j < n_sub;) {
+    size_t off = 0;
+    int k = j;
+    for (; k < n_sub && (k == j || !subs[k].wait); ++k) {
+      ws_off[k] = off;
+      off += round_up(plans[k].ws_bytes, 256);
+    }
+    ws_bytes = off > ws_bytes ? off : ws_bytes;
+    j = k;
+  }
   const size_t total = steps_bytes + ctl_bytes + ws_bytes;
   if (hipMalloc(&c->mem, total) != hipSuccess) {
     delete c;
@@ -804,17 +882,18 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   ChainStep* d_steps = reinterpret_cast<ChainStep*>(base);
   uint32_t* d_ctl = reinterpret_cast<uint32_t*>(base + steps_bytes);
   uint8_t* d_ws = base + steps_bytes + ctl_bytes;
-  std::vector<ChainStep> h(n_steps);
-  for (int j = 0; j < n_steps; ++j) {
-    assign_workspace(plans[j], d_ws);
+  std::vector<ChainStep> h(n_sub);
+  for (int j = 0; j < n_sub; ++j) {
+    assign_workspace(plans[j], d_ws + ws_off[j]);
     h[j].a = plans[j].a;
-    h[j].type = steps[j].type;
+    h[j].type = subs[j].type;
     h[j].grid = (int32_t)plans[j].grid;
+    h[j].wait = subs[j].wait ? 1 : 0;
   }
   rc = KQ_OK;
   if (hipHostGetDevicePointer(reinterpret_cast<void**>(&d_flag), c->flag, 0) != hipSuccess ||
-      hipMemcpy(d_steps, h.data(), (size_t)n_steps * sizeof(ChainStep), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_ws, 0, kCounterBytes) != hipSuccess ||
+      hipMemcpy(d_steps, h.data(), (size_t)n_sub * sizeof(ChainStep), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_ws, 0, ws_bytes) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess)
     rc = KQ_ERR_HIP;
   if (rc != KQ_OK) {
@@ -831,10 +910,11 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   c->grid = (int)groups;
   c->lds = lds;
   c->counters = reinterpret_cast<uint32_t*>(d_ws);
+  c->ws_bytes = ws_bytes;
   c->args.steps = d_steps;
-  c->args.n_steps = n_steps;
-  uint32_t* d_done = d_ctl + (size_t)n_steps * groups;
-  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_steps, d_done + n_steps + 1, d_flag, (uint32_t)groups, 0};
+  c->args.n_steps = n_sub;
+  uint32_t* d_done = d_ctl + (size_t)n_sub * groups;
+  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_sub, d_done + n_sub + 1, d_flag, (uint32_t)groups, 0};
   *out = c;
   return KQ_OK;
 }
@@ -872,7 +952,7 @@ int kq_chain_status(kq_chain* c) {
   if (rc == KQ_OK && (err || *reinterpret_cast<volatile uint32_t*>(c->flag))) {
     // reset: the split-tile and head counters (a workgroup that stopped waiting may have entered a
     // step early and left them non-zero), the device error word and the host flag
-    rc = hipMemset(c->counters, 0, kCounterBytes) == hipSuccess &&
+    rc = hipMemset(c->counters, 0, c->ws_bytes) == hipSuccess &&
                  hipMemset(c->args.ctl.error, 0, sizeof(err)) == hipSuccess && hipDeviceSynchronize() == hipSuccess
              ? KQ_ERR_TIMEOUT
              : KQ_ERR_HIP;

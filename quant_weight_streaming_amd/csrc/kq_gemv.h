@@ -1262,7 +1262,9 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
   for (int j = 0; j < c.n_steps; ++j) {
     ConstChainStep& st = steps[j];
     const int g = st.grid;
-    bool waited = false;
+    // a further weight type of the same step reads the same x as the sub-step
+    // before it and writes other outputs: no wait
+    bool waited = st.wait == 0;
     // the step's logical blocks, as a single launch numbers them, grid-stride
     // over the resident workgroups (the launch is a multiple of 8 workgroups, so
     // every logical block keeps the XCD it would have had); the first block
@@ -1276,7 +1278,8 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
       else
         waited |= gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
     }
-    if (blockIdx.x == 0 && j > 0 && !waited) chain_collect(c.ctl, j - 1, tag);   // the collector never skips a step
+    // the collector never skips a step that waits
+    if (blockIdx.x == 0 && j > 0 && st.wait && !waited) chain_collect(c.ctl, j - 1, tag);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's y / partial stores are done
     __syncthreads();
     if (threadIdx.x == 0) store_coherent(c.ctl.arrive + (size_t)j * c.ctl.groups + blockIdx.x, tag);

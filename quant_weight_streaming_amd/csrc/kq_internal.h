@@ -76,12 +76,16 @@ struct ChainCtl {
   uint32_t spin;       // polls before a wait gives up
 };
 
-// One step of a chain, device-resident: its launch arguments, weight type and
-// logical workgroups (a multiple of 8, at most the launch's).
+// One step of a chain, device-resident: its launch arguments, weight type,
+// logical workgroups (a multiple of 8, at most the launch's), and whether it
+// waits for the previous step (0: a further weight type of the same step, which
+// shares its x and writes other outputs).
 struct ChainStep {
   GemvArgs a;
   int32_t type;
   int32_t grid;
+  int32_t wait;
+  int32_t pad;
 };
 
 struct ChainArgs {

@@ -44,7 +44,8 @@ class ChainStep(ctypes.Structure):
                 ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("y16", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy16", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("epilogue", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("head_eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("head_eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("types", ctypes.c_int32 * KQ_MAX_PROJ)]
 
 
 class KQError(RuntimeError):
@@ -301,8 +302,9 @@ def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tens
 
 
 def kq_chain_create(steps, xtype: int, batch: int) -> int:
-    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps[, head_eps[, y16s]]]]) as kq_gemv_multi
-    and kq_gemv_fused take them, the epilogue packed four bits per segment; returns the handle."""
+    """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps[, head_eps[, y16s[, types]]]]]) as
+    kq_gemv_multi and kq_gemv_fused take them, the epilogue packed four bits per segment; qtype may be a list
+    of per-segment types (a mixed-type step), or `types` gives them; returns the handle."""
     arr = (ChainStep * len(steps))()
     for st, step in zip(arr, steps):
         qtype, ws, rows, cols, x, ys = step[:6]
@@ -310,10 +312,16 @@ def kq_chain_create(steps, xtype: int, batch: int) -> int:
         st.rms_eps = step[7] if len(step) > 7 else 0.0
         st.head_eps = step[8] if len(step) > 8 else 0.0
         y16s = step[9] if len(step) > 9 else None
+        types = step[10] if len(step) > 10 else None
+        if isinstance(qtype, (list, tuple)):
+            qtype, types = qtype[0], qtype
         n = len(ws)
-        if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ:
-            raise ValueError("ws, rows and ys must have the same length, at most KQ_MAX_PROJ")
+        if len(rows) != n or len(ys) != n or n > KQ_MAX_PROJ or (types is not None and len(types) != n):
+            raise ValueError("ws, rows, ys (and types) must have the same length, at most KQ_MAX_PROJ")
         st.type, st.n, st.cols = _type(qtype), n, cols
+        if types is not None:
+            for i, t in enumerate(types):
+                st.types[i] = _type(t)
         for i in range(n):
             st.w[i], st.rows[i], st.y[i], st.ldy[i] = ws[i].data_ptr(), rows[i], ys[i].data_ptr(), ys[i].stride(0)
             if y16s is not None and y16s[i] is not None:

@@ -214,6 +214,15 @@ class Gemv:
     rows: int
     cols: int
     parts: Sequence[int] = ()       # row split for the multi-projection call (empty = one matrix)
+    types: Sequence[str] = ()       # per-part weight types of a mixed-type projection (empty = qtype for all)
+
+    def part_types(self):
+        n = len(self.parts) or 1
+        return list(self.types) if self.types else [self.qtype] * n
+
+    def weight_bytes(self) -> int:
+        parts = list(self.parts) or [self.rows]
+        return sum(r * self.cols // QK * SB_BYTES[t] for r, t in zip(parts, self.part_types()))
 
 
 HIDDEN, INTER, VOCAB = 5120, 31232, 131072
@@ -237,6 +246,28 @@ def sweep(gate_up_type: str = "q4k"):
 
 def sweep_bytes(gate_up_type: str = "q4k") -> int:
     return sum(g.rows * g.cols // QK * SB_BYTES[g.qtype] for _, g in sweep(gate_up_type))
+
+
+# A mixed-type build in the manner of the GGUF "Q4_K_M" recipe (the SGLang Day-0 post's GGUF checkpoints,
+# "Q4KM"; the daily.dev summary's "k-quant" build): most tensors Q4_K, the attention V rows and half of
+# the down projections kept at Q6_K.  The exact per-tensor recipe is not on the pages; this reading puts V
+# at Q6_K in every layer (so every QKV projection mixes two types in one launch) and down at Q6_K in the
+# even layers and Q4_K in the odd ones.
+QKV_Q4KM = Gemv("qkv", "q4k", 4608, HIDDEN, (4096, 256, 256), ("q4k", "q4k", "q6k"))
+DOWN_Q4K = Gemv("down", "q4k", HIDDEN, INTER)
+
+
+def sweep_q4km():
+    """The 52-layer sweep with the Q4_K_M-style type mix, in launch order."""
+    out = []
+    for layer in range(N_LAYERS):
+        out += [(layer, QKV_Q4KM), (layer, O_PROJ), (layer, GATE_UP), (layer, DOWN if layer % 2 == 0 else DOWN_Q4K)]
+    out.append((N_LAYERS, HEAD))
+    return out
+
+
+def sweep_q4km_bytes() -> int:
+    return sum(g.weight_bytes() for _, g in sweep_q4km())
 
 
 # The text decoder described on the "Muse-Glimmer-30B (text decoder) - Apple Core AI" card, section
