@@ -108,6 +108,21 @@ static int aligned_tiles() {
   return (x >= 1 && x <= 8) ? x : 0;
 }
 
+// Units per CU below which a launch gives each workgroup whole tiles (KQ_WHOLE_TILES_BELOW; 0 = never).
+static int64_t whole_tiles_below() {
+  const char* e = getenv("KQ_WHOLE_TILES_BELOW");
+  const long x = e ? atol(e) : 0;
+  return (x >= 0 && x <= 4096) ? x : 0;
+}
+
+// Extra column windows the planner may add beyond the fewest that fit (KQ_WIN_SEARCH, 0..64; 3 measured
+// best on the batch-8 sweep: each extra window adds a piece to every tile's hand-off).
+static int64_t window_search() {
+  const char* e = getenv("KQ_WIN_SEARCH");
+  const long x = e ? atol(e) : 3;
+  return (x >= 0 && x <= 64) ? x : 3;
+}
+
 // Batches from which column windows are used (KQ_WINDOWS_FROM overrides; 9 = never).
 static int windows_from_batch() {
   const char* e = getenv("KQ_WINDOWS_FROM");
@@ -116,13 +131,13 @@ static int windows_from_batch() {
 }
 
 // Batches (bf16 activations) from which the matrix cores compute the products
-// (KQ_MATRIX_CORES_FROM, 2..9; 9 = never, every batch on the dot2 VALU path).
+// (KQ_MATRIX_CORES_FROM, 1..9; 9 = never, every batch on the dot2 VALU path).
 // The default, 3, is where the dot2 path becomes VALU-issue bound: at batch 2
 // it is as fast or faster on every sweep shape, from batch 3 on it is slower.
 static int matrix_cores_from() {
   const char* e = getenv("KQ_MATRIX_CORES_FROM");
   const int x = e ? atoi(e) : 0;
-  return (x >= 2 && x <= 9) ? x : 3;
+  return (x >= 1 && x <= 9) ? x : 3;
 }
 
 // Wavefronts per workgroup of a single launch (KQ_WG_WAVES = 4 or 8
@@ -268,24 +283,52 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   a.n_tiles = (int32_t)tiles;
   a.tiles_per_wg = 0;
   const int64_t n_win = (n_cols + max_cols - 1) / max_cols;
-  const int forced_r = aligned_tiles();
+  // small steps (fewer units than `whole_tiles_below()` per CU): one whole tile per workgroup, so no
+  // tile is split between workgroups
+  const int64_t small = whole_tiles_below();
+  const int forced_r = n_units < (int64_t)cus * small && n_win == 1 ? 1 : aligned_tiles();
   if (((srows >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
       n_win * tiles <= 2 * (int64_t)kMaxGroups) {
     int64_t g_target = (int64_t)cus * wpc / nw;
     if (g_target < 1) g_target = 1;
     if (g_target > max_groups) g_target = max_groups;
-    int64_t g_win = g_target / n_win > 0 ? g_target / n_win : 1;
-    int64_t r = forced_r > 0 ? forced_r : (tiles + g_win - 1) / g_win;
-    // at most nw tiles per workgroup (a wavefront's run then touches at most two
-    // tiles) unless that needs more than max_groups workgroups
-    if (r > nw && ((tiles + nw - 1) / nw * n_win + 7) / 8 * 8 <= max_groups) r = nw;
-    g_win = (tiles + r - 1) / r;
-    const int64_t wgrid = (n_win * g_win + 7) / 8 * 8;
+    int64_t nwin = n_win, r = 0, g_win = 0;
+    if (forced_r > 0) {
+      r = forced_r;
+      g_win = (tiles + r - 1) / r;
+    } else {
+      // the window count (at least n_win, so each window fits the staging budget) and whole tiles per
+      // workgroup (at most nw, so a wavefront's run touches at most two tiles) with the least work per
+      // CU: rounds of resident workgroups x the units of the largest workgroup; ties go to fewer
+      // workgroups, then to fewer windows (fewer pieces per tile to hand over)
+      int64_t best = -1, best_groups = 0;
+      for (int64_t nwc = n_win; nwc <= n_win + window_search() && nwc <= n_cols; ++nwc) {
+        if (nwc * tiles > 2 * (int64_t)kMaxGroups) break;
+        const int64_t cols_w = (n_cols + nwc - 1) / nwc;
+        for (int64_t rc = 1; rc <= nw; ++rc) {
+          const int64_t gw = (tiles + rc - 1) / rc, groups = nwc * gw;
+          if ((groups + 7) / 8 * 8 > max_groups) continue;
+          const int64_t span = (groups + g_target - 1) / g_target * rc * cols_w;
+          if (best < 0 || span < best || (span == best && groups < best_groups)) {
+            best = span;
+            best_groups = groups;
+            nwin = nwc;
+            r = rc;
+            g_win = gw;
+          }
+        }
+      }
+      if (best < 0) {   // no plan within max_groups: the widest tiles per workgroup
+        r = (tiles + (max_groups / 8 * 8) / n_win - 1) / ((max_groups / 8 * 8) / n_win);
+        g_win = (tiles + r - 1) / r;
+      }
+    }
+    const int64_t wgrid = (nwin * g_win + 7) / 8 * 8;
     if (wgrid <= max_groups) {
       even_ok = true;
-      a.n_win = (int32_t)n_win;
-      a.win_base = (int32_t)(n_cols / n_win);
-      a.win_extra = (int32_t)(n_cols % n_win);
+      a.n_win = (int32_t)nwin;
+      a.win_base = (int32_t)(n_cols / nwin);
+      a.win_extra = (int32_t)(n_cols % nwin);
       a.wg_per_win = (int32_t)g_win;
       a.tiles_per_wg = (int32_t)r;
       tcols = a.win_base + (a.win_extra ? 1 : 0);

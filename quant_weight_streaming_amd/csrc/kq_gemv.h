@@ -39,6 +39,12 @@
 #ifndef KQ_DEPTH
 #define KQ_DEPTH 2
 #endif
+#ifndef KQ_EXP_DUAL
+#define KQ_EXP_DUAL 0
+#endif
+#ifndef KQ_EXP_NOSB
+#define KQ_EXP_NOSB 0
+#endif
 
 namespace kq {
 
@@ -273,6 +279,17 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         for (int v = 0; v < NV; ++v) xn[v] = xl[v];
         if constexpr (MINS) tn = Tc[gn * B + bn];
       }
+#if KQ_EXP_DUAL
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        s0 = dot2_bf16(pr[4 * v + 0], xc[v].x, s0);
+        s1 = dot2_bf16(pr[4 * v + 1], xc[v].y, s1);
+        s0 = dot2_bf16(pr[4 * v + 2], xc[v].z, s0);
+        s1 = dot2_bf16(pr[4 * v + 3], xc[v].w, s1);
+      }
+      const float s = s0 + s1;
+#else
       float s = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -281,12 +298,17 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         s = dot2_bf16(pr[4 * v + 2], xc[v].z, s);
         s = dot2_bf16(pr[4 * v + 3], xc[v].w, s);
       }
+#endif
       acc[b] = __builtin_fmaf(ca[g], s, acc[b]);
       if constexpr (MINS) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
 #pragma unroll
       for (int v = 0; v < NV; ++v) xc[v] = xn[v];
       tc = tn;
+#if !KQ_EXP_NOSB
       __builtin_amdgcn_sched_barrier(0);
+#else
+      if (B > 1) __builtin_amdgcn_sched_barrier(0);
+#endif
     }
   }
 }
@@ -1313,13 +1335,10 @@ static hipError_t launch_wide(const GemvArgs& a, int grid, size_t lds, hipStream
   return hipGetLastError();
 }
 
-// The matrix-core variant exists from 2 staged rows.
+// Both paths exist at every batch.
 template <int QT, int B, bool XF32>
 static hipError_t launch_one(const GemvArgs& a, int nw, bool mf, int grid, size_t lds, hipStream_t s) {
-  if constexpr (B >= 2) {
-    if (mf) return launch_nw<QT, B, XF32, true>(a, nw, grid, lds, s);
-  }
-  if (mf) return hipErrorInvalidValue;
+  if (mf) return launch_nw<QT, B, XF32, true>(a, nw, grid, lds, s);
   return launch_nw<QT, B, XF32, false>(a, nw, grid, lds, s);
 }
 
@@ -1387,10 +1406,7 @@ static hipError_t launch_chain_nw(const ChainArgs& c, int nw, int grid, size_t l
 // activations) and one activation type.
 template <int B, bool XF32>
 hipError_t launch_chain_b(const ChainArgs& c, int nw, bool mf, int grid, size_t lds, hipStream_t s, int* occupancy) {
-  if constexpr (B >= 2) {
-    if (mf) return launch_chain_nw<B, XF32, true>(c, nw, grid, lds, s, occupancy);
-  }
-  if (mf) return hipErrorInvalidValue;
+  if (mf) return launch_chain_nw<B, XF32, true>(c, nw, grid, lds, s, occupancy);
   return launch_chain_nw<B, XF32, false>(c, nw, grid, lds, s, occupancy);
 }
 
