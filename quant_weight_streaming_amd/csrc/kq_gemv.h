@@ -39,12 +39,7 @@
 #ifndef KQ_DEPTH
 #define KQ_DEPTH 2
 #endif
-#ifndef KQ_EXP_DUAL
-#define KQ_EXP_DUAL 0
-#endif
-#ifndef KQ_EXP_NOSB
-#define KQ_EXP_NOSB 0
-#endif
+
 
 namespace kq {
 
@@ -279,17 +274,6 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         for (int v = 0; v < NV; ++v) xn[v] = xl[v];
         if constexpr (MINS) tn = Tc[gn * B + bn];
       }
-#if KQ_EXP_DUAL
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        s0 = dot2_bf16(pr[4 * v + 0], xc[v].x, s0);
-        s1 = dot2_bf16(pr[4 * v + 1], xc[v].y, s1);
-        s0 = dot2_bf16(pr[4 * v + 2], xc[v].z, s0);
-        s1 = dot2_bf16(pr[4 * v + 3], xc[v].w, s1);
-      }
-      const float s = s0 + s1;
-#else
       float s = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -298,17 +282,12 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
         s = dot2_bf16(pr[4 * v + 2], xc[v].z, s);
         s = dot2_bf16(pr[4 * v + 3], xc[v].w, s);
       }
-#endif
       acc[b] = __builtin_fmaf(ca[g], s, acc[b]);
       if constexpr (MINS) acc[b] = __builtin_fmaf(-cm[g], tc, acc[b]);
 #pragma unroll
       for (int v = 0; v < NV; ++v) xc[v] = xn[v];
       tc = tn;
-#if !KQ_EXP_NOSB
       __builtin_amdgcn_sched_barrier(0);
-#else
-      if (B > 1) __builtin_amdgcn_sched_barrier(0);
-#endif
     }
   }
 }
