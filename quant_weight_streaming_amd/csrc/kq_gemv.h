@@ -3,10 +3,12 @@
 // Work decomposition.  A "unit" is one tile column: 64 rows (lane == row) x one
 // 256-weight super-block column, 9 / 11 / 13 KiB of weights read as coalesced
 // 1 KiB wavefront loads.  Units are ordered tile-major (all columns of tile 0,
-// then tile 1, ...).  By default each wavefront takes a contiguous run of `upw`
-// units and a workgroup the runs of its NW (4 or 8) wavefronts, so the chip
-// gets an even share per wavefront whatever the matrix shape; with column
-// windows a workgroup instead takes whole tiles of one window of columns.
+// then tile 1, ...).  By default a workgroup takes a contiguous run of NW * upw
+// units and each of its NW (4 or 8) wavefronts an even part of that run (the
+// parts differ by at most one unit, the longer ones on wavefronts 0, 1, ..., so
+// on different SIMDs), so the chip gets an even share per wavefront whatever
+// the matrix shape; with column windows a workgroup instead takes whole tiles
+// of one window of columns, split between its wavefronts the same way.
 // Per-tile sums go to LDS; after the main loop the workgroup adds its
 // wavefronts' pieces of each tile in wavefront order, writes y for tiles it
 // covered completely, and hands the rest to the other workgroups sharing the
@@ -872,11 +874,19 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
 }
 
 // Step barrier of a chain.  Workgroup g arrives at step j by storing the run's
-// tag in arrive[j][g]; workgroup 0 (the collector) polls the arrivals of the
-// step and then stores the tag in done[j]; the others poll done[j].  Plain
-// stores and loads through the device coherence point: no read-modify-write on
-// a shared word (hundreds of them on one address serialise at the memory).
-// Every poll loop is bounded by `spin`; one that gives up sets the error word.
+// tag in arrive[j][g].  Two forms of the wait:
+//  * two hops (batch 1): workgroup 0 (the collector) polls the arrivals of the
+//    step and then stores the tag in done[j]; the others poll done[j];
+//  * one hop (larger batches): every workgroup's first wavefront polls the
+//    arrivals itself.
+// Measured on a decoder's sweep of projections, the one-hop form is 3-4%
+// faster at batch 8 and 1% slower at batch 1, where its releases are spread
+// wider (hundreds of pollers on the same words).
+// All plain stores and loads through the device coherence point: no
+// read-modify-write on a shared word (hundreds of them on one address serialise
+// at the memory).  Every poll loop is bounded by `spin`; one that gives up sets
+// the error word.  Arriving at step j implies having arrived at every earlier
+// step, so both forms also order step j+1 after all earlier steps.
 __device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -914,9 +924,26 @@ __device__ __forceinline__ void chain_collect(const ChainCtl& c, int step, uint3
 
 // Wait before reading step `step`'s activations until every workgroup has
 // finished step - 1.
+template <bool ONE_HOP>
 __device__ __forceinline__ void chain_wait(const ChainCtl& c, int step, uint32_t tag) {
   if (step == 0) return;
-  if (blockIdx.x == 0) {
+  if constexpr (ONE_HOP) {
+    if (threadIdx.x < 64) {
+      const uint32_t* arr = c.arrive + (size_t)(step - 1) * c.groups;
+      uint32_t n = 0;
+      for (;;) {
+        bool mine = true;
+        for (uint32_t g = threadIdx.x; g < c.groups; g += 64) mine &= load_coherent(arr + g) == tag;
+        if (__all(mine)) break;
+        // bounded: give up after `spin` polls, or at once once another wait of the run has
+        if (++n > c.spin || __builtin_amdgcn_readfirstlane(load_coherent(c.error)) != 0u) {
+          if (threadIdx.x == 0) chain_fail(c);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  } else if (blockIdx.x == 0) {
     chain_collect(c, step - 1, tag);
   } else if (threadIdx.x == 0) {
     uint32_t n = 0;
@@ -954,7 +981,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   // cs + u % cw).  Without windows cs = 0, cw = n_cols and the runs split the
   // whole unit range evenly; with windows each workgroup takes whole tiles of
   // one window.
-  int cs = 0, cw = n_cols, w = 0, U0, U1, upw;
+  int cs = 0, cw = n_cols, w = 0, U0, U1;
   if (a.tiles_per_wg > 0) {
     w = lblock / a.wg_per_win;
     const int t_first = (lblock - w * a.wg_per_win) * a.tiles_per_wg;
@@ -963,9 +990,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     cw = a.win_base + (w < a.win_extra ? 1 : 0);
     U0 = t_first * cw;
     U1 = min(t_first + a.tiles_per_wg, a.n_tiles) * cw;
-    upw = (a.tiles_per_wg * cw + NW - 1) / NW;
   } else {
-    upw = a.upw;
     U0 = lblock * a.wgu;
     if (U0 >= a.n_units) return false;               // whole workgroup idle
     U1 = min(U0 + a.wgu, a.n_units);
@@ -994,8 +1019,11 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   // the dynamic prologue fills buffer k with unit wid + k * NW and the LDS
   // counter starts past them; that numbering is written for two buffers
   static_assert(!DYN || DEPTH == 2, "dynamic units assume two weight buffers");
-  const int u0 = DYN ? U0 + wid : U0 + wid * upw;
-  const int u1 = DYN ? U1 : min(u0 + upw, U1);
+  // wavefront i's part of the run: [run_begin(i), run_begin(i + 1))
+  const int run_base = (U1 - U0) / NW, run_ext = (U1 - U0) % NW;
+  auto run_begin = [&](int i) { return U0 + i * run_base + min(i, run_ext); };
+  const int u0 = DYN ? U0 + wid : run_begin(wid);
+  const int u1 = DYN ? U1 : run_begin(wid + 1);
   const bool active = u0 < U1;
   const int t0 = u0 / cw;                          // first tile of this wavefront
   // The weight stream runs DEPTH-1 units ahead of the unit being computed.
@@ -1020,11 +1048,13 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   XStage<QT, B, XF32, NW, kRS> xs;
   if constexpr (CHAIN) {
     // before the step barrier every buffer is filled (DYN: the first unit), so
-    // twice as many weights stream in while the previous step drains
+    // twice as many weights stream in while the previous step drains.  (Filling
+    // the last buffer after the activation loads instead, so that they do not
+    // wait for its weights, measured slower.)
 #pragma unroll
     for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
     if constexpr (!DYN) refill(DEPTH - 1);
-    if (wait) chain_wait(*ctl, step, tag);
+    if (wait) chain_wait<!DYN>(*ctl, step, tag);
     xs.template load<true>(a, c0w, len, 0);
   } else {
     xs.template load<false>(a, c0w, len, 0);
@@ -1188,7 +1218,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         for (int b = 0; b < B; ++b) s[b] += S[((U - U0) * B + b) * kTileRows + lane];
     } else {
       for (int i = 0; i < NW; ++i) {
-        const int a0 = U0 + i * upw, a1 = min(a0 + upw, U1);
+        const int a0 = run_begin(i), a1 = run_begin(i + 1);
         if (max(a0, ts) >= min(a1, te)) continue;
         const float* pw = P + ((i * a.tpw + (t - a0 / cw)) * B) * kTileRows;
 #pragma unroll
@@ -1279,8 +1309,10 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
       else
         waited |= gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
     }
-    // the collector never skips a step that waits
-    if (blockIdx.x == 0 && j > 0 && st.wait && !waited) chain_collect(c.ctl, j - 1, tag);
+    // the collector of the two-hop wait never skips a step that waits
+    if constexpr (dyn_units<B, NW, MF>()) {
+      if (blockIdx.x == 0 && j > 0 && st.wait && !waited) chain_collect(c.ctl, j - 1, tag);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's y / partial stores are done
     __syncthreads();
     if (threadIdx.x == 0) store_coherent(c.ctl.arrive + (size_t)j * c.ctl.groups + blockIdx.x, tag);
