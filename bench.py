@@ -857,6 +857,98 @@ def summarize_pmc(dirs: list) -> str:
     return "\n".join(out) + "\n"
 
 
+def timeline_report(batches, runs: int = 3) -> str:
+    """Per-step timeline of the B = 1 / B = 8 chain sweeps from libkq_timeline.so (the -DKQ_TIMELINE build, see
+    include/kq_timeline.h): per projection class, medians over the 52 layers of where each step's time goes."""
+    import ctypes
+    import numpy as np
+    import torch
+    from quant_weight_streaming_amd import kq
+    kq.LIB_PATH = os.path.join(ROOT, "quant_weight_streaming_amd", "libkq_timeline.so")
+    kq._lib = None
+    L = kq.lib()
+    L.kq_chain_timeline.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    L.kq_chain_timeline.restype = ctypes.c_int
+    kq.kq_init(0)
+    sw = Sweep(3, "q4k", batches, 0.0, 0.0)
+    names = [spec.name for (_, spec, _, _) in sw.entries]
+    out = ["Per-step timeline of the chain sweep (52 x {QKV, O, gate+up, down} + head, Q4_K / Q6_K, bf16 x):",
+           "device clock stamps (100 MHz) of every workgroup at six points of every step, last of "
+           f"{runs} runs after warm-up.",
+           "Per class, medians over the 52 layers of: span = last arrival of the step - last arrival of the",
+           "step before; release = a workgroup's exit from the barrier wait - the previous step's last arrival",
+           "(median / max over workgroups); stage, main, tail = staging, main loop, tile writes and hand-off",
+           "(median over workgroups; main also max); drain = last arrival - slowest main loop end.", ""]
+    for B in batches:
+        chain = kq.Chain([(spec.part_types() if spec.types else spec.qtype, reps, parts, spec.cols, sw.x[B][i],
+                           sw.y[B][i]) for i, (layer, spec, reps, parts) in enumerate(sw.entries)], B)
+        s = torch.cuda.current_stream()
+        for _ in range(3):
+            chain.run(s)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ms = []
+        for _ in range(runs):
+            ev[0].record(s)
+            chain.run(s)
+            ev[1].record(s)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        if chain.status() != 0:
+            raise RuntimeError("a chain wait gave up during the timeline run")
+        buf = np.zeros((len(names) + 8) * 256 * 8 * 4, dtype=np.uint64)
+        g, n = ctypes.c_int(), ctypes.c_int()
+        rc = L.kq_chain_timeline(ctypes.c_void_p(chain.handle), buf.ctypes.data, buf.nbytes, ctypes.byref(g),
+                                 ctypes.byref(n))
+        if rc != 0:
+            raise RuntimeError(f"kq_chain_timeline failed: {rc}")
+        G, N = g.value, n.value
+        t = buf[:N * G * 8].reshape(N, G, 8).astype(np.int64)
+        chain.close()
+        xcc = t[0, :, 6].copy()
+        us = (t[:, :, :6] - t[0, :, 0].min()) * 0.01
+        act = t[:, :, 1] > 0
+        rows = {}
+        prev_end = us[0, :, 0].min()
+        for j in range(N):
+            v = act[j]
+            r = us[j]
+            end = r[:, 5].max()
+            rel = r[v, 1] - prev_end
+            main = r[v, 3] - r[v, 2]
+            d = dict(span=end - prev_end, rel_med=np.median(rel), rel_max=rel.max(),
+                     stage=np.median(r[v, 2] - r[v, 1]), main_med=np.median(main), main_max=main.max(),
+                     tail=np.median(r[v, 4] - r[v, 3]), drain=end - r[v, 3].max(), groups=int(v.sum()))
+            rows.setdefault(names[j] if j < len(names) else "?", []).append(d)
+            prev_end = end
+        out.append(f"batch {B}: chain run {np.median(ms):.3f} ms (event timing of the timeline build), "
+                   f"{G} workgroups, {N} steps")
+        out.append(f"  {'class':8s} {'steps':>5s} {'groups':>6s} {'span':>7s} {'rel med':>8s} {'rel max':>8s} "
+                   f"{'stage':>7s} {'main med':>9s} {'main max':>9s} {'tail':>6s} {'drain':>6s}   (us)")
+        for name, ds in rows.items():
+            med = {k: float(np.median([d[k] for d in ds])) for k in ds[0]}
+            out.append(f"  {name:8s} {len(ds):5d} {int(med['groups']):6d} {med['span']:7.2f} {med['rel_med']:8.2f} "
+                       f"{med['rel_max']:8.2f} {med['stage']:7.2f} {med['main_med']:9.2f} {med['main_max']:9.2f} "
+                       f"{med['tail']:6.2f} {med['drain']:6.2f}")
+        tot = sum(float(np.sum([d["span"] for d in ds])) for ds in rows.values())
+        out.append(f"  sum of spans {tot / 1e3:.3f} ms; per layer "
+                   + ", ".join(f"{k} {np.median([d['span'] for d in ds]):.2f}" for k, ds in rows.items() if len(ds) > 1)
+                   + " us")
+        # main-loop time of each workgroup relative to its step's median, averaged over the big steps, by XCC
+        big = [j for j in range(N) if j < len(names) and names[j] in ("gate_up", "down")]
+        relm = []
+        for j in big:
+            v = act[j]
+            m = us[j, :, 3] - us[j, :, 2]
+            relm.append(np.where(v, m / np.median(m[v]), np.nan))
+        relm = np.array(relm)
+        per_xcc = [relm[:, xcc == x] for x in range(8)]
+        out.append("  gate+up and down main loop relative to the step median, mean per XCC: "
+                   + " ".join(f"{x}:{np.nanmean(m):.3f}" for x, m in enumerate(per_xcc) if np.isfinite(m).any()))
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -876,6 +968,8 @@ def main():
                     help="print the HBM-traffic JSON of the dominant kernel from four rocprofv3 --pmc runs")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ROCPROF_DIR",
                     help="print per-dispatch counter means of the GEMV dispatches of rocprofv3 --pmc runs")
+    ap.add_argument("--timeline", action="store_true",
+                    help="print the per-step timeline of the B=1 and B=8 chain sweeps (needs libkq_timeline.so)")
     args = ap.parse_args()
     if args.summarize_pmc:
         sys.stdout.write(summarize_pmc(args.summarize_pmc))
@@ -898,6 +992,9 @@ def main():
         return profile_kernel(args.profile_kernel, args.profile_batch)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.timeline:
+        sys.stdout.write(timeline_report((1, 8)))
+        return
 
     import torch
     from quant_weight_streaming_amd import kq, synth

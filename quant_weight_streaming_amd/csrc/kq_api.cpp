@@ -12,6 +12,9 @@
 #include <vector>
 
 #include "../../include/kq.h"
+#ifdef KQ_TIMELINE
+#include "../../include/kq_timeline.h"
+#endif
 #include "kq_internal.h"
 
 namespace kq {
@@ -587,6 +590,7 @@ struct kq_chain {
   uint32_t* counters = nullptr; // the workspace (its counter blocks are reset after a run whose wait gave up)
   size_t ws_bytes = 0;
   uint32_t* flag = nullptr;     // pinned host word, set by the device when a wait gives up
+  size_t tl_bytes = 0;          // timeline builds: the clock stamps after the workspace
 };
 
 using namespace kq;
@@ -908,7 +912,12 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     ws_bytes = off > ws_bytes ? off : ws_bytes;
     j = k;
   }
-  const size_t total = steps_bytes + ctl_bytes + ws_bytes;
+#ifdef KQ_TIMELINE
+  const size_t tl_bytes = (size_t)n_sub * groups * 8 * sizeof(uint64_t);
+#else
+  const size_t tl_bytes = 0;
+#endif
+  const size_t total = steps_bytes + ctl_bytes + ws_bytes + tl_bytes;
   if (hipMalloc(&c->mem, total) != hipSuccess) {
     delete c;
     return KQ_ERR_NOMEM;
@@ -936,7 +945,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   rc = KQ_OK;
   if (hipHostGetDevicePointer(reinterpret_cast<void**>(&d_flag), c->flag, 0) != hipSuccess ||
       hipMemcpy(d_steps, h.data(), (size_t)n_sub * sizeof(ChainStep), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_ws, 0, ws_bytes) != hipSuccess ||
+      hipMemset(d_ctl, 0, ctl_bytes) != hipSuccess || hipMemset(d_ws, 0, ws_bytes + tl_bytes) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess)
     rc = KQ_ERR_HIP;
   if (rc != KQ_OK) {
@@ -957,7 +966,9 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   c->args.steps = d_steps;
   c->args.n_steps = n_sub;
   uint32_t* d_done = d_ctl + (size_t)n_sub * groups;
-  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_sub, d_done + n_sub + 1, d_flag, (uint32_t)groups, 0};
+  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_sub, d_done + n_sub + 1, d_flag,
+                         tl_bytes ? reinterpret_cast<uint64_t*>(d_ws + ws_bytes) : nullptr, (uint32_t)groups, 0};
+  c->tl_bytes = tl_bytes;
   *out = c;
   return KQ_OK;
 }
@@ -977,6 +988,22 @@ int kq_chain_run(kq_chain* c, void* stream) {
     return KQ_ERR_HIP;
   return KQ_OK;
 }
+
+#ifdef KQ_TIMELINE
+int kq_chain_timeline(kq_chain* c, uint64_t* host, size_t bytes, int* groups, int* n_sub) {
+  if (!c || !host || !groups || !n_sub) return KQ_ERR_NULL;
+  if (bytes < c->tl_bytes) return KQ_ERR_SHAPE;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(c->dev) != hipSuccess) return KQ_ERR_HIP;
+  const bool ok = hipDeviceSynchronize() == hipSuccess &&
+                  hipMemcpy(host, c->args.ctl.tl, c->tl_bytes, hipMemcpyDeviceToHost) == hipSuccess;
+  (void)hipSetDevice(prev);
+  if (!ok) return KQ_ERR_HIP;
+  *groups = (int)c->args.ctl.groups;
+  *n_sub = c->args.n_steps;
+  return KQ_OK;
+}
+#endif
 
 int kq_chain_query(kq_chain* c) {
   if (!c) return KQ_ERR_NULL;

@@ -894,6 +894,33 @@ __device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Per-step timeline of a chain, in measurement builds only (-DKQ_TIMELINE,
+// libkq_timeline.so): the first thread of each workgroup stores the device
+// clock (s_memrealtime, 100 MHz) at fixed points of every step it takes part
+// in, into tl[step][workgroup][k]:
+//   0 step start, 1 after the barrier wait, 2 activations staged,
+//   3 main loop done (all wavefronts), 4 tiles written or handed over,
+//   5 arrival stored; at step 0, slot 6 holds the XCC id and 7 the HW_ID word.
+#ifdef KQ_TIMELINE
+__device__ __forceinline__ void tl_stamp(const ChainCtl* c, int step, int k) {
+  if (c && c->tl && threadIdx.x == 0)
+    __hip_atomic_store(c->tl + ((size_t)step * c->groups + blockIdx.x) * 8 + k,
+                       (uint64_t)__builtin_amdgcn_s_memrealtime(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void tl_ids(const ChainCtl* c) {
+  if (c->tl && threadIdx.x == 0) {
+    uint32_t x, h;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(h));
+    __hip_atomic_store(c->tl + (size_t)blockIdx.x * 8 + 6, (uint64_t)x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(c->tl + (size_t)blockIdx.x * 8 + 7, (uint64_t)h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+#else
+__device__ __forceinline__ void tl_stamp(const ChainCtl*, int, int) {}
+__device__ __forceinline__ void tl_ids(const ChainCtl*) {}
+#endif
+
 // A wait gave up: set the device error word (later waits of the run then give
 // up at once, and later runs do nothing) and the host-visible word that
 // kq_chain_run and kq_chain_query read without a device synchronisation.
@@ -1055,6 +1082,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
     if constexpr (!DYN) refill(DEPTH - 1);
     if (wait) chain_wait<!DYN>(*ctl, step, tag);
+    tl_stamp(ctl, step, 1);
     xs.template load<true>(a, c0w, len, 0);
   } else {
     xs.template load<false>(a, c0w, len, 0);
@@ -1080,6 +1108,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     }
   }
   __syncthreads();
+  if constexpr (CHAIN) tl_stamp(ctl, step, 2);
 
   if constexpr (DYN) {
     // unit indices (relative to U0) held by the buffers; >= n: nothing
@@ -1187,6 +1216,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     }
   }
   __syncthreads();
+  if constexpr (CHAIN) tl_stamp(ctl, step, 3);
 
   // Each tile of the workgroup: add the wavefronts' sums in wavefront order;
   // write y if the workgroup covered the whole tile, else hand it over.
@@ -1257,6 +1287,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
       hand_off<BU, CHAIN>(a, t, lblock, a.wgu, lane, su, q);
     }
   }
+  if constexpr (CHAIN) tl_stamp(ctl, step, 4);
   return wait;
 }
 
@@ -1293,6 +1324,7 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
   for (int j = 0; j < c.n_steps; ++j) {
     ConstChainStep& st = steps[j];
     const int g = st.grid;
+    tl_stamp(&c.ctl, j, 0);
     // a further weight type of the same step reads the same x as the sub-step
     // before it and writes other outputs: no wait
     bool waited = st.wait == 0;
@@ -1316,7 +1348,9 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's y / partial stores are done
     __syncthreads();
     if (threadIdx.x == 0) store_coherent(c.ctl.arrive + (size_t)j * c.ctl.groups + blockIdx.x, tag);
+    tl_stamp(&c.ctl, j, 5);
   }
+  tl_ids(&c.ctl);
   if (blockIdx.x == 0) {
     chain_collect(c.ctl, c.n_steps - 1, tag);
     if (threadIdx.x == 0) store_coherent(c.ctl.epoch, tag);

@@ -72,6 +72,7 @@ struct ChainCtl {
   uint32_t* epoch;     // tag of the last completed run
   uint32_t* error;     // set when a wait gave up
   uint32_t* error_host;// pinned host word, set with the error word (read by the host without a sync)
+  uint64_t* tl;        // timeline builds (KQ_TIMELINE): [step][workgroup][8] device clock stamps; else null
   uint32_t groups;     // workgroups of the launch
   uint32_t spin;       // polls before a wait gives up
 };

@@ -27,6 +27,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_timeline_symbol_only_in_the_measurement_build(tmp_path):
+    """kq_timeline.h compiles as C99; its one symbol is exported by libkq_timeline.so (when built) and not by the
+    product library, whose chain kernel records nothing."""
+    import subprocess
+    src = tmp_path / "tl.c"
+    src.write_text('#include "kq_timeline.h"\nint main(void) { return kq_chain_timeline != 0 ? 0 : 1; }\n')
+    subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-I", os.path.join(ROOT, "include"), str(src)], check=True)
+    assert not hasattr(kq.lib(), "kq_chain_timeline")
+    tl = os.path.join(ROOT, "quant_weight_streaming_amd", "libkq_timeline.so")
+    if os.path.exists(tl):
+        assert hasattr(ctypes.CDLL(tl), "kq_chain_timeline")
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """No fallback path: without the built library every entry point raises instead of computing on the CPU."""
     monkeypatch.setattr(kq, "LIB_PATH", str(tmp_path / "libkq.so"))
