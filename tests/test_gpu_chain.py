@@ -198,16 +198,17 @@ def test_chain_graph_replay():
     ch.close()
 
 
-def test_chain_wait_that_gives_up_is_reported(monkeypatch):
+@pytest.mark.parametrize("batch", [1, 8])
+def test_chain_wait_that_gives_up_is_reported(batch, monkeypatch):
     """With no polls allowed (KQ_CHAIN_SPIN=0, read at each run) a wait that finds the previous step unfinished
     gives up: the run's results are invalid, the host-visible flag says so without a device synchronisation
     (kq_chain_query), the next kq_chain_run is refused, and kq_chain_status reports it and resets the chain.
     The same chain then runs clean with the default limit and matches its single launches bitwise (so the
     time-out left no stale split-tile counters behind).  Step 1 gives every workgroup work, so every
-    workgroup waits for step 0, and the first to finish step 0 finds it unfinished."""
-    batch = 1
+    workgroup waits for step 0, and the first to finish step 0 finds it unfinished.  Batch 1 waits in two
+    hops (collector, done word), batch 8 in one (every workgroup polls the arrivals)."""
     timeout = kq.STATUS_CODE["KQ_ERR_TIMEOUT"]
-    say("case chain spin 0")
+    say(f"case chain spin 0 B={batch}")
     specs = [("q6k", (64 * 64,), 122 * 256), ("q4k", (16384,), 4096), ("q4k", (256,), 1024)]
     steps, hosts = _independent_steps(specs, batch, "bf16", "spin")
     ch = kq.Chain(steps, batch)
