@@ -875,9 +875,10 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
 
 // Step barrier of a chain.  Workgroup g arrives at step j by storing the run's
 // tag in arrive[j][g].  Two forms of the wait:
-//  * two hops (batch 1): workgroup 0 (the collector) polls the arrivals of the
-//    step and then stores the tag in done[j]; the others poll done[j];
-//  * one hop (larger batches): every workgroup's first wavefront polls the
+//  * two hops (the dynamic-units shape: batch 1, 8-wavefront workgroups):
+//    workgroup 0 (the collector) polls the arrivals of the step and then
+//    stores the tag in done[j]; the others poll done[j];
+//  * one hop (every other shape): every workgroup's first wavefront polls the
 //    arrivals itself.
 // Measured on a decoder's sweep of projections, the one-hop form is 3-4%
 // faster at batch 8 and 1% slower at batch 1, where its releases are spread
