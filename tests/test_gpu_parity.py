@@ -60,6 +60,16 @@ def test_runs_span_many_tiles(qtype, batch):
     run_case(qtype, 3000 * 64 + 5, 256, batch, "bf16", 250 + batch, check_w=False)
 
 
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("cols_sb", [26, 29])
+@pytest.mark.parametrize("xdtype,batch", [("bf16", 8), ("f32", 4)])
+def test_window_workgroups_smaller_than_their_wavefronts(qtype, cols_sb, xdtype, batch):
+    """Eight staged rows and 26 or 29 super-block columns: column windows of 5 or 6 columns over 4 row tiles,
+    one tile per workgroup, so a workgroup has fewer units than wavefronts; its wavefronts take parts of 1 or 0
+    units (the longer ones first), and the tile sums still add in unit order."""
+    run_case(qtype, 3 * 64 + 9, cols_sb * 256, batch, xdtype, 900 + cols_sb + batch, check_w=False)
+
+
 @pytest.mark.parametrize("qtype", ["q4k", "q6k"])
 def test_long_rows_split_many_ways(qtype):
     # 5 tiles x 122 columns (the down projection's K): one unit per wavefront, 122 partials per tile
