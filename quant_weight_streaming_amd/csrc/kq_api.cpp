@@ -941,6 +941,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     h[j].type = subs[j].type;
     h[j].grid = (int32_t)plans[j].grid;
     h[j].wait = subs[j].wait ? 1 : 0;
+    // a further weight type of a step starts on the workgroups after those of the types before it
+    h[j].first = subs[j].wait || j == 0 ? 0 : (int32_t)(((int64_t)h[j - 1].first + h[j - 1].grid) % groups / 8 * 8);
   }
   rc = KQ_OK;
   if (hipHostGetDevicePointer(reinterpret_cast<void**>(&d_flag), c->flag, 0) != hipSuccess ||

@@ -1330,10 +1330,10 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
     // before it and writes other outputs: no wait
     bool waited = st.wait == 0;
     // the step's logical blocks, as a single launch numbers them, grid-stride
-    // over the resident workgroups (the launch is a multiple of 8 workgroups, so
-    // every logical block keeps the XCD it would have had); the first block
-    // with work waits at the step barrier
-    for (int vb = blockIdx.x; vb < g; vb += gridDim.x) {
+    // over the resident workgroups from workgroup st.first on (the launch and
+    // st.first are multiples of 8, so every logical block keeps the XCD it would
+    // have had); the first block with work waits at the step barrier
+    for (int vb = ((int)blockIdx.x + (int)gridDim.x - st.first) % (int)gridDim.x; vb < g; vb += gridDim.x) {
       const int lblock = (vb & 7) * (g >> 3) + (vb >> 3);
       if (st.type == KQ_Q4_K)
         waited |= gemv_block<KQ_Q4_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);

@@ -78,15 +78,17 @@ struct ChainCtl {
 };
 
 // One step of a chain, device-resident: its launch arguments, weight type,
-// logical workgroups (a multiple of 8, at most the launch's), and whether it
+// logical workgroups (a multiple of 8, at most the launch's), whether it
 // waits for the previous step (0: a further weight type of the same step, which
-// shares its x and writes other outputs).
+// shares its x and writes other outputs), and the resident workgroup that takes
+// its logical block 0 (a multiple of 8: a further weight type starts after the
+// workgroups of the types before it, so they do not take both).
 struct ChainStep {
   GemvArgs a;
   int32_t type;
   int32_t grid;
   int32_t wait;
-  int32_t pad;
+  int32_t first;
 };
 
 struct ChainArgs {
