@@ -875,7 +875,7 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
 
 // Step barrier of a chain.  Workgroup g arrives at step j by storing the run's
 // tag in arrive[j][g].  Two forms of the wait:
-//  * two hops (the dynamic-units shape: batch 1, 8-wavefront workgroups):
+//  * two hops (the dynamic-units shape: one or two staged rows, 8 wavefronts):
 //    workgroup 0 (the collector) polls the arrivals of the step and then
 //    stores the tag in done[j]; the others poll done[j];
 //  * one hop (every other shape): every workgroup's first wavefront polls the
@@ -1036,7 +1036,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
                  : T + a.tsb * TSB * B;
   float* P = norm ? Q2 + ((a.tsb * B + 3) & ~3) : Q2;
   if (!norm) Q2 = nullptr;
-  // DYN (batch 1, one 8-wavefront workgroup per CU): instead of fixed runs the
+  // DYN (one or two staged rows, one 8-wavefront workgroup per CU): instead of fixed runs the
   // wavefronts take the workgroup's units one at a time from an LDS counter, so
   // a wavefront that gets fewer issue slots than its neighbours simply computes
   // fewer units; each unit's row sums go to an LDS slot of their own and a

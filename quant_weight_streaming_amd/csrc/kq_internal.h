@@ -115,10 +115,13 @@ hipError_t launch_gemv_type(int xtype, int rows, int nw, bool mf, const GemvArgs
 // (Q4_K/Q5_K) their sub-block sums (matrix cores: rows padded to 528 bytes,
 // then a 512-byte zero block), plus each wavefront's partial sums of the tiles its run touches
 // (dynamic workgroups: a counter and one slot per unit).
-// Workgroups whose wavefronts take units dynamically (see gemv_block).
+// Workgroups whose wavefronts take units dynamically (see gemv_block): the dot2
+// path (one or two staged rows: batch 1 or 2 with bf16 x, batch 1 with fp32 x)
+// in 8-wavefront workgroups.  With more staged rows the per-unit LDS slots
+// would not fit beside the staged activations.
 template <int B, int NW, bool MF>
-__host__ __device__ constexpr bool dyn_units() { return B == 1 && NW == 8 && !MF; }
-inline bool dyn_units(int batch, int nw, bool mf) { return batch == 1 && nw == 8 && !mf; }
+__host__ __device__ constexpr bool dyn_units() { return B <= 2 && NW == 8 && !MF; }
+inline bool dyn_units(int batch, int nw, bool mf) { return batch <= 2 && nw == 8 && !mf; }
 
 // `run_units`: units of one workgroup (the per-unit slots of dynamic workgroups);
 // `tpw`: tiles one wavefront's run can touch (its tile sums otherwise).
