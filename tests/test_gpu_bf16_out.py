@@ -78,3 +78,47 @@ def test_bf16_activation_chain(batch, monkeypatch):
     for j in range(3):
         assert torch.equal(ys[j], ys2[j]) and torch.equal(cs[j].view(torch.int16), cs2[j].view(torch.int16)), j
         assert torch.equal(cs[j].view(torch.int16), rne(ys[j]).view(torch.int16)), j
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 8])
+def test_chain_rereads_a_rewritten_activation(batch, monkeypatch):
+    """Step 0 reads A, step 1 overwrites A with the bf16 copy of its output, step 2 reads A again and must see the
+    new values, not lines that step 0's reads left in a cache.  A second run's step 0 reads what the first run's
+    step 1 wrote.  Every run equals the launches in order."""
+    monkeypatch.setenv("KQ_WG_WAVES", "8")
+    K = 1536
+    say(f"case chain re-reads a rewritten activation B={batch}")
+    ws = [kq.repack("q4k", synth.gen_weights("q4k", K, K, synth.seed_of("reread", j), device=DEV), K, K)
+          for j in range(3)]
+    a0 = synth.gen_x(batch, K, synth.seed_of("reread-a", batch), "bf16", device=DEV)
+    c = synth.gen_x(batch, K, synth.seed_of("reread-c", batch), "bf16", device=DEV)
+
+    def launches(a, n_runs):
+        a = a.clone()
+        ys = [torch.zeros(batch, K, device=DEV) for _ in range(3)]
+        out = []
+        for _ in range(n_runs):
+            kq.kq_gemv_fused("q4k", [ws[0]], [K], K, a, [ys[0]])
+            kq.kq_gemv_fused("q4k", [ws[1]], [K], K, c, [ys[1]], y16s=[a])
+            kq.kq_gemv_fused("q4k", [ws[2]], [K], K, a, [ys[2]])
+            torch.cuda.synchronize()
+            out.append([y.clone() for y in ys] + [a.clone()])
+        return out
+
+    ref = launches(a0, 2)
+    a = a0.clone()
+    ys = [torch.zeros(batch, K, device=DEV) for _ in range(3)]
+    ch = kq.Chain([("q4k", [ws[0]], [K], K, a, [ys[0]]),
+                   ("q4k", [ws[1]], [K], K, c, [ys[1]], kq.KQ_EPI_NONE, 0.0, 0.0, [a]),
+                   ("q4k", [ws[2]], [K], K, a, [ys[2]])], batch)
+    for run in range(2):
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        got = [y.clone() for y in ys] + [a.clone()]
+        for j, (g, r) in enumerate(zip(got, ref[run])):
+            assert torch.equal(g.view(torch.int32) if g.dtype == torch.float32 else g.view(torch.int16),
+                               r.view(torch.int32) if r.dtype == torch.float32 else r.view(torch.int16)), \
+                f"run {run} output {j}"
+    ch.close()
+    assert not torch.equal(ref[0][0], ref[1][0]), "the second run's first step must read a different A"
