@@ -896,8 +896,10 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   }
 
   const size_t steps_bytes = round_up((size_t)n_sub * sizeof(ChainStep), 256);
-  // control words: arrive[n_sub][groups], done[n_sub], epoch, error
-  const size_t ctl_bytes = round_up(((size_t)n_sub * (groups + 1) + 2) * sizeof(uint32_t), 256);
+  // control words: arrive[n_sub][groups], done[n_sub][kDoneReplicas][16] (one 64-byte line per replica),
+  // epoch, error
+  const size_t ctl_bytes =
+      round_up(((size_t)n_sub * (groups + kDoneReplicas * 16) + 2) * sizeof(uint32_t), 256);
   // Steps run one after another and share one workspace; the sub-steps of one step may run at the
   // same time, so each has its own region of it: the workspace is the largest step's sum of regions.
   std::vector<size_t> ws_off(n_sub);
@@ -968,7 +970,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   c->args.steps = d_steps;
   c->args.n_steps = n_sub;
   uint32_t* d_done = d_ctl + (size_t)n_sub * groups;
-  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + n_sub, d_done + n_sub + 1, d_flag,
+  c->args.ctl = ChainCtl{d_ctl, d_done, d_done + (size_t)n_sub * kDoneReplicas * 16,
+                         d_done + (size_t)n_sub * kDoneReplicas * 16 + 1, d_flag,
                          tl_bytes ? reinterpret_cast<uint64_t*>(d_ws + ws_bytes) : nullptr, (uint32_t)groups, 0};
   c->tl_bytes = tl_bytes;
   *out = c;

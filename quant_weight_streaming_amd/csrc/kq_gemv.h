@@ -877,7 +877,9 @@ __device__ __forceinline__ void hand_off_windows(GA& a, int t, int w, int lane, 
 // tag in arrive[j][g].  Two forms of the wait:
 //  * two hops (the dynamic-units shape: one or two staged rows, 8 wavefronts):
 //    workgroup 0 (the collector) polls the arrivals of the step and then
-//    stores the tag in done[j]; the others poll done[j];
+//    stores the tag in the kDoneReplicas copies of done[j] (a line each);
+//    workgroup g polls copy g % kDoneReplicas, so the pollers spread over
+//    lines instead of queueing on one;
 //  * one hop (every other shape): every workgroup's first wavefront polls the
 //    arrivals itself.
 // Measured on a decoder's sweep of projections, the one-hop form is 3-4%
@@ -944,10 +946,8 @@ __device__ __forceinline__ void chain_collect(const ChainCtl& c, int step, uint3
     if (quit) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if (threadIdx.x == 0) {
-    if (!all) chain_fail(c);
-    store_coherent(c.done + step, tag);
-  }
+  if (threadIdx.x == 0 && !all) chain_fail(c);
+  if (threadIdx.x < kDoneReplicas) store_coherent(c.done + ((size_t)step * kDoneReplicas + threadIdx.x) * 16, tag);
 }
 
 // Wait before reading step `step`'s activations until every workgroup has
@@ -975,7 +975,8 @@ __device__ __forceinline__ void chain_wait(const ChainCtl& c, int step, uint32_t
     chain_collect(c, step - 1, tag);
   } else if (threadIdx.x == 0) {
     uint32_t n = 0;
-    while (load_coherent(c.done + step - 1) != tag) {
+    const uint32_t* dw = c.done + ((size_t)(step - 1) * kDoneReplicas + blockIdx.x % kDoneReplicas) * 16;
+    while (load_coherent(dw) != tag) {
       if (++n > c.spin || load_coherent(c.error) != 0u) {
         chain_fail(c);
         break;

@@ -65,10 +65,14 @@ struct GemvArgs {
   uint32_t* counters;                  // workspace: arrival counters per split tile, zero between calls
 };
 
+// The two-hop step barrier's done word of a step is stored in this many
+// copies, one 64-byte line each; workgroup g polls copy g % kDoneReplicas.
+constexpr int kDoneReplicas = 16;
+
 // Control words of a chain launch (device memory owned by the chain).
 struct ChainCtl {
   uint32_t* arrive;    // [step][workgroup]: the run's tag once the workgroup finished the step
-  uint32_t* done;      // [step]: the run's tag once every workgroup finished the step
+  uint32_t* done;      // [step][kDoneReplicas][16]: the run's tag once every workgroup finished the step
   uint32_t* epoch;     // tag of the last completed run
   uint32_t* error;     // set when a wait gave up
   uint32_t* error_host;// pinned host word, set with the error word (read by the host without a sync)
