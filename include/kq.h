@@ -349,7 +349,24 @@ int kq_gather_rows(int type, const void *w, int64_t rows, int64_t cols, const in
  * the sub-steps after the first run without waiting for it (they share x and
  * write other outputs).  Each sub-step's results are bitwise those of the
  * kq_gemv_fused call over its segments with the chain's workgroup shape.
+ *
+ * Overlap of independent steps (flags & KQ_STEP_OVERLAP): such a step does not
+ * wait at the step barrier when none of its buffers (x, every y and y16, as
+ * byte ranges of batch rows) meets a buffer of a step that may still be running
+ * (every step since the last one that waited) in a way that orders them: its x
+ * against their outputs, its outputs against their x and outputs.  It then
+ * starts on the workgroups after the previous step's and runs while that step
+ * drains.  Each step of such an overlapping run has a workspace region of its
+ * own, so the chain's device memory grows with the run's length; a run is cut
+ * by a wait once its regions would pass 512 MiB.  A step that meets such a
+ * buffer waits as without the flag, and results are bitwise those of the same
+ * chain without the flag.  This is for sequences whose steps read inputs that
+ * are already in memory, such as GEMVs with activations of their own run back
+ * to back; in a decoder, where each projection reads the previous one's
+ * output, every step still waits.  Steps without the flag always wait.
  */
+#define KQ_STEP_OVERLAP 1
+
 typedef struct kq_chain_step {
   int32_t type;                   /* KQ_Q4_K / KQ_Q5_K / KQ_Q6_K */
   int32_t n;                      /* row segments sharing x, 1..KQ_MAX_PROJ */
@@ -366,7 +383,7 @@ typedef struct kq_chain_step {
                                      w from kq_repack_swiglu, rows[0] = inter) */
   float rms_eps;                  /* > 0: weight-less RMSNorm of x first, as kq_gemv_fused; 0: none */
   float head_eps;                 /* epsilon of KQ_EPI_HEADNORM segments, as kq_gemv_fused */
-  int32_t reserved;               /* set to 0 */
+  int32_t flags;                  /* 0 or KQ_STEP_OVERLAP (above); any other bit: KQ_ERR_SHAPE */
   int32_t types[KQ_MAX_PROJ];     /* segment i's weight type; 0 = `type` (a zeroed array: one type) */
 } kq_chain_step;
 
@@ -376,8 +393,9 @@ typedef struct kq_chain kq_chain;
  * Plan a chain of n_steps (1..65536) steps on the current device: validates
  * every step as kq_gemv_multi would, sizes the persistent grid from the
  * kernel's occupancy, and allocates the chain's device memory (the step table,
- * the step barrier's words, about 2.5 KB per step, and one workspace of the
- * largest step's size) and one pinned host word for its time-out flag.
+ * the step barrier's words, about 2.5 KB per step, and a workspace: the
+ * largest step's size, or with KQ_STEP_OVERLAP the largest run of overlapping
+ * steps' regions) and one pinned host word for its time-out flag.
  * Synchronous; must not be called inside a stream capture.  The step table is copied, so `steps` may be freed after.
  * Every x must also satisfy ((batch-1)*ldx + cols) * element size < 2^31.
  * On success *out owns the plan; release it with kq_chain_destroy.
@@ -400,6 +418,14 @@ int kq_chain_create(int n_steps, const kq_chain_step *steps, int xtype, int batc
  * enqueuing nothing, once the host word is set (no device synchronisation).
  */
 int kq_chain_run(kq_chain *c, void *stream);
+
+/*
+ * Host only: waits[j] = 1 if step j of the chain waits at the step barrier,
+ * 0 if it overlaps the steps before it (KQ_STEP_OVERLAP with independent
+ * buffers; step 0 always reads 1).  n must be the chain's step count, else
+ * KQ_ERR_SHAPE.
+ */
+int kq_chain_waits(const kq_chain *c, uint8_t *waits, int n);
 
 /*
  * Non-synchronising: KQ_ERR_TIMEOUT if a run's wait has given up since the

@@ -525,6 +525,8 @@ struct SubStep {
   uint32_t epi = 0;
   float rms_eps = 0.0f, head_eps = 0.0f;
   bool wait = true;
+  int step = 0;          // index of the chain step it belongs to
+  bool overlap = false;  // the step carries KQ_STEP_OVERLAP
 };
 
 // Split a chain step into one sub-step per weight type (segment i's type is
@@ -550,6 +552,7 @@ static int split_by_type(const kq_chain_step& st, std::vector<SubStep>& out) {
     u.rms_eps = st.rms_eps;
     u.head_eps = st.head_eps;
     u.wait = g == 0;
+    u.overlap = (st.flags & KQ_STEP_OVERLAP) != 0;
     for (int i = 0; i < st.n; ++i) {
       if (seg_type[i] != u.type) continue;
       const int k = u.n++;
@@ -591,6 +594,7 @@ struct kq_chain {
   size_t ws_bytes = 0;
   uint32_t* flag = nullptr;     // pinned host word, set by the device when a wait gives up
   size_t tl_bytes = 0;          // timeline builds: the clock stamps after the workspace
+  std::vector<uint8_t> waits;   // per chain step: 1 if it waits at the step barrier
 };
 
 using namespace kq;
@@ -819,6 +823,70 @@ int kq_gather_rows(int type, const void* w, int64_t rows, int64_t cols, const in
 
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Byte ranges a sub-step reads (x) and writes (y, y16), batch rows included.
+struct ByteRange {
+  uintptr_t lo, hi;
+};
+static bool meets(const ByteRange& a, const ByteRange& b) { return a.lo < b.hi && b.lo < a.hi; }
+static ByteRange x_range(const SubStep& u, int batch, int64_t esize) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(u.x);
+  return {p, p + (uintptr_t)(((int64_t)(batch - 1) * u.ldx + u.cols) * esize)};
+}
+static void out_ranges(const SubStep& u, int batch, std::vector<ByteRange>& out) {
+  for (int i = 0; i < u.n; ++i) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(u.y[i]);
+    out.push_back({p, p + (uintptr_t)(((int64_t)(batch - 1) * u.ldy[i] + u.rows[i]) * 4)});
+    if (u.y16[i]) {
+      const uintptr_t q = reinterpret_cast<uintptr_t>(u.y16[i]);
+      out.push_back({q, q + (uintptr_t)(((int64_t)(batch - 1) * u.ldy16[i] + u.rows[i]) * 2)});
+    }
+  }
+}
+
+// Largest workspace of one run of overlapping steps (their regions are disjoint).
+constexpr size_t kMaxOverlapWorkspace = (size_t)512 << 20;
+
+// Which steps skip the step barrier.  The steps that may still be running when
+// a step starts are those since the last step that waited (a wait orders a
+// step after every earlier one).  A step with KQ_STEP_OVERLAP skips its wait
+// unless its x meets an output of one of them, or one of its outputs meets
+// their x or outputs (read after write, write after read, write after write),
+// or the run's workspace regions would pass kMaxOverlapWorkspace.  The sub-steps
+// of one step (one per weight type) go together: only the first can wait.
+static void mark_overlaps(std::vector<SubStep>& subs, const std::vector<Plan>& plans, int batch, int64_t esize) {
+  std::vector<ByteRange> run_x, run_out;   // buffers of the steps that may still be running
+  size_t run_ws = 0;
+  const int n_sub = (int)subs.size();
+  for (int f = 0; f < n_sub;) {
+    int l = f;
+    while (l + 1 < n_sub && subs[l + 1].step == subs[f].step) ++l;
+    std::vector<ByteRange> xs, outs;
+    size_t ws = 0;
+    for (int k = f; k <= l; ++k) {
+      xs.push_back(x_range(subs[k], batch, esize));
+      out_ranges(subs[k], batch, outs);
+      ws += round_up(plans[k].ws_bytes, 256);
+    }
+    bool free_to_run = f > 0 && subs[f].overlap && run_ws + ws <= kMaxOverlapWorkspace;
+    for (const ByteRange& o : outs) {
+      for (const ByteRange& r : run_x) free_to_run &= !meets(o, r);
+      for (const ByteRange& r : run_out) free_to_run &= !meets(o, r);
+    }
+    for (const ByteRange& x : xs)
+      for (const ByteRange& r : run_out) free_to_run &= !meets(x, r);
+    if (!free_to_run) {
+      run_x.clear();
+      run_out.clear();
+      run_ws = 0;
+    }
+    subs[f].wait = !free_to_run;
+    run_x.insert(run_x.end(), xs.begin(), xs.end());
+    run_out.insert(run_out.end(), outs.begin(), outs.end());
+    run_ws += ws;
+    f = l + 1;
+  }
+}
+
 int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batch, kq_chain** out) {
   if (!out) return KQ_ERR_NULL;
   *out = nullptr;
@@ -834,8 +902,11 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   for (int j = 0; j < n_steps; ++j) {
     const kq_chain_step& st = steps[j];
     if (st.n < 1 || st.n > KQ_MAX_PROJ) return KQ_ERR_BATCH;
+    if (st.flags & ~KQ_STEP_OVERLAP) return KQ_ERR_SHAPE;
+    const size_t first_sub = subs.size();
     int rc = split_by_type(st, subs);
     if (rc != KQ_OK) return rc;
+    for (size_t k = first_sub; k < subs.size(); ++k) subs[k].step = j;
   }
   for (const SubStep& u : subs) {
     const int rc = validate(u.type, u.n, u.w, u.rows, u.cols, u.x, xtype, u.ldx, batch, u.y, u.ldy);
@@ -895,6 +966,8 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     return rc;
   }
 
+  mark_overlaps(subs, plans, batch, esize);
+
   const size_t steps_bytes = round_up((size_t)n_sub * sizeof(ChainStep), 256);
   // control words: arrive[n_sub][groups], done[n_sub][kDoneReplicas][16] (one 64-byte line per replica),
   // epoch, error
@@ -943,6 +1016,7 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     h[j].type = subs[j].type;
     h[j].grid = (int32_t)plans[j].grid;
     h[j].wait = subs[j].wait ? 1 : 0;
+    h[j].gate = subs[j].wait ? j : j == 0 ? 0 : h[j - 1].gate;
     // a further weight type of a step starts on the workgroups after those of the types before it
     h[j].first = subs[j].wait || j == 0 ? 0 : (int32_t)(((int64_t)h[j - 1].first + h[j - 1].grid) % groups / 8 * 8);
   }
@@ -974,6 +1048,9 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
                          d_done + (size_t)n_sub * kDoneReplicas * 16 + 1, d_flag,
                          tl_bytes ? reinterpret_cast<uint64_t*>(d_ws + ws_bytes) : nullptr, (uint32_t)groups, 0};
   c->tl_bytes = tl_bytes;
+  c->waits.assign(n_steps, 0);
+  for (const SubStep& u : subs)
+    if (u.wait) c->waits[u.step] = 1;
   *out = c;
   return KQ_OK;
 }
@@ -1009,6 +1086,13 @@ int kq_chain_timeline(kq_chain* c, uint64_t* host, size_t bytes, int* groups, in
   return KQ_OK;
 }
 #endif
+
+int kq_chain_waits(const kq_chain* c, uint8_t* waits, int n) {
+  if (!c || !waits) return KQ_ERR_NULL;
+  if (n != (int)c->waits.size()) return KQ_ERR_SHAPE;
+  for (int j = 0; j < n; ++j) waits[j] = c->waits[j];
+  return KQ_OK;
+}
 
 int kq_chain_query(kq_chain* c) {
   if (!c) return KQ_ERR_NULL;

@@ -993,7 +993,7 @@ __device__ __forceinline__ void chain_wait(const ChainCtl& c, int step, uint32_t
 // written, through the device coherence point.
 template <int QT, int B, bool XF32, bool MF, int NW, int DEPTH, bool CHAIN, class GA>
 __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ctl, int step, uint32_t tag,
-                                           bool wait = true) {
+                                           bool wait = true, int gate = 0) {
   using F = Fmt<QT>;
   constexpr int NCH = F::kChunks, SB = F::kSubBlocks;
   constexpr int XW = 128;                          // 32-bit words per staged (bf16) row
@@ -1083,7 +1083,7 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
 #pragma unroll
     for (int k = 0; k + 1 < DEPTH; ++k) refill(k);
     if constexpr (!DYN) refill(DEPTH - 1);
-    if (wait) chain_wait<!DYN>(*ctl, step, tag);
+    if (wait) chain_wait<!DYN>(*ctl, gate, tag);
     tl_stamp(ctl, step, 1);
     xs.template load<true>(a, c0w, len, 0);
   } else {
@@ -1323,13 +1323,22 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
   // results are invalid and reported either way.)
   if (__builtin_amdgcn_readfirstlane(load_coherent(c.ctl.error)) != 0u) return;
   const uint32_t tag = __builtin_amdgcn_readfirstlane(load_coherent(c.ctl.epoch)) + 1u;
+  // the latest barrier sub-step this workgroup has passed: every sub-step before
+  // it is complete on every workgroup
+  int passed = 0;
   for (int j = 0; j < c.n_steps; ++j) {
     ConstChainStep& st = steps[j];
     const int g = st.grid;
     tl_stamp(&c.ctl, j, 0);
-    // a further weight type of the same step reads the same x as the sub-step
-    // before it and writes other outputs: no wait
-    bool waited = st.wait == 0;
+    // A sub-step reads its x once the barrier of its gate (itself, or for a
+    // sub-step that is no barrier the latest barrier sub-step before it) has
+    // been passed.  Not barriers: a further weight type of the same step (it
+    // reads the same x as the sub-step before it and writes other outputs), and
+    // a step whose buffers meet none of those of the sub-steps since its gate
+    // (KQ_STEP_OVERLAP).  A workgroup that had no work in the gate sub-step has
+    // not passed its barrier yet, so its first block here waits at it.
+    const int gate = st.gate;
+    bool waited = passed >= gate;
     // the step's logical blocks, as a single launch numbers them, grid-stride
     // over the resident workgroups from workgroup st.first on (the launch and
     // st.first are multiples of 8, so every logical block keeps the XCD it would
@@ -1337,16 +1346,23 @@ __global__ void __launch_bounds__(64 * NW) chain_kernel(const ChainArgs c) {
     for (int vb = ((int)blockIdx.x + (int)gridDim.x - st.first) % (int)gridDim.x; vb < g; vb += gridDim.x) {
       const int lblock = (vb & 7) * (g >> 3) + (vb >> 3);
       if (st.type == KQ_Q4_K)
-        waited |= gemv_block<KQ_Q4_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
+        waited |= gemv_block<KQ_Q4_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited,
+                                                                             gate);
       else if (st.type == KQ_Q5_K)
-        waited |= gemv_block<KQ_Q5_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
+        waited |= gemv_block<KQ_Q5_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited,
+                                                                             gate);
       else
-        waited |= gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited);
+        waited |= gemv_block<KQ_Q6_K, B, XF32, MF, NW, KQ_DEPTH, true>(st.a, lblock, &c.ctl, j, tag, !waited,
+                                                                             gate);
     }
-    // the collector of the two-hop wait never skips a step that waits
+    // the collector of the two-hop wait never skips a barrier sub-step
     if constexpr (dyn_units<B, NW, MF>()) {
-      if (blockIdx.x == 0 && j > 0 && st.wait && !waited) chain_collect(c.ctl, j - 1, tag);
+      if (blockIdx.x == 0 && j > 0 && st.wait && !waited) {
+        chain_collect(c.ctl, j - 1, tag);
+        waited = true;
+      }
     }
+    if (waited && gate > passed) passed = gate;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's y / partial stores are done
     __syncthreads();
     if (threadIdx.x == 0) store_coherent(c.ctl.arrive + (size_t)j * c.ctl.groups + blockIdx.x, tag);

@@ -91,8 +91,9 @@ struct ChainStep {
   GemvArgs a;
   int32_t type;
   int32_t grid;
-  int32_t wait;
+  int32_t wait;    // a barrier sub-step: its workgroups wait until every earlier sub-step is complete
   int32_t first;
+  int32_t gate;    // the latest barrier sub-step at or before this one (0: none)
 };
 
 struct ChainArgs {

@@ -20,6 +20,7 @@ KQ_X_F32, KQ_X_BF16 = 0, 1
 KQ_MAX_BATCH, KQ_MAX_BATCH_F32, KQ_MAX_PROJ = 16, 8, 8
 KQ_EPI_NONE, KQ_EPI_SWIGLU, KQ_EPI_SIGMOID, KQ_EPI_RESIDUAL, KQ_EPI_HEADNORM = 0, 1, 2, 3, 4
 KQ_HEAD_ROWS = 128
+KQ_STEP_OVERLAP = 1               # kq_chain_step.flags: skip the step barrier where buffers are independent
 TYPE_ID = {"q4k": KQ_Q4_K, "q5k": KQ_Q5_K, "q6k": KQ_Q6_K}
 SB_BYTES = {"q4k": 144, "q5k": 176, "q6k": 210}
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN", 4: "KQ_ERR_BATCH",
@@ -34,7 +35,7 @@ EXPORTS = ("kq_abi_version", "kq_status_str", "kq_init", "kq_gemv_workspace_byte
            "kq_gather_rows", "kq_stream_read",
            "kq_repack_swiglu",
            "kq_gemv_swiglu", "kq_chain_create", "kq_chain_run",
-           "kq_chain_query", "kq_chain_status", "kq_chain_destroy")
+           "kq_chain_waits", "kq_chain_query", "kq_chain_status", "kq_chain_destroy")
 
 
 class ChainStep(ctypes.Structure):
@@ -44,7 +45,7 @@ class ChainStep(ctypes.Structure):
                 ("y", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("y16", ctypes.c_void_p * KQ_MAX_PROJ), ("ldy16", ctypes.c_int64 * KQ_MAX_PROJ),
                 ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("epilogue", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("head_eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("head_eps", ctypes.c_float), ("flags", ctypes.c_int32),
                 ("types", ctypes.c_int32 * KQ_MAX_PROJ)]
 
 
@@ -113,6 +114,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).restype = ci
         L.kq_chain_run.argtypes = [vp, vp]
         L.kq_chain_run.restype = ci
+        L.kq_chain_waits.argtypes = [vp, ctypes.POINTER(ctypes.c_uint8), ci]
+        L.kq_chain_waits.restype = ci
         _lib = L
     return _lib
 
@@ -301,12 +304,14 @@ def kq_gather_rows(qtype, w: torch.Tensor, rows: int, cols: int, ids: torch.Tens
                                                   out.data_ptr(), out.stride(0), _stream(stream)))
 
 
-def kq_chain_create(steps, xtype: int, batch: int) -> int:
+def kq_chain_create(steps, xtype: int, batch: int, overlap: bool = False) -> int:
     """steps: sequence of (qtype, ws, rows, cols, x, ys[, epilogue[, rms_eps[, head_eps[, y16s[, types]]]]]) as
     kq_gemv_multi and kq_gemv_fused take them, the epilogue packed four bits per segment; qtype may be a list
-    of per-segment types (a mixed-type step), or `types` gives them; returns the handle."""
+    of per-segment types (a mixed-type step), or `types` gives them; overlap: every step carries
+    KQ_STEP_OVERLAP (it skips the step barrier where its buffers are independent); returns the handle."""
     arr = (ChainStep * len(steps))()
     for st, step in zip(arr, steps):
+        st.flags = KQ_STEP_OVERLAP if overlap else 0
         qtype, ws, rows, cols, x, ys = step[:6]
         st.epilogue = step[6] if len(step) > 6 else KQ_EPI_NONE
         st.rms_eps = step[7] if len(step) > 7 else 0.0
@@ -336,6 +341,13 @@ def kq_chain_run(handle: int, stream=None) -> None:
     _check("kq_chain_run", lib().kq_chain_run(handle, _stream(stream)))
 
 
+def kq_chain_waits(handle: int, n_steps: int) -> list:
+    """Per step: True if it waits at the step barrier, False if it overlaps the steps before it."""
+    w = (ctypes.c_uint8 * n_steps)()
+    _check("kq_chain_waits", lib().kq_chain_waits(handle, w, n_steps))
+    return [bool(v) for v in w]
+
+
 def kq_chain_query(handle: int) -> int:
     """KQ_OK, or KQ_ERR_TIMEOUT once a run's wait has given up (no device synchronisation); does not raise."""
     return lib().kq_chain_query(handle)
@@ -356,18 +368,21 @@ def kq_chain_destroy(handle: int) -> None:
 class Chain:
     """A chain plan that keeps the tensors of its steps alive; run() enqueues one run."""
 
-    def __init__(self, steps, batch: int):
+    def __init__(self, steps, batch: int, overlap: bool = False):
         self.steps = list(steps)
         xt = {_xtype(s[4]) for s in self.steps}
         if len(xt) != 1:
             raise ValueError("every step of a chain takes the same activation type")
-        self.handle = kq_chain_create(self.steps, xt.pop(), batch)
+        self.handle = kq_chain_create(self.steps, xt.pop(), batch, overlap)
 
     def run(self, stream=None) -> None:
         kq_chain_run(self.handle, stream)
 
     def status(self) -> int:
         return kq_chain_status(self.handle)
+
+    def waits(self) -> list:
+        return kq_chain_waits(self.handle, len(self.steps))
 
     def query(self) -> int:
         return kq_chain_query(self.handle)

@@ -289,3 +289,69 @@ def test_chain_p4_layer(batch):
         _, yo, ao = oracle_rows(qtype, g, idx, cols, x)
         check_y(y, yo, ao, f"chain p4 step {j} B={batch}")
     ch.close()
+
+
+@pytest.mark.parametrize("batch,xdtype", [(1, "bf16"), (2, "bf16"), (8, "bf16"), (16, "bf16"), (4, "f32")])
+def test_chain_overlap_of_independent_steps(batch, xdtype):
+    """KQ_STEP_OVERLAP on steps whose buffers are all distinct: no step after the first waits at the step
+    barrier, and every step still gives its single launch's result bitwise (and the oracle's within the
+    tolerance), on two runs in a row."""
+    say(f"case chain overlap independent B={batch} x={xdtype}")
+    steps, hosts = _independent_steps(MIXED + MIXED[:3], batch, xdtype, f"ovl{batch}{xdtype}")
+    ch = kq.Chain(steps, batch, overlap=True)
+    assert ch.waits() == [True] + [False] * (len(steps) - 1)
+    for rep in range(2):
+        for s in steps:
+            for y in s[5]:
+                y.fill_(SENTINEL)
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        _check_steps(steps, hosts, _singles(steps), f"overlap B={batch} {xdtype} run {rep}")
+    ch.close()
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_chain_overlap_keeps_dependencies(batch):
+    """KQ_STEP_OVERLAP with buffers shared between steps (fp32 activations, so an output can be a later
+    step's input or overwrite an earlier step's input):
+      A: own x -> yA;  B: own x -> yB;  C: x = yA (reads A's output: waits);
+      D: own x -> yD (meets nothing still running: overlaps);  E: x = yB (B finished before C read: overlaps);
+      F: own x -> writes D's x in place (D may still be reading it: waits).
+    Each step must equal its single launch on the input it should have read."""
+    say(f"case chain overlap dependencies B={batch}")
+    f32 = dict(dtype=torch.float32, device=DEV)
+
+    def xg(cols, tag):
+        return synth.gen_x(batch, cols, synth.seed_of("ovl-dep-x", tag, batch), "f32").to(DEV)
+
+    specs = {"A": ("q4k", (512,), 1024), "B": ("q6k", (768,), 512), "C": ("q5k", (256,), 512),
+             "D": ("q4k", (300, 212), 256), "E": ("q6k", (256,), 768), "F": ("q4k", (256,), 512)}
+    W = {k: _weights(q, p, c, f"ovl-dep{k}")[1] for k, (q, p, c) in specs.items()}
+    xa, xb, xd0, xf = xg(1024, "a"), xg(512, "b"), xg(256, "d"), xg(512, "f")
+    xd = xd0.clone()
+    Y = {k: [torch.full((batch, r), SENTINEL, **f32) for r in p] for k, (q, p, c) in specs.items() if k != "F"}
+    Y["F"] = [xd]                                     # F overwrites D's input
+    X = {"A": xa, "B": xb, "C": Y["A"][0], "D": xd, "E": Y["B"][0], "F": xf}
+    order = "ABCDEF"
+    steps = [(specs[k][0], W[k], list(specs[k][1]), specs[k][2], X[k], Y[k]) for k in order]
+    ch = kq.Chain(steps, batch, overlap=True)
+    assert ch.waits() == [True, False, True, False, False, True]
+    for rep in range(3):
+        xd.copy_(xd0)
+        for k in "ABCDE":
+            for y in Y[k]:
+                y.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        inputs = {"A": xa, "B": xb, "C": Y["A"][0], "D": xd0, "E": Y["B"][0], "F": xf}
+        for k in order:
+            q, parts, cols = specs[k]
+            ref = [torch.empty((batch, r), **f32) for r in parts]
+            kq.kq_gemv_multi(q, W[k], list(parts), cols, inputs[k], ref)
+            torch.cuda.synchronize()
+            for i, (y, y1) in enumerate(zip(Y[k], ref)):
+                assert torch.equal(y, y1), f"overlap with dependencies, run {rep} step {k} part {i}"
+    ch.close()

@@ -131,3 +131,36 @@ def test_q4km_qkv_full_size(batch):
         _, yo, ao = oracle_rows(t, g, idx, spec.cols, x)
         check_y(y[:, torch.as_tensor(idx, device=DEV)].cpu().numpy(), yo, ao, f"Q4_K_M QKV segment {i} B={batch}")
     ch.close()
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_mixed_step_reads_previous_output(batch):
+    """A mixed step whose x is the previous step's output: the workgroups of its later sub-steps (which start
+    on the workgroups after the first sub-step's) must also wait until the previous step is complete, not
+    only those of its first sub-step.  The previous step's output is reset to a sentinel before each run, so
+    a read that comes too early shows."""
+    say(f"case mixed step reading the previous output B={batch}")
+    cols = 1024
+    g0 = synth.gen_weights("q6k", cols, 64 * 256, synth.seed_of("mixed-prev-0"))
+    w0 = kq.repack("q6k", g0.to(DEV), cols, 64 * 256)
+    x0 = synth.gen_x(batch, 64 * 256, synth.seed_of("mixed-prev-x", batch), "f32").to(DEV)
+    y0 = torch.empty((batch, cols), device=DEV)
+    types, parts = ["q4k", "q6k"], [64, 64]
+    gs, ws = _segments(types, parts, cols, f"prev{batch}")
+    ys = [torch.empty((batch, r), device=DEV) for r in parts]
+    ch = kq.Chain([("q6k", [w0], [cols], 64 * 256, x0, [y0]), (types, ws, parts, cols, y0, ys)], batch)
+    for rep in range(4):
+        y0.fill_(SENTINEL)
+        for y in ys:
+            y.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        ch.run()
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        for t, idx in _by_type(types):
+            ref = [torch.empty((batch, parts[i]), device=DEV) for i in idx]
+            kq.kq_gemv_fused(t, [ws[i] for i in idx], [parts[i] for i in idx], cols, y0, ref)
+            torch.cuda.synchronize()
+            for i, r in zip(idx, ref):
+                assert torch.equal(ys[i], r), f"run {rep} segment {i} ({t}) read its x before it was complete"
+    ch.close()
