@@ -359,8 +359,13 @@ int kq_gather_rows(int type, const void *w, int64_t rows, int64_t cols, const in
  * drains.  Each step of such an overlapping run has a workspace region of its
  * own, so the chain's device memory grows with the run's length; a run is cut
  * by a wait once its regions would pass 512 MiB.  A step that meets such a
- * buffer waits as without the flag, and results are bitwise those of the same
- * chain without the flag.  This is for sequences whose steps read inputs that
+ * buffer waits as without the flag.  A step that skips the barrier and has
+ * fewer than 8 units (64 rows x 256 columns) per CU takes one whole 64-row
+ * tile per workgroup, so none of its tiles is handed over between workgroups:
+ * its results are then those of its single launch planned the same way
+ * (KQ_WHOLE_TILES_BELOW=8) and within the GEMV's tolerance of the default
+ * plan; every other step's results are bitwise those of the same chain
+ * without the flag.  This is for sequences whose steps read inputs that
  * are already in memory, such as GEMVs with activations of their own run back
  * to back; in a decoder, where each projection reads the previous one's
  * output, every step still waits.  Steps without the flag always wait.

@@ -215,7 +215,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
                      int xtype, int64_t ldx, int batch, float* const* y, const int64_t* ldy, void* const* y16,
                      const int64_t* ldy16, int cus,
                      int64_t max_grid, int force_nw, bool single, uint32_t epi, float rms_eps, float head_eps,
-                     Plan* out) {
+                     Plan* out, int64_t whole_below = -1) {
   const int64_t n_cols = cols / 256;
   const bool norm = rms_eps > 0.0f;
   GemvArgs a{};
@@ -288,7 +288,7 @@ static int plan_gemv(int type, int n, const void* const* w, const int64_t* rows,
   const int64_t n_win = (n_cols + max_cols - 1) / max_cols;
   // small steps (fewer units than `whole_tiles_below()` per CU): one whole tile per workgroup, so no
   // tile is split between workgroups
-  const int64_t small = whole_tiles_below();
+  const int64_t small = whole_below >= 0 ? whole_below : whole_tiles_below();
   const int forced_r = n_units < (int64_t)cus * small && n_win == 1 ? 1 : aligned_tiles();
   if (((srows >= windows_from_batch() && n_win > 1) || forced_r > 0) && tiles <= kMaxGroups &&
       n_win * tiles <= 2 * (int64_t)kMaxGroups) {
@@ -527,6 +527,7 @@ struct SubStep {
   bool wait = true;
   int step = 0;          // index of the chain step it belongs to
   bool overlap = false;  // the step carries KQ_STEP_OVERLAP
+  bool overlapped = false;  // ... and skips the step barrier (mark_overlaps)
 };
 
 // Split a chain step into one sub-step per weight type (segment i's type is
@@ -845,6 +846,11 @@ static void out_ranges(const SubStep& u, int batch, std::vector<ByteRange>& out)
 
 // Largest workspace of one run of overlapping steps (their regions are disjoint).
 constexpr size_t kMaxOverlapWorkspace = (size_t)512 << 20;
+// Units per CU below which a step that skips the barrier takes whole tiles per workgroup.  Measured on
+// the sweep's 209 GEMVs overlapped (QKV 5.6 and O 5.0 units per CU, the rest 38 or more): B = 1
+// 3.00-3.01 ms against 3.19-3.25 ms with split tiles, B = 8 4.30-4.32 against 4.57-4.59 ms; 40 (down
+// too) gave the same.
+constexpr int64_t kOverlapWholeTilesBelow = 8;
 
 // Which steps skip the step barrier.  The steps that may still be running when
 // a step starts are those since the last step that waited (a wait orders a
@@ -880,6 +886,7 @@ static void mark_overlaps(std::vector<SubStep>& subs, const std::vector<Plan>& p
       run_ws = 0;
     }
     subs[f].wait = !free_to_run;
+    for (int k = f; k <= l; ++k) subs[k].overlapped = free_to_run;
     run_x.insert(run_x.end(), xs.begin(), xs.end());
     run_out.insert(run_out.end(), outs.begin(), outs.end());
     run_ws += ws;
@@ -951,6 +958,23 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
   size_t lds = 0;
   int rc = plan_all(kMaxGroups, &lds);
   if (rc == KQ_ERR_RANGE && nw == 4 && srows <= 8) rc = plan_all(kMaxGroups, &lds);
+  // Steps that skip the barrier and have fewer than kOverlapWholeTilesBelow units per CU take one
+  // whole tile per workgroup: no tile is split, so no hand-off (partials, arrival counter, the last
+  // arriver's reads) delays the workgroup's next step.  The step then streams on fewer CUs, which costs
+  // nothing here since the other CUs run other steps meanwhile.  The workspace regions only shrink, so
+  // the overlap decisions stand.
+  if (rc == KQ_OK) {
+    mark_overlaps(subs, plans, batch, esize);
+    const int64_t whole = whole_tiles_below() > kOverlapWholeTilesBelow ? whole_tiles_below()
+                                                                          : kOverlapWholeTilesBelow;
+    for (int j = 0; j < n_sub && rc == KQ_OK; ++j) {
+      const SubStep& u = subs[j];
+      if (!u.overlapped) continue;
+      rc = plan_gemv(u.type, u.n, u.w, u.rows, u.cols, u.x, xtype, u.ldx, batch, u.y, u.ldy, u.y16, u.ldy16,
+                     cus, kMaxGroups, nw, false, u.epi, u.rms_eps, u.head_eps, &plans[j], whole);
+      if (rc == KQ_OK && plans[j].lds > lds) lds = plans[j].lds;
+    }
+  }
   int64_t groups = (int64_t)cus * (8 / nw);
   int occ = 0;
   if (rc == KQ_OK &&
@@ -965,8 +989,6 @@ int kq_chain_create(int n_steps, const kq_chain_step* steps, int xtype, int batc
     delete c;
     return rc;
   }
-
-  mark_overlaps(subs, plans, batch, esize);
 
   const size_t steps_bytes = round_up((size_t)n_sub * sizeof(ChainStep), 256);
   // control words: arrive[n_sub][groups], done[n_sub][kDoneReplicas][16] (one 64-byte line per replica),

@@ -292,14 +292,20 @@ def test_chain_p4_layer(batch):
 
 
 @pytest.mark.parametrize("batch,xdtype", [(1, "bf16"), (2, "bf16"), (8, "bf16"), (16, "bf16"), (4, "f32")])
-def test_chain_overlap_of_independent_steps(batch, xdtype):
+@pytest.mark.parametrize("same_plans", [True, False])
+def test_chain_overlap_of_independent_steps(batch, xdtype, same_plans, monkeypatch):
     """KQ_STEP_OVERLAP on steps whose buffers are all distinct: no step after the first waits at the step
-    barrier, and every step still gives its single launch's result bitwise (and the oracle's within the
-    tolerance), on two runs in a row."""
-    say(f"case chain overlap independent B={batch} x={xdtype}")
+    barrier.  Overlapping steps with fewer than 8 units per CU (all of these) take whole tiles per
+    workgroup; with KQ_WHOLE_TILES_BELOW=8 the single launches (and the chain's first step) are planned the
+    same way, and every step gives its single launch's result bitwise.  Either way every output is within
+    the oracle's bound, and two runs in a row give the same bits."""
+    if same_plans:
+        monkeypatch.setenv("KQ_WHOLE_TILES_BELOW", "8")
+    say(f"case chain overlap independent B={batch} x={xdtype} same plans {same_plans}")
     steps, hosts = _independent_steps(MIXED + MIXED[:3], batch, xdtype, f"ovl{batch}{xdtype}")
     ch = kq.Chain(steps, batch, overlap=True)
     assert ch.waits() == [True] + [False] * (len(steps) - 1)
+    first = None
     for rep in range(2):
         for s in steps:
             for y in s[5]:
@@ -307,18 +313,34 @@ def test_chain_overlap_of_independent_steps(batch, xdtype):
         ch.run()
         torch.cuda.synchronize()
         assert ch.status() == 0
-        _check_steps(steps, hosts, _singles(steps), f"overlap B={batch} {xdtype} run {rep}")
+        if same_plans:
+            _check_steps(steps, hosts, _singles(steps), f"overlap B={batch} {xdtype} run {rep}")
+        else:
+            got = [[y.clone() for y in s[5]] for s in steps]
+            if first is None:
+                first = got
+                for j, ((qtype, ws, parts, cols, x, ys), (gs, xh)) in enumerate(zip(steps, hosts)):
+                    for i, (g, r, y) in enumerate(zip(gs, parts, ys)):
+                        assert (y[:, r:].cpu() == SENTINEL).all(), f"overlap step {j} part {i}: wrote outside"
+                        yo, ao = O.gemv(qtype, r, cols, g.numpy(), x_host(xh))
+                        check_y(y[:, :r].cpu().numpy(), yo, ao, f"overlap B={batch} {xdtype} step {j} part {i}")
+            else:
+                for j, (a, b) in enumerate(zip(first, got)):
+                    for i, (ya, yb) in enumerate(zip(a, b)):
+                        assert torch.equal(ya, yb), f"overlap step {j} part {i}: runs differ"
     ch.close()
 
 
 @pytest.mark.parametrize("batch", [1, 3])
-def test_chain_overlap_keeps_dependencies(batch):
+def test_chain_overlap_keeps_dependencies(batch, monkeypatch):
     """KQ_STEP_OVERLAP with buffers shared between steps (fp32 activations, so an output can be a later
     step's input or overwrite an earlier step's input):
       A: own x -> yA;  B: own x -> yB;  C: x = yA (reads A's output: waits);
       D: own x -> yD (meets nothing still running: overlaps);  E: x = yB (B finished before C read: overlaps);
       F: own x -> writes D's x in place (D may still be reading it: waits).
-    Each step must equal its single launch on the input it should have read."""
+    Each step must equal its single launch on the input it should have read (all steps planned with whole
+    tiles per workgroup, as the overlapping ones are)."""
+    monkeypatch.setenv("KQ_WHOLE_TILES_BELOW", "8")
     say(f"case chain overlap dependencies B={batch}")
     f32 = dict(dtype=torch.float32, device=DEV)
 
