@@ -150,7 +150,9 @@ struct XStage {
   // The SB items of one (column, row) sit in SB consecutive lanes (n and every
   // round's start are multiples of SB), so their squares are added by a fixed
   // butterfly and every workgroup that stages a column gets the same bits for it.
-  template <bool WITH_T>
+  // WITH_T: T[(ic * SB + g) * TS + b] = the sub-block's sum of staged row b
+  // (TS = B on the dot2 path; the matrix-core path pads each item to NB * 4).
+  template <bool WITH_T, int TS = B>
   __device__ __forceinline__ void store(uint8_t* X, float* T, float* Q2, int len, int r) const {
     const int n = len * BU * SB;
 #pragma unroll
@@ -220,8 +222,8 @@ struct XStage {
             }
           }
           if constexpr (WITH_T) {
-            T[(ic * SB + g) * B + b] = th;
-            T[(ic * SB + g) * B + b + BU] = tl;
+            T[(ic * SB + g) * TS + b] = th;
+            T[(ic * SB + g) * TS + b + BU] = tl;
           }
         } else {
           u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * 2);
@@ -231,7 +233,7 @@ struct XStage {
             xl[e] = v[j][e];
             if constexpr (WITH_T) t = tsum(v[j][e], t);
           }
-          if constexpr (WITH_T) T[(ic * SB + g) * B + b] = t;
+          if constexpr (WITH_T) T[(ic * SB + g) * TS + b] = t;
         }
       }
     }
@@ -312,8 +314,8 @@ __device__ __forceinline__ void process_unit(const u32x4* buf, uint32_t d6, cons
 //              batch rows 4..7).
 // A sub-block is 4 (Q6_K: 2) such instructions accumulating in place, then
 // scaled on the VALU as in the dot2 path.  For Q4_K/Q5_K the activation sum X
-// of each column's sub-blocks is the same instruction sequence with every
-// operand 1, computed once per column and sub-block while staging.
+// of each column's sub-blocks is taken while staging, as on the dot2 path (the
+// operands are exact, so X need not round like the products).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -387,64 +389,6 @@ __device__ __forceinline__ int a_operand_offset(int lane, int gb, int ic, int x_
   const int b = 4 * gb + (lane & 3);
   const bool active = ((lane & 15) >> 2) == (lane >> 4) && b < B;
   return active ? x_base + (ic * B + b) * 528 : z_base;
-}
-
-// T for the matrix-core path of Q4_K/Q5_K, from the staged activations (after a
-// barrier): T[ic][g][gb][b'] = the sub-block's activation sum, as the same
-// instruction sequence computes it with every operand 1.  One chain serves four
-// items: lane group j = lane / 16 takes item 4c + j's activations into its block
-// of the operand.  A wavefront runs two chains interleaved.
-template <int QT, int B, int NW>
-__device__ __forceinline__ void stage_T_mfma(uint8_t* lds, int len, int wid, int lane) {
-  using F = Fmt<QT>;
-  using L = MfmaLds<QT, B>;
-  constexpr int NB = L::NB, SB = F::kSubBlocks, KB = F::kSubW / 8;
-  constexpr int H = NB <= 2 ? 2 : 1;                  // chains in flight (registers allow two up to NB 2)
-  const int t_base = len * L::kXCol, z_base = t_base + len * L::kTCol;
-  static_assert(QT != KQ_Q6_K, "Q6_K has no mins and needs no activation sums");
-  const uint32_t kc = 0x3F803F80u;   // bf16 (1, 1)
-  const bf16x8 bconst = __builtin_bit_cast(bf16x8, u32x4{kc, kc, kc, kc});
-  const int nt = len * SB, nch = (nt + 3) / 4;
-  for (int c0 = wid; c0 < nch; c0 += H * NW) {
-    int it[H];
-    const uint8_t* ap[H][NB];
-    f32x4 t[H][NB];
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      const int ch = min(c0 + h * NW, nch - 1);
-      it[h] = min(4 * ch + (lane >> 4), nt - 1);
-      const int ic = it[h] / SB, g = it[h] - ic * SB;
-#pragma unroll
-      for (int gb = 0; gb < NB; ++gb) {
-        ap[h][gb] = lds + a_operand_offset<B>(lane, gb, ic, 0, z_base) + g * F::kSubW * 2;
-      }
-    }
-    bf16x8 av[H][NB][KB], bc[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) bc[kb] = bconst;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int h = 0; h < H; ++h)
-#pragma unroll
-        for (int gb = 0; gb < NB; ++gb) av[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[h][gb] + kb * 16);
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      if constexpr (NB == 1) {
-        mfma_chain<KB>(t[h][0], av[h][0], bc);
-      } else {
-#pragma unroll
-        for (int gb = 0; gb + 1 < NB; gb += 2) mfma_chain2<KB>(t[h][gb], t[h][gb + 1], av[h][gb], av[h][gb + 1], bc);
-        if constexpr (NB % 2 == 1) mfma_chain<KB>(t[h][NB - 1], av[h][NB - 1], bc);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < H; ++h)
-      if (c0 + h * NW < nch && 4 * (c0 + h * NW) + (lane >> 4) < nt && (lane & 15) == 0)
-#pragma unroll
-        for (int gb = 0; gb < NB; ++gb)
-          *reinterpret_cast<f32x4*>(lds + t_base + (it[h] * NB + gb) * 16) = t[h][gb];
-  }
 }
 
 // One unit on the matrix cores: ap[gb] are this lane's A-operand pointers for
@@ -1096,17 +1040,18 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
   }
   {
     uint8_t* Xb = reinterpret_cast<uint8_t*>(lds_words);
-    xs.template store<!MF && TSB != 0>(Xb, T, Q2, len, 0);
+    // the sub-block sums: after the dot2 path's staged rows, or in the matrix-core path's T block
+    constexpr int TS = MF ? MfmaLds<QT, B>::NB * 4 : B;
+    float* Ts = MF ? reinterpret_cast<float*>(Xb + len * MfmaLds<QT, B>::kXCol) : T;
+    xs.template store<TSB != 0, TS>(Xb, Ts, Q2, len, 0);
     const int nr = XStage<QT, B, XF32, NW, kRS>::rounds(len);
     for (int r = 1; r < nr; ++r) {
       xs.template load<CHAIN>(a, c0w, len, r);
-      xs.template store<!MF && TSB != 0>(Xb, T, Q2, len, r);
+      xs.template store<TSB != 0, TS>(Xb, Ts, Q2, len, r);
     }
     if constexpr (MF) {
       const int z_base = len * MfmaLds<QT, B>::kPerCol;
       if (threadIdx.x < 32) *reinterpret_cast<u32x4*>(Xb + z_base + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
-      __syncthreads();
-      if constexpr (QT != KQ_Q6_K) stage_T_mfma<QT, B, NW>(Xb, len, wid, lane);
     }
   }
   __syncthreads();
