@@ -150,9 +150,12 @@ struct XStage {
   // The SB items of one (column, row) sit in SB consecutive lanes (n and every
   // round's start are multiples of SB), so their squares are added by a fixed
   // butterfly and every workgroup that stages a column gets the same bits for it.
-  // WITH_T: T[(ic * SB + g) * TS + b] = the sub-block's sum of staged row b
-  // (TS = B on the dot2 path; the matrix-core path pads each item to NB * 4).
-  template <bool WITH_T, int TS = B>
+  // WITH_T: the sub-block's sum t of staged row b.  Dot2 path (TB false):
+  // T[(ic * SB + g) * TS + b] = t with TS = B.  Matrix-core path (TB): t as three
+  // bf16 parts hi + mid + lo (each the rounding of what the earlier parts leave;
+  // the differences are exact, so the parts hold t's 24 bits), part s at byte
+  // ((ic * 3 + s) * TS + b) * 16 + 2 g of T, TS = NB * 4 rows of 8 sub-blocks.
+  template <bool WITH_T, int TS = B, bool TB = false>
   __device__ __forceinline__ void store(uint8_t* X, float* T, float* Q2, int len, int r) const {
     const int n = len * BU * SB;
 #pragma unroll
@@ -185,6 +188,20 @@ struct XStage {
         const int g = i % SB, q = i / SB, b = q % BU, ic = q / BU;
         const uint32_t kc = 0x3F803F80u;   // bf16 (1, 1)
         // T: the sub-block's activation sum X, per staged row
+        auto put_t = [&](int row, float v) {
+          if constexpr (TB) {
+            uint8_t* tb = reinterpret_cast<uint8_t*>(T) + ((ic * 3) * TS + row) * 16 + g * 2;
+            const uint32_t h = bf16_bits(v);
+            const float r1 = v - __uint_as_float(h << 16);
+            const uint32_t m = bf16_bits(r1);
+            const uint32_t l = bf16_bits(r1 - __uint_as_float(m << 16));
+            *reinterpret_cast<uint16_t*>(tb) = (uint16_t)h;
+            *reinterpret_cast<uint16_t*>(tb + TS * 16) = (uint16_t)m;
+            *reinterpret_cast<uint16_t*>(tb + 2 * TS * 16) = (uint16_t)l;
+          } else {
+            T[(ic * SB + g) * TS + row] = v;
+          }
+        };
         auto tsum = [&](const u32x4& w, float t) {
           t = dot2_bf16(kc, w.x, t);
           t = dot2_bf16(kc, w.y, t);
@@ -222,8 +239,8 @@ struct XStage {
             }
           }
           if constexpr (WITH_T) {
-            T[(ic * SB + g) * TS + b] = th;
-            T[(ic * SB + g) * TS + b + BU] = tl;
+            put_t(b, th);
+            put_t(b + BU, tl);
           }
         } else {
           u32x4* xl = reinterpret_cast<u32x4*>(X + (ic * B + b) * RS + g * F::kSubW * 2);
@@ -233,7 +250,7 @@ struct XStage {
             xl[e] = v[j][e];
             if constexpr (WITH_T) t = tsum(v[j][e], t);
           }
-          if constexpr (WITH_T) T[(ic * SB + g) * TS + b] = t;
+          if constexpr (WITH_T) put_t(b, t);
         }
       }
     }
@@ -339,6 +356,13 @@ __device__ __forceinline__ void mfma_chain<4>(f32x4& s, const bf16x8* a, const b
                : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
 }
 template <>
+__device__ __forceinline__ void mfma_chain<3>(f32x4& s, const bf16x8* a, const bf16x8* b) {
+  asm volatile("s_nop 1\n\t" KQ_MF("%0", "%1", "%4", "0") KQ_MF("%0", "%2", "%5", "%0") KQ_MF("%0", "%3", "%6", "%0")
+                   "s_nop 7"
+               : "=&v"(s)
+               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(b[0]), "v"(b[1]), "v"(b[2]));
+}
+template <>
 __device__ __forceinline__ void mfma_chain<2>(f32x4& s, const bf16x8* a, const bf16x8* b) {
   asm volatile("s_nop 1\n\t" KQ_MF("%0", "%1", "%3", "0") KQ_MF("%0", "%2", "%4", "%0") "s_nop 7"
                : "=&v"(s)
@@ -372,14 +396,16 @@ __device__ __forceinline__ void mfma_chain2<2>(f32x4& s0, f32x4& s1, const bf16x
 // Byte offsets inside the workgroup's LDS for the matrix-core path:
 //   X [ic][b][256] bf16 in rows of kXRow = 528 bytes (the 16-byte pad puts the
 //   four batch rows one instruction reads in different LDS banks), then
-//   (Q4_K/Q5_K) T [ic][g][NB][4] floats, the sub-block activation sums, then Z,
-//   512 zero bytes that the inactive operand lanes read.
+//   (Q4_K/Q5_K) T [ic][3][NB * 4][8] bf16, the sub-block activation sums of each
+//   staged row as three exact bf16 parts (the A operands of the mins' product),
+//   then Z, 512 zero bytes that the inactive operand lanes read.
 template <int QT, int B>
 struct MfmaLds {
   static constexpr int NB = (B + 3) / 4;                       // operand sets of 4 batch rows
   static constexpr int kXRow = 528;                            // bytes per staged row of x
   static constexpr int kXCol = B * kXRow;                      // bytes of x per column
-  static constexpr int kTCol = QT == KQ_Q6_K ? 0 : Fmt<QT>::kSubBlocks * NB * 16;  // bytes of T per column
+  static constexpr int kTPart = NB * 4 * 16;                  // bytes of one part of T per column
+  static constexpr int kTCol = QT == KQ_Q6_K ? 0 : 3 * kTPart;  // bytes of T per column
   static constexpr int kPerCol = kXCol + kTCol;
 };
 
@@ -391,44 +417,69 @@ __device__ __forceinline__ int a_operand_offset(int lane, int gb, int ic, int x_
   return active ? x_base + (ic * B + b) * 528 : z_base;
 }
 
+// T-operand byte offset of this lane for operand set gb at column ic, and the
+// stride between T's three parts (0 for a lane that reads the zero block).
+template <int QT, int B>
+__device__ __forceinline__ int t_operand_offset(int lane, int gb, int ic, int t_base, int z_base, int& stride) {
+  const int b = 4 * gb + (lane & 3);
+  const bool active = ((lane & 15) >> 2) == (lane >> 4) && b < B;
+  stride = active ? MfmaLds<QT, B>::kTPart : 0;
+  return active ? t_base + ic * MfmaLds<QT, B>::kTCol + b * 16 : z_base;
+}
+
+// The mins of a Q4_K/Q5_K super-block as the B operand of the mins' product:
+// lane l supplies its own row's m_0..m_7 times p, the power of two (with sign)
+// of dmin, which keeps each m_g * p exact in bf16 and the product's magnitude
+// that of dmin * m_g * X (no overflow where the output itself is in range).
+// dmin = p * f with f = dmin's mantissa in [1, 2); f = 1 when dmin is zero.
+template <int QT>
+__device__ __forceinline__ bf16x8 sb_mins_operand(const u32x4* c, float& f) {
+  const u32x4 h = c[0];
+  const uint32_t u = __float_as_uint(f16_bits_to_f32(h.x >> 16));
+  const float p = __uint_as_float(u & 0xFF800000u);
+  f = __uint_as_float((u & 0x007FFFFFu) | 0x3F800000u);
+  const uint32_t lo = h.z & 0x3F3F3F3Fu;
+  const uint32_t hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+  auto pk = [p](uint32_t v, int i) {
+    return pk_bf16((float)((v >> (16 * i)) & 0xFFu) * p, (float)((v >> (16 * i + 8)) & 0xFFu) * p);
+  };
+  return __builtin_bit_cast(bf16x8, u32x4{pk(lo, 0), pk(lo, 1), pk(hi, 0), pk(hi, 1)});
+}
+
 // One unit on the matrix cores: ap[gb] are this lane's A-operand pointers for
-// the unit's column, Tc the column's T block.  The operands and T of sub-block
-// g+1 are read from LDS while sub-block g is on the matrix core, so the read
-// latency is not paid per instruction.  LEAN (chain kernels, which hold the code
-// of every weight type and would otherwise spill registers at batch 5..8): with
-// two operand sets, each sub-block's operands are read just before use.
+// the unit's column; tp[gb] / ts[gb] its T-operand pointers and part strides
+// (Q4_K/Q5_K).  Each sub-block's products are scaled by d*sc_g on the VALU; the
+// mins' term, sum over g of dmin*m_g*X_g, is one more product per operand set:
+// A = the staged sums X_g of the column (three exact bf16 parts, chained), B =
+// the row's eight m_g times dmin's power of two, then acc -= dmin's mantissa
+// times that.  The operands of sub-block g+1 are read from LDS while sub-block
+// g is on the matrix core, so the read latency is not paid per instruction.
+// LEAN (chain kernels, which hold the code of every weight type and would
+// otherwise spill registers at batch 5..8): with two operand sets, each
+// sub-block's operands are read just before use.
 template <int QT, int B, bool LEAN>
 __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6, const uint8_t* const* ap,
-                                                  const float* Tc, float* acc) {
+                                                  const uint8_t* const* tp, const int* ts, float* acc) {
   using F = Fmt<QT>;
   constexpr int SB = F::kSubBlocks, NP = F::kPairs, KB = F::kSubW / 8, NB = MfmaLds<QT, B>::NB;
   constexpr bool MINS = QT != KQ_Q6_K;
   float ca[SB], cm[SB];
   sb_coeffs<QT>(buf, d6, ca, cm);
-  auto scale = [&](int g, int gb, const f32x4& S, const f32x4& t) {
+  auto scale = [&](int g, int gb, const f32x4& S) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * gb + r < B) {
-        float& v = acc[4 * gb + r];
-        v = __builtin_fmaf(ca[g], S[r], v);
-        if constexpr (MINS) v = __builtin_fmaf(-cm[g], t[r], v);
-      }
-    }
+    for (int r = 0; r < 4; ++r)
+      if (4 * gb + r < B) acc[4 * gb + r] = __builtin_fmaf(ca[g], S[r], acc[4 * gb + r]);
   };
   uint32_t pr[NP];
   if constexpr (LEAN && NB == 2) {
 #pragma unroll
     for (int g = 0; g < SB; ++g) {
       bf16x8 A[NB][KB];
-      f32x4 Tv[NB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int gb = 0; gb < NB; ++gb)
           A[gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-#pragma unroll
-      for (int gb = 0; gb < NB; ++gb)
-        Tv[gb] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
       unpack_pairs<QT>(buf, g, pr);
       bf16x8 bop[KB];
 #pragma unroll
@@ -437,20 +488,16 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
       f32x4 S[NB];
       mfma_chain2<KB>(S[0], S[1], A[0], A[1], bop);
 #pragma unroll
-      for (int gb = 0; gb < NB; ++gb) scale(g, gb, S[gb], Tv[gb]);
+      for (int gb = 0; gb < NB; ++gb) scale(g, gb, S[gb]);
     }
   } else if constexpr (NB <= 2) {
     bf16x8 A[2][NB][KB];
-    f32x4 Tv[2][NB];
     auto read_operands = [&](int g, int h) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int gb = 0; gb < NB; ++gb)
           A[h][gb][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-#pragma unroll
-      for (int gb = 0; gb < NB; ++gb)
-        Tv[h][gb] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
     };
     read_operands(0, 0);
 #pragma unroll
@@ -466,7 +513,7 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
       if constexpr (NB == 1) mfma_chain<KB>(S[0], A[h][0], bop);
       else mfma_chain2<KB>(S[0], S[NB - 1], A[h][0], A[h][NB - 1], bop);
 #pragma unroll
-      for (int gb = 0; gb < NB; ++gb) scale(g, gb, S[gb], Tv[h][gb]);
+      for (int gb = 0; gb < NB; ++gb) scale(g, gb, S[gb]);
     }
   } else if constexpr (LEAN) {
     // batch 9..16 in a chain kernel: operand sets two at a time, read just before use
@@ -481,7 +528,6 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
 #pragma unroll
       for (int q = 0; q < NPAIR; ++q) {
         bf16x8 A[2][KB];
-        f32x4 Tv[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int gb = 2 * q + i;
@@ -489,14 +535,13 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
               A[i][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-            Tv[i] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
           }
         }
         f32x4 S[2];
         if (2 * q + 1 < NB) mfma_chain2<KB>(S[0], S[1], A[0], A[1], bop);
         else mfma_chain<KB>(S[0], A[0], bop);
-        scale(g, 2 * q, S[0], Tv[0]);
-        if (2 * q + 1 < NB) scale(g, 2 * q + 1, S[1], Tv[1]);
+        scale(g, 2 * q, S[0]);
+        if (2 * q + 1 < NB) scale(g, 2 * q + 1, S[1]);
       }
     }
   } else {
@@ -504,7 +549,6 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
     // pair's operands are read from LDS while the current pair computes
     constexpr int NPAIR = (NB + 1) / 2;
     bf16x8 A[2][2][KB];
-    f32x4 Tv[2][2];
     auto read_pair = [&](int g, int q, int h) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -513,7 +557,6 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
             A[h][i][kb] = *reinterpret_cast<const bf16x8*>(ap[gb] + (g * F::kSubW + 8 * kb) * 2);
-          Tv[h][i] = MINS ? *reinterpret_cast<const f32x4*>(Tc + (g * NB + gb) * 4) : f32x4{};
         }
       }
     };
@@ -533,9 +576,25 @@ __device__ __forceinline__ void process_unit_mfma(const u32x4* buf, uint32_t d6,
         f32x4 S[2];
         if (2 * q + 1 < NB) mfma_chain2<KB>(S[0], S[1], A[h][0], A[h][1], bop);
         else mfma_chain<KB>(S[0], A[h][0], bop);
-        scale(g, 2 * q, S[0], Tv[h][0]);
-        if (2 * q + 1 < NB) scale(g, 2 * q + 1, S[1], Tv[h][1]);
+        scale(g, 2 * q, S[0]);
+        if (2 * q + 1 < NB) scale(g, 2 * q + 1, S[1]);
       }
+    }
+  }
+  if constexpr (MINS) {
+    float f;
+    const bf16x8 mb = sb_mins_operand<QT>(buf, f);
+    const bf16x8 mbs[3] = {mb, mb, mb};
+#pragma unroll
+    for (int gb = 0; gb < NB; ++gb) {
+      bf16x8 tv[3];
+#pragma unroll
+      for (int s = 0; s < 3; ++s) tv[s] = *reinterpret_cast<const bf16x8*>(tp[gb] + s * ts[gb]);
+      f32x4 M;
+      mfma_chain<3>(M, tv, mbs);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * gb + r < B) acc[4 * gb + r] = __builtin_fmaf(-f, M[r], acc[4 * gb + r]);
     }
   }
 }
@@ -1043,11 +1102,11 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
     // the sub-block sums: after the dot2 path's staged rows, or in the matrix-core path's T block
     constexpr int TS = MF ? MfmaLds<QT, B>::NB * 4 : B;
     float* Ts = MF ? reinterpret_cast<float*>(Xb + len * MfmaLds<QT, B>::kXCol) : T;
-    xs.template store<TSB != 0, TS>(Xb, Ts, Q2, len, 0);
+    xs.template store<TSB != 0, TS, MF>(Xb, Ts, Q2, len, 0);
     const int nr = XStage<QT, B, XF32, NW, kRS>::rounds(len);
     for (int r = 1; r < nr; ++r) {
       xs.template load<CHAIN>(a, c0w, len, r);
-      xs.template store<TSB != 0, TS>(Xb, Ts, Q2, len, r);
+      xs.template store<TSB != 0, TS, MF>(Xb, Ts, Q2, len, r);
     }
     if constexpr (MF) {
       const int z_base = len * MfmaLds<QT, B>::kPerCol;
@@ -1118,11 +1177,14 @@ __device__ __forceinline__ bool gemv_block(GA& a, int lblock, const ChainCtl* ct
         uint8_t* base = reinterpret_cast<uint8_t*>(lds_words);
         const int t_base = len * MfmaLds<QT, B>::kXCol, z_base = t_base + len * MfmaLds<QT, B>::kTCol;
         const uint8_t* ap[NB];
+        const uint8_t* tp[NB];
+        int ts[NB];
 #pragma unroll
-        for (int gb = 0; gb < NB; ++gb) ap[gb] = base + a_operand_offset<B>(lane, gb, ic, 0, z_base);
-        process_unit_mfma<QT, B, CHAIN>(buf[k], d6[k], ap,
-                                 reinterpret_cast<const float*>(base + t_base + ic * MfmaLds<QT, B>::kTCol),
-                                 acc);
+        for (int gb = 0; gb < NB; ++gb) {
+          ap[gb] = base + a_operand_offset<B>(lane, gb, ic, 0, z_base);
+          tp[gb] = base + t_operand_offset<QT, B>(lane, gb, ic, t_base, z_base, ts[gb]);
+        }
+        process_unit_mfma<QT, B, CHAIN>(buf[k], d6[k], ap, tp, ts, acc);
       } else {
         process_unit<QT, B>(buf[k], d6[k], X + ic * B * XW, T + ic * TSB * B, acc);
       }

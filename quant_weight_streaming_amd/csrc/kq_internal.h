@@ -117,8 +117,9 @@ hipError_t launch_gemv_type(int xtype, int rows, int nw, bool mf, const GemvArgs
 
 // The dynamic LDS a workgroup of `nw` wavefronts staging `staged_cols` columns
 // needs on the chosen path: per column the activations of every batch row and
-// (Q4_K/Q5_K) their sub-block sums (matrix cores: rows padded to 528 bytes,
-// then a 512-byte zero block), plus each wavefront's partial sums of the tiles its run touches
+// (Q4_K/Q5_K) their sub-block sums (matrix cores: rows padded to 528 bytes, the
+// sums as three bf16 parts per row padded to a multiple of 4 rows, then a
+// 512-byte zero block), plus each wavefront's partial sums of the tiles its run touches
 // (dynamic workgroups: a counter and one slot per unit).
 // Workgroups whose wavefronts take units dynamically (see gemv_block): the dot2
 // path (one or two staged rows: batch 1 or 2 with bf16 x, batch 1 with fp32 x)
@@ -140,7 +141,7 @@ inline size_t gemv_lds_bytes(int type, int rows, int nw, bool mf, int staged_col
   const int sb = type == KQ_Q6_K ? 0 : 8;   // staged sub-block activation sums per column (Q6_K has no mins)
   if (mf) {
     const int nb = (rows + 3) / 4;
-    return (size_t)staged_cols * (rows * 528 + sb * nb * 16) + 512 + partials;
+    return (size_t)staged_cols * (rows * 528 + (sb ? 3 * nb * 64 : 0)) + 512 + partials;
   }
   return (size_t)staged_cols * rows * 4 * (128 + sb) + partials;
 }
