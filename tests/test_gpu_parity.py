@@ -173,6 +173,26 @@ def test_subnormal_and_extreme_scales(qtype):
 
 
 @pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
+@pytest.mark.parametrize("batch,path", [(1, "dot2"), (4, "mfma"), (8, "mfma"), (8, "dot2")])
+def test_negative_scales(qtype, batch, path, monkeypatch):
+    """Negative fp16 d and dmin (the format's sign bit), normal and subnormal, beside positive ones: the
+    dot2 path and the matrix-core path (whose mins' product carries dmin's sign in its power of two)."""
+    monkeypatch.setenv("KQ_MATRIX_CORES_FROM", "2" if path == "mfma" else "9")
+    rows, cols = 70, 512
+    say(f"case negative scales {qtype} B={batch} {path}")
+    rng = np.random.default_rng(5)
+    f = _fields(qtype, rows * 2, rng)
+    f["d"][:50] |= 0x8000                                               # negative d
+    f["d"][50:60] = torch.as_tensor(rng.integers(1, 0x400, 10)) | 0x8000   # negative subnormal d
+    if qtype != "q6k":
+        f["dmin"][30:100] |= 0x8000                                     # negative dmin
+        f["dmin"][100:110] = torch.as_tensor(rng.integers(1, 0x400, 10)) | 0x8000
+        f["dmin"][110:115] = 0x8000                                     # -0
+    x = synth.gen_x(5, cols, batch, "bf16")
+    _run_fields(qtype, f, rows, cols, x, f"negative scales {qtype} B={batch} {path}")
+
+
+@pytest.mark.parametrize("qtype", ["q4k", "q5k", "q6k"])
 @pytest.mark.parametrize("xdtype", ["bf16", "f32"])
 def test_one_hot_picks_columns_exactly(qtype, xdtype):
     """x = e_k gives y = W[:, k] bit-exactly: each weight is rounded once, like the dequantised value."""
